@@ -1,0 +1,215 @@
+/*
+ * rd.h — C ABI of the MI355X (gfx950) batch-1 decode-step library.
+ *
+ * The library runs the autoregressive decode step of a dense decoder-only
+ * transformer on one GPU: RMSNorm, weight-streaming fp16 GEMVs (fused QKV,
+ * output projection, SwiGLU gate/up and down, LM head), RoPE with KV-cache
+ * append, single-query attention over the cache split along the key axis
+ * with a log-sum-exp merge, and greedy argmax on the device.
+ *
+ * Sources for what is computed (page titles as printed):
+ *  - "Real-time LLM inference on standard GPUs: 3,000 tokens/s per request"
+ *    (Kog), section "Memory bandwidth is the main bottleneck ...": at batch 1
+ *    every active weight crosses HBM once per token, so
+ *    tokens/s <= BW / (beta * weight bytes + KV bytes); section "Where
+ *    standard inference stacks lose microseconds": kernel boundaries, CPU
+ *    sampling and grid synchronisation are the losses to remove, sampling
+ *    stays on the GPU.
+ *  - "How the xAI engineering team cut Grok Bot latency to milliseconds",
+ *    §2.1 (per-token forward; whole-step graph capture), §2.3 (KV cache in
+ *    FP8 E5M2, dequantized to fp16 when read), §3.3 (engine options: model,
+ *    device, KV cache dtype, maximum KV length), §4.1 (capture once, replay
+ *    with a static input buffer).
+ *  - "Grok-3 v3.2.4 hot update deep dive", §3.2: adaptive-range INT8 KV
+ *    quantization per 128-token segment, scale=(max-min)/255,
+ *    zero_point=round(-min/scale).
+ *  - "LLM inference architecture rebuild (state-driven layered design)",
+ *    §3.3: kernels called with an explicit softmax scale and returning
+ *    errors as values; §5.2: quantization scales kept in fp32.
+ *
+ * Conventions of every entry point:
+ *  - Returns rd_status; RD_OK == 0, errors are negative.  No exception
+ *    crosses the ABI and nothing aborts.  rd_last_error() gives a message
+ *    for the calling thread's last failure.
+ *  - "host" pointers are ordinary CPU memory owned by the caller; "device"
+ *    pointers are HIP device memory on the model's (or given) device, owned
+ *    by the caller unless said otherwise.
+ *  - A model is not thread-safe; distinct models may run on distinct
+ *    streams concurrently.
+ *  - After an RD_ERR_DEVICE the model is poisoned: every later call on it
+ *    returns RD_ERR_DEVICE until rd_model_destroy.
+ */
+#ifndef RD_H
+#define RD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rd_model rd_model; /* opaque; owns all of its device memory */
+
+typedef enum {
+    RD_OK = 0,
+    RD_ERR_INVALID_ARG = -1,   /* NULL pointer, size out of range, batch != max_batch, ... */
+    RD_ERR_BAD_BLOB = -2,      /* malformed or mis-sized weight blob */
+    RD_ERR_OUT_OF_MEMORY = -3, /* device allocation failed */
+    RD_ERR_CONTEXT_FULL = -4,  /* position would reach max_context; state unchanged */
+    RD_ERR_UNSUPPORTED = -5,   /* valid request this build does not implement */
+    RD_ERR_DEVICE = -6,        /* HIP error; the model is poisoned */
+    RD_ERR_NUMERIC = -7        /* non-finite logit or out-of-range token seen on the device */
+} rd_status;
+
+typedef enum {
+    RD_KV_FP16 = 0,        /* K/V rows stored as fp16 */
+    RD_KV_FP8_E5M2 = 1,    /* fp16 row rounded to OCP E5M2 (RNE, no scale, overflow -> inf) */
+    RD_KV_INT8_SEG128 = 2  /* u8 codes per 128-token segment per (layer, K|V, kv-head) with
+                              fp32 scale and zero point; the open segment stays fp16 */
+} rd_kv_format;
+
+typedef enum {
+    RD_EXEC_AUTO = 0,      /* the fastest measured executor */
+    RD_EXEC_EAGER = 1,     /* one kernel launch per phase */
+    RD_EXEC_GRAPH = 2,     /* the step's launches captured once into a hipGraph, replayed per step */
+    RD_EXEC_PERSISTENT = 3 /* one cooperative launch per step, grid barriers between phases */
+} rd_executor;
+
+typedef struct {
+    uint32_t struct_size; /* sizeof(rd_options) */
+    int32_t device;       /* HIP device ordinal */
+    void* stream;         /* hipStream_t to run on, or NULL for a library-owned stream */
+    int32_t max_context;  /* positions per sequence (KV rows allocated), >= 1 */
+    int32_t max_batch;    /* independent sequences advancing in lockstep: 1 */
+    int32_t kv_format;    /* rd_kv_format */
+    int32_t executor;     /* rd_executor */
+    int32_t attn_splits;  /* maximum key-axis splits per kv-head, 0 = default (64) */
+} rd_options;
+
+typedef struct {
+    int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ff, vocab;
+    float rope_base, norm_eps;
+    int32_t max_context, max_batch, kv_format, executor, attn_splits;
+    uint64_t weight_bytes;      /* device bytes of all weights */
+    uint64_t streamed_bytes;    /* weight bytes one step must read (all but the embedding table,
+                                   plus one embedding row per sequence) */
+    uint64_t kv_bytes;          /* device bytes of the KV cache (all formats' parts) */
+} rd_model_info;
+
+/* Initialise an options struct with defaults (device 0, NULL stream,
+ * max_context 4096, max_batch 1, fp16 KV, AUTO executor, 0 splits). */
+void rd_options_init(rd_options* opt);
+
+/* Create a model from a weight blob ("RDW1"): a 256-byte header (magic,
+ * version 1, header bytes 256, dtype 1 = fp16, n_layers, d_model, n_heads,
+ * n_kv_heads, head_dim, d_ff, vocab as i32, rope_base and norm_eps as f32,
+ * flags 0), then fp16 row-major [out,in] tensors on 256-byte boundaries:
+ * embed[V,D]; per layer attn_norm[D], wq[H*hd,D], wk[Hk*hd,D], wv[Hk*hd,D],
+ * wo[D,H*hd], ffn_norm[D], w_gate[F,D], w_up[F,D], w_down[D,F]; then
+ * final_norm[D], lm_head[V,D]; the blob ends there.
+ * blob: host, borrowed for the call only (copied and re-tiled).
+ * Errors: INVALID_ARG (NULL, bad options), BAD_BLOB, UNSUPPORTED (a shape the
+ * kernels do not cover: head_dim must be 64 or 128, d_model and d_ff
+ * multiples of 8, n_heads a multiple of n_kv_heads), OUT_OF_MEMORY, DEVICE. */
+rd_status rd_model_create(const void* blob, size_t blob_bytes, const rd_options* opt, rd_model** out);
+
+/* Release everything; NULL-safe. */
+void rd_model_destroy(rd_model* m);
+
+rd_status rd_model_get_info(const rd_model* m, rd_model_info* out);
+
+/* Position := 0 for every sequence (cache contents become unreachable). */
+rd_status rd_reset(rd_model* m);
+
+/* Position of the next token to be decoded (the same for every sequence). */
+rd_status rd_get_position(const rd_model* m, int32_t* pos);
+
+/* One decode step.  tokens: host [batch] ids at the current position.
+ * logits: host [batch*vocab] fp32 or NULL.  next: host [batch] greedy argmax
+ * (lowest index on ties) or NULL.  batch must equal max_batch.
+ * Errors: INVALID_ARG, CONTEXT_FULL (nothing changed), NUMERIC (a non-finite
+ * logit or an out-of-range token was seen; the step still advanced), DEVICE. */
+rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, float* logits, int32_t* next);
+
+/* n_steps greedy steps with the token fed back on the device (no host round
+ * trip between steps).  first: host [batch], the token at the current
+ * position.  out_tokens: host [n_steps*batch], step-major: the argmax of
+ * every step.  Errors as rd_decode_step; CONTEXT_FULL if the steps do not fit. */
+rd_status rd_generate(rd_model* m, const int32_t* first, int32_t batch, int32_t n_steps, int32_t* out_tokens);
+
+/* Same as rd_generate but out_tokens_dev is a device [n_steps*batch] int32
+ * buffer and nothing is synchronised: the call only enqueues work on the
+ * model's stream (errors found on the device surface at the next
+ * synchronising call). */
+rd_status rd_generate_async(rd_model* m, const int32_t* first, int32_t batch, int32_t n_steps,
+                            int32_t* out_tokens_dev);
+
+/* Wait for the model's stream and report device-side errors. */
+rd_status rd_synchronize(rd_model* m);
+
+/* Copy the raw KV storage of (seq, layer, which: 0 = K, 1 = V) into host
+ * memory dst (capacity cap bytes).  Layout per format:
+ *  FP16:  u16 [n_kv_heads][max_context][head_dim]
+ *  E5M2:  u8  [n_kv_heads][max_context][head_dim]
+ *  INT8:  u8 codes [n_kv_heads][max_context][head_dim], then
+ *         u16 staging [n_kv_heads][128][head_dim] (row = pos % 128), then
+ *         f32 meta [n_kv_heads][ceil(max_context/128)][2] (scale, zero point).
+ * *written receives the byte count.  Synchronises the stream. */
+rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, void* dst, size_t cap,
+                             size_t* written);
+
+/* Overwrite the raw KV storage of (seq, layer, which) from host memory, same
+ * layout as rd_debug_export_kv, and set the position of every sequence to
+ * pos.  For parity checks that hand the same cache to another
+ * implementation. */
+rd_status rd_debug_import_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, const void* src,
+                             size_t bytes, int32_t pos);
+
+const char* rd_last_error(void);
+
+/* ---- kernels of the step, callable alone (device pointers) ------------------
+ * Each runs exactly the device code the model's step uses, on the given
+ * stream (NULL = the null stream), asynchronously.  Argument errors return
+ * INVALID_ARG before anything is enqueued. */
+
+/* y[b][n] = sum_k W[n][k] * x[b][k], fp16 inputs, fp32 accumulate and output.
+ * W: device fp16 row-major [N][K]; x: device fp16 [batch][K]; y: device f32
+ * [batch][N].  K a multiple of 8 and <= 16384, batch 1.  Weight-streaming GEMV
+ * ("Real-time LLM inference on standard GPUs", section on memory bandwidth:
+ * about 1 FLOP per weight byte at fp16). */
+rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t K, int32_t batch, void* stream);
+
+/* Single-query attention of n_heads query heads over one sequence's cache
+ * with grouped kv heads (query head h reads kv head h / (n_heads/n_kv_heads)):
+ * out[h] = softmax(q[h] . K[g][0..L) * scale) V[g][0..L), computed as
+ * partial softmaxes over at most `splits` key ranges merged by log-sum-exp.
+ * q: device f32 [n_heads][hd]; K, V: device fp16 [n_kv_heads][ld][hd];
+ * out: device f32 [n_heads][hd]; scale: the softmax scale (1/sqrt(hd) in the
+ * model); hd 64 or 128; 1 <= L <= ld; 1 <= splits <= 256.  Uses a library
+ * scratch buffer allocated on first use. */
+rd_status rd_attention_f16(const float* q, const void* K, const void* V, float* out, int32_t n_heads,
+                           int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
+                           void* stream);
+
+/* out[i] = E5M2 encoding of the fp16 value in[i] (round to nearest even on
+ * the dropped mantissa bits, overflow to inf, NaN to quiet NaN).
+ * in: device u16 [n]; out: device u8 [n]. */
+rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* stream);
+
+/* Segment quantization of n_seg independent segments of seg_elems fp16
+ * values each: per segment min/max in fp32, scale=(max-min)/255 (1 when
+ * max==min), zp=rint(-min/scale), code=clamp(rint(x/scale)+zp, 0, 255).
+ * in: device u16 [n_seg][seg_elems]; codes: device u8 [n_seg][seg_elems];
+ * meta: device f32 [n_seg][2] (scale, zp).  seg_elems <= 65536. */
+rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uint8_t* codes, float* meta,
+                       void* stream);
+
+/* *out = index of the largest of v[0..n) (lowest index on ties).
+ * v: device f32 [n]; out: device i32 [1]. */
+rd_status rd_argmax_f32(const float* v, int32_t n, int32_t* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

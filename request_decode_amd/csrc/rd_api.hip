@@ -1,0 +1,717 @@
+// Host runtime and C ABI of the decode-step library (see include/rd.h).
+//
+// create: parse the weight blob, re-tile it into the layout the kernels
+// stream (once), allocate the KV cache in the requested format, build the
+// RoPE table, and set up the executor.  A step is a fixed sequence of
+// launches whose per-step scalars (position, token) live in device memory,
+// so the whole step can be captured once into a hipGraph and replayed
+// ("How the xAI engineering team cut Grok Bot latency to milliseconds",
+// §2.1 and §4.1: capture the decode step once, feed it through a static
+// buffer, replay it), and generated tokens feed the next step on the device
+// without a host round trip (sampling stays on the GPU, "Real-time LLM
+// inference on standard GPUs", loss table).
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "rd.h"
+#include "rd_internal.h"
+
+using namespace rd;
+
+static thread_local std::string g_err;
+
+static rd_status fail(rd_status st, const std::string& msg) {
+    g_err = msg;
+    return st;
+}
+
+extern "C" const char* rd_last_error(void) { return g_err.c_str(); }
+
+#define HIP_TRY(expr)                                                                         \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess) return dev_fail(m, #expr, e_);                                  \
+    } while (0)
+
+// ---------------------------------------------------------------------------
+// blob parsing (host only)
+// ---------------------------------------------------------------------------
+namespace {
+
+struct BlobDims {
+    int L, D, H, Hk, hd, F, V;
+    float base, eps;
+    size_t embed, final_norm, lm_head;
+    std::vector<size_t> layer;  // 9 offsets per layer
+};
+
+template <class T>
+T rd_le(const uint8_t* p) {
+    T v;
+    memcpy(&v, p, sizeof v);
+    return v;
+}
+
+bool parse_blob(const uint8_t* b, size_t n, BlobDims& d, std::string& err) {
+    if (!b || n < 256) { err = "blob shorter than its 256-byte header"; return false; }
+    if (memcmp(b, "RDW1", 4) != 0) { err = "bad blob magic"; return false; }
+    if (rd_le<uint32_t>(b + 4) != 1) { err = "unsupported blob version"; return false; }
+    if (rd_le<uint32_t>(b + 8) != 256) { err = "unsupported header size"; return false; }
+    if (rd_le<uint32_t>(b + 12) != 1) { err = "unsupported tensor dtype (fp16 = 1 expected)"; return false; }
+    if (rd_le<uint32_t>(b + 52) != 0) { err = "unsupported flags"; return false; }
+    d.L = rd_le<int32_t>(b + 16); d.D = rd_le<int32_t>(b + 20); d.H = rd_le<int32_t>(b + 24);
+    d.Hk = rd_le<int32_t>(b + 28); d.hd = rd_le<int32_t>(b + 32); d.F = rd_le<int32_t>(b + 36);
+    d.V = rd_le<int32_t>(b + 40);
+    d.base = rd_le<float>(b + 44);
+    d.eps = rd_le<float>(b + 48);
+    if (d.L <= 0 || d.D <= 0 || d.H <= 0 || d.Hk <= 0 || d.hd <= 0 || d.F <= 0 || d.V <= 0 || d.L > 4096 ||
+        d.D > (1 << 20) || d.V > (1 << 24) || d.F > (1 << 22) || d.H > 4096 || d.Hk > 4096 || d.hd > 4096) {
+        err = "bad dimensions in blob header";
+        return false;
+    }
+    if (!(d.base > 1.0f) || !(d.eps >= 0.0f) || !isfinite(d.base) || !isfinite(d.eps)) {
+        err = "bad rope_base / norm_eps";
+        return false;
+    }
+    size_t off = 256;
+    auto take = [&](size_t elems) {
+        off = (off + 255) / 256 * 256;
+        size_t o = off;
+        off += elems * 2;
+        return o;
+    };
+    const size_t D = d.D, H = d.H, Hk = d.Hk, hd = d.hd, F = d.F, V = d.V;
+    d.embed = take(V * D);
+    d.layer.clear();
+    for (int l = 0; l < d.L; ++l) {
+        d.layer.push_back(take(D));
+        d.layer.push_back(take(H * hd * D));
+        d.layer.push_back(take(Hk * hd * D));
+        d.layer.push_back(take(Hk * hd * D));
+        d.layer.push_back(take(D * H * hd));
+        d.layer.push_back(take(D));
+        d.layer.push_back(take(F * D));
+        d.layer.push_back(take(F * D));
+        d.layer.push_back(take(D * F));
+    }
+    d.final_norm = take(D);
+    d.lm_head = take(V * D);
+    if (off != n) {
+        err = "blob is " + std::to_string(n) + " bytes, its header implies " + std::to_string(off);
+        return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// model
+// ---------------------------------------------------------------------------
+struct rd_model {
+    int dev = 0;
+    hipStream_t stream = nullptr;
+    bool own_stream = false;
+    hipStream_t cap_stream = nullptr;
+    BlobDims d;
+    rd_options opt{};
+    int S = 64;
+    bool poisoned = false;
+    int host_pos = 0;
+
+    void* wbuf = nullptr;
+    size_t wbytes = 0, streamed = 0;
+    std::vector<LayerW> layers;
+    const _Float16 *embed = nullptr, *g_final = nullptr, *lm_head = nullptr;
+
+    void* kc = nullptr;
+    void* vc = nullptr;
+    uint16_t* stage = nullptr;
+    float* meta = nullptr;
+    size_t kv_bytes = 0;
+    int nseg = 0;
+
+    void* act = nullptr;  // activations, partials, counters, state, tables
+    StepArgs A{};
+    int* gen_host = nullptr;     // pinned [max_ctx]
+    float* logits_host = nullptr; // pinned [V]
+    StepState* state_host = nullptr;
+
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t gexec = nullptr;
+};
+
+static rd_status dev_fail(rd_model* m, const char* what, hipError_t e) {
+    if (m) m->poisoned = true;
+    return fail(RD_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+extern "C" void rd_options_init(rd_options* o) {
+    if (!o) return;
+    memset(o, 0, sizeof *o);
+    o->struct_size = sizeof(rd_options);
+    o->max_context = 4096;
+    o->max_batch = 1;
+    o->kv_format = RD_KV_FP16;
+    o->executor = RD_EXEC_AUTO;
+}
+
+namespace {
+
+__global__ void k_set_state(StepState* st, int pos, int token, int reset_gen) {
+    st->pos = pos;
+    st->token[0] = token;
+    st->err = 0;
+    if (reset_gen) st->n_gen = 0;
+}
+
+__global__ void k_set_int(int* p, int v) { *p = v; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+void free_model(rd_model* m) {
+    if (!m) return;
+    (void)hipSetDevice(m->dev);
+    if (m->gexec) (void)hipGraphExecDestroy(m->gexec);
+    if (m->graph) (void)hipGraphDestroy(m->graph);
+    if (m->stream) (void)hipStreamSynchronize(m->stream);
+    (void)hipFree(m->wbuf);
+    (void)hipFree(m->kc);
+    (void)hipFree(m->vc);
+    (void)hipFree(m->stage);
+    (void)hipFree(m->meta);
+    (void)hipFree(m->act);
+    if (m->gen_host) (void)hipHostFree(m->gen_host);
+    if (m->logits_host) (void)hipHostFree(m->logits_host);
+    if (m->state_host) (void)hipHostFree(m->state_host);
+    if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+    if (m->own_stream && m->stream) (void)hipStreamDestroy(m->stream);
+    delete m;
+}
+
+rd_status step_enqueue(rd_model* m) {
+    if (m->opt.executor == RD_EXEC_EAGER) {
+        HIP_TRY(launch_step(m->A, m->stream));
+        return RD_OK;
+    }
+    if (!m->gexec) {
+        HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal));
+        hipError_t le = launch_step(m->A, m->cap_stream);
+        hipGraph_t g = nullptr;
+        hipError_t ce = hipStreamEndCapture(m->cap_stream, &g);
+        if (le != hipSuccess) return dev_fail(m, "launch_step (capture)", le);
+        if (ce != hipSuccess) return dev_fail(m, "hipStreamEndCapture", ce);
+        m->graph = g;
+        HIP_TRY(hipGraphInstantiate(&m->gexec, m->graph, nullptr, nullptr, 0));
+    }
+    HIP_TRY(hipGraphLaunch(m->gexec, m->stream));
+    return RD_OK;
+}
+
+rd_status check_model(const rd_model* m) {
+    if (!m) return fail(RD_ERR_INVALID_ARG, "model is NULL");
+    if (m->poisoned) return fail(RD_ERR_DEVICE, "model is poisoned by an earlier device error");
+    return RD_OK;
+}
+
+}  // namespace
+
+extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const rd_options* opt_in, rd_model** out) {
+    if (!out) return fail(RD_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!blob) return fail(RD_ERR_INVALID_ARG, "blob is NULL");
+    rd_options opt;
+    rd_options_init(&opt);
+    if (opt_in) {
+        if (opt_in->struct_size != sizeof(rd_options)) return fail(RD_ERR_INVALID_ARG, "rd_options.struct_size mismatch");
+        opt = *opt_in;
+    }
+    if (opt.max_context < 1 || opt.max_context > (1 << 22)) return fail(RD_ERR_INVALID_ARG, "max_context out of range");
+    if (opt.max_batch != 1) return fail(RD_ERR_UNSUPPORTED, "max_batch must be 1");
+    if (opt.kv_format < RD_KV_FP16 || opt.kv_format > RD_KV_INT8_SEG128)
+        return fail(RD_ERR_INVALID_ARG, "bad kv_format");
+    if (opt.executor < RD_EXEC_AUTO || opt.executor > RD_EXEC_PERSISTENT) return fail(RD_ERR_INVALID_ARG, "bad executor");
+    if (opt.executor == RD_EXEC_PERSISTENT) return fail(RD_ERR_UNSUPPORTED, "persistent executor not built");
+    if (opt.executor == RD_EXEC_AUTO) opt.executor = RD_EXEC_GRAPH;
+    if (opt.attn_splits < 0 || opt.attn_splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "attn_splits out of range");
+
+    BlobDims d;
+    std::string err;
+    if (!parse_blob((const uint8_t*)blob, blob_bytes, d, err)) return fail(RD_ERR_BAD_BLOB, err);
+    const char* why = nullptr;
+    if (!step_supported(d.D, d.H, d.Hk, d.hd, d.F, &why)) return fail(RD_ERR_UNSUPPORTED, why);
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(RD_ERR_DEVICE, "no HIP device");
+    if (opt.device < 0 || opt.device >= ndev) return fail(RD_ERR_INVALID_ARG, "device ordinal out of range");
+
+    rd_model* m = new rd_model();
+    m->dev = opt.device;
+    m->d = d;
+    m->opt = opt;
+    m->S = opt.attn_splits ? opt.attn_splits : 64;
+    auto bail = [&](rd_status st) {
+        std::string keep = g_err;
+        free_model(m);
+        g_err = keep;
+        return st;
+    };
+#define CREATE_TRY(expr)                                                                      \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ == hipErrorOutOfMemory) return bail(fail(RD_ERR_OUT_OF_MEMORY, #expr));        \
+        if (e_ != hipSuccess) return bail(fail(RD_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_))); \
+    } while (0)
+
+    CREATE_TRY(hipSetDevice(m->dev));
+    if (opt.stream) {
+        m->stream = (hipStream_t)opt.stream;
+    } else {
+        CREATE_TRY(hipStreamCreateWithFlags(&m->stream, hipStreamNonBlocking));
+        m->own_stream = true;
+    }
+    CREATE_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
+
+    const size_t D = d.D, H = d.H, Hk = d.Hk, hd = d.hd, F = d.F, V = d.V, NL = d.L;
+    const size_t Nqkv = (H + 2 * Hk) * hd;
+    // ---- device weight image: embed | per layer {wqkv, wo, wgu, wd, g_attn, g_ffn} | g_final | lm_head
+    size_t off = 0;
+    auto put = [&](size_t elems) {
+        size_t o = off;
+        off = align256(off + elems * 2);
+        return o;
+    };
+    const size_t o_embed = put(V * D);
+    std::vector<size_t> o_layer;
+    for (size_t l = 0; l < NL; ++l) {
+        o_layer.push_back(put(Nqkv * D));
+        o_layer.push_back(put(D * H * hd));
+        o_layer.push_back(put(2 * F * D));
+        o_layer.push_back(put(D * F));
+        o_layer.push_back(put(D));
+        o_layer.push_back(put(D));
+    }
+    const size_t o_gfinal = put(D);
+    const size_t o_lm = put(V * D);
+    m->wbytes = off;
+    CREATE_TRY(hipMalloc(&m->wbuf, m->wbytes));
+    uint8_t* W = (uint8_t*)m->wbuf;
+    const uint8_t* B = (const uint8_t*)blob;
+    auto up = [&](size_t dst, const void* src, size_t bytes) { return hipMemcpy(W + dst, src, bytes, hipMemcpyHostToDevice); };
+
+    CREATE_TRY(up(o_embed, B + d.embed, V * D * 2));
+    std::vector<uint16_t> tmp;
+    for (size_t l = 0; l < NL; ++l) {
+        const size_t* L9 = &d.layer[l * 9];
+        const uint16_t* wq = (const uint16_t*)(B + L9[1]);
+        const uint16_t* wk = (const uint16_t*)(B + L9[2]);
+        const uint16_t* wv = (const uint16_t*)(B + L9[3]);
+        // fused QKV with each RoPE pair (j, j+hd/2) of a q or k head on adjacent rows
+        tmp.resize(Nqkv * D);
+        for (size_t rho = 0; rho < Nqkv; ++rho) {
+            const uint16_t* src;
+            if (rho < (H + Hk) * hd) {
+                const bool isq = rho < H * hd;
+                const size_t r = isq ? rho : rho - H * hd;
+                const size_t head = r / hd, w = r % hd, j = w / 2, half = w % 2;
+                const size_t srow = head * hd + j + half * (hd / 2);
+                src = (isq ? wq : wk) + srow * D;
+            } else {
+                src = wv + (rho - (H + Hk) * hd) * D;
+            }
+            memcpy(&tmp[rho * D], src, D * 2);
+        }
+        CREATE_TRY(up(o_layer[l * 6 + 0], tmp.data(), Nqkv * D * 2));
+        CREATE_TRY(up(o_layer[l * 6 + 1], B + L9[4], D * H * hd * 2));
+        // gate/up interleaved: row 2i = gate_i, row 2i+1 = up_i
+        const uint16_t* wg = (const uint16_t*)(B + L9[6]);
+        const uint16_t* wu = (const uint16_t*)(B + L9[7]);
+        tmp.resize(2 * F * D);
+        for (size_t i = 0; i < F; ++i) {
+            memcpy(&tmp[(2 * i) * D], wg + i * D, D * 2);
+            memcpy(&tmp[(2 * i + 1) * D], wu + i * D, D * 2);
+        }
+        CREATE_TRY(up(o_layer[l * 6 + 2], tmp.data(), 2 * F * D * 2));
+        CREATE_TRY(up(o_layer[l * 6 + 3], B + L9[8], D * F * 2));
+        CREATE_TRY(up(o_layer[l * 6 + 4], B + L9[0], D * 2));
+        CREATE_TRY(up(o_layer[l * 6 + 5], B + L9[5], D * 2));
+        LayerW Lw;
+        Lw.wqkv = (const _Float16*)(W + o_layer[l * 6 + 0]);
+        Lw.wo = (const _Float16*)(W + o_layer[l * 6 + 1]);
+        Lw.wgu = (const _Float16*)(W + o_layer[l * 6 + 2]);
+        Lw.wd = (const _Float16*)(W + o_layer[l * 6 + 3]);
+        Lw.g_attn = (const _Float16*)(W + o_layer[l * 6 + 4]);
+        Lw.g_ffn = (const _Float16*)(W + o_layer[l * 6 + 5]);
+        m->layers.push_back(Lw);
+    }
+    CREATE_TRY(up(o_gfinal, B + d.final_norm, D * 2));
+    CREATE_TRY(up(o_lm, B + d.lm_head, V * D * 2));
+    m->embed = (const _Float16*)(W + o_embed);
+    m->g_final = (const _Float16*)(W + o_gfinal);
+    m->lm_head = (const _Float16*)(W + o_lm);
+    m->streamed = (NL * (Nqkv * D + D * H * hd + 2 * F * D + D * F + 2 * D) + D + V * D + D) * 2;
+
+    // ---- KV cache
+    const size_t ctx = opt.max_context;
+    const size_t kv_elems = NL * Hk * ctx * hd;
+    const size_t es = opt.kv_format == RD_KV_FP16 ? 2 : 1;
+    m->nseg = (int)((ctx + SEG - 1) / SEG);
+    CREATE_TRY(hipMalloc(&m->kc, kv_elems * es));
+    CREATE_TRY(hipMalloc(&m->vc, kv_elems * es));
+    CREATE_TRY(hipMemset(m->kc, 0, kv_elems * es));
+    CREATE_TRY(hipMemset(m->vc, 0, kv_elems * es));
+    m->kv_bytes = 2 * kv_elems * es;
+    if (opt.kv_format == RD_KV_INT8_SEG128) {
+        const size_t st_elems = NL * 2 * Hk * SEG * hd, meta_elems = NL * 2 * Hk * m->nseg * 2;
+        CREATE_TRY(hipMalloc(&m->stage, st_elems * 2));
+        CREATE_TRY(hipMalloc(&m->meta, meta_elems * 4));
+        CREATE_TRY(hipMemset(m->stage, 0, st_elems * 2));
+        CREATE_TRY(hipMemset(m->meta, 0, meta_elems * 4));
+        m->kv_bytes += st_elems * 2 + meta_elems * 4;
+    }
+
+    // ---- activations, partials, counters, state, RoPE table
+    const int n_lm_wg = lm_head_workgroups(d.V);
+    size_t a = 0;
+    auto carve = [&](size_t bytes) {
+        size_t o = a;
+        a = align256(a + bytes);
+        return o;
+    };
+    const size_t o_x = carve(D * 4), o_q = carve(H * hd * 4), o_a = carve(H * hd * 4), o_m = carve(F * 4);
+    const size_t o_logits = carve(V * 4);
+    const size_t o_po = carve(H * MAX_SPLITS * hd * 4), o_pml = carve(H * MAX_SPLITS * 2 * 4);
+    const size_t o_cnt = carve(Hk * 4), o_av = carve(n_lm_wg * 4), o_ai = carve(n_lm_wg * 4), o_ac = carve(4);
+    const size_t o_st = carve(sizeof(StepState)), o_gen = carve(ctx * 4);
+    const size_t o_rope = carve(ctx * (hd / 2) * sizeof(float2));
+    CREATE_TRY(hipMalloc(&m->act, a));
+    CREATE_TRY(hipMemset(m->act, 0, a));
+    uint8_t* X = (uint8_t*)m->act;
+    {
+        std::vector<float2> rope(ctx * (hd / 2));
+        for (size_t p = 0; p < ctx; ++p)
+            for (size_t j = 0; j < hd / 2; ++j) {
+                const double theta = pow((double)d.base, -2.0 * (double)j / (double)hd);
+                const double ang = (double)p * theta;
+                rope[p * (hd / 2) + j] = make_float2((float)cos(ang), (float)sin(ang));
+            }
+        CREATE_TRY(hipMemcpy(X + o_rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice));
+    }
+    CREATE_TRY(hipHostMalloc((void**)&m->gen_host, ctx * 4, hipHostMallocDefault));
+    CREATE_TRY(hipHostMalloc((void**)&m->logits_host, V * 4, hipHostMallocDefault));
+    CREATE_TRY(hipHostMalloc((void**)&m->state_host, sizeof(StepState), hipHostMallocDefault));
+
+    StepArgs& A = m->A;
+    A.D = d.D; A.H = d.H; A.Hk = d.Hk; A.hd = d.hd; A.F = d.F; A.V = d.V;
+    A.max_ctx = opt.max_context; A.S = m->S; A.kvfmt = opt.kv_format; A.n_layers = d.L;
+    A.eps = d.eps;
+    A.scale = (float)(1.0 / sqrt((double)d.hd));
+    A.embed = m->embed; A.g_final = m->g_final; A.lm_head = m->lm_head;
+    A.layers = m->layers.data();
+    A.x = (float*)(X + o_x); A.q = (float*)(X + o_q); A.a = (float*)(X + o_a); A.m = (float*)(X + o_m);
+    A.logits = (float*)(X + o_logits);
+    A.part_o = (float*)(X + o_po); A.part_ml = (float*)(X + o_pml);
+    A.cnt = (int*)(X + o_cnt);
+    A.arg_val = (float*)(X + o_av); A.arg_idx = (int*)(X + o_ai); A.arg_cnt = (int*)(X + o_ac);
+    A.st = (StepState*)(X + o_st); A.gen_out = (int*)(X + o_gen);
+    A.rope = (const float2*)(X + o_rope);
+    A.kc = m->kc; A.vc = m->vc; A.stage = m->stage; A.meta = m->meta; A.nseg = m->nseg;
+#undef CREATE_TRY
+    *out = m;
+    return RD_OK;
+}
+
+extern "C" void rd_model_destroy(rd_model* m) { free_model(m); }
+
+extern "C" rd_status rd_model_get_info(const rd_model* m, rd_model_info* o) {
+    if (!m || !o) return fail(RD_ERR_INVALID_ARG, "NULL argument");
+    o->n_layers = m->d.L; o->d_model = m->d.D; o->n_heads = m->d.H; o->n_kv_heads = m->d.Hk;
+    o->head_dim = m->d.hd; o->d_ff = m->d.F; o->vocab = m->d.V;
+    o->rope_base = m->d.base; o->norm_eps = m->d.eps;
+    o->max_context = m->opt.max_context; o->max_batch = m->opt.max_batch;
+    o->kv_format = m->opt.kv_format; o->executor = m->opt.executor; o->attn_splits = m->S;
+    o->weight_bytes = m->wbytes;
+    o->streamed_bytes = m->streamed;
+    o->kv_bytes = m->kv_bytes;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_reset(rd_model* m) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    m->host_pos = 0;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_get_position(const rd_model* m, int32_t* pos) {
+    if (!m || !pos) return fail(RD_ERR_INVALID_ARG, "NULL argument");
+    *pos = m->host_pos;
+    return RD_OK;
+}
+
+static rd_status finish_sync(rd_model* m) {
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    if (m->state_host->err & ERR_TOKEN) return fail(RD_ERR_NUMERIC, "token id out of range seen on the device");
+    if (m->state_host->err & ERR_NONFINITE) return fail(RD_ERR_NUMERIC, "non-finite logit");
+    return RD_OK;
+}
+
+extern "C" rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, float* logits, int32_t* next) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!tokens) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
+    if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
+    if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
+    if (tokens[0] < 0 || tokens[0] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    HIP_TRY(hipSetDevice(m->dev));
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tokens[0], 1);
+    HIP_TRY(hipGetLastError());
+    if ((st = step_enqueue(m))) return st;
+    if (logits)
+        HIP_TRY(hipMemcpyAsync(m->logits_host, m->A.logits, (size_t)m->d.V * 4, hipMemcpyDeviceToHost, m->stream));
+    HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    m->host_pos += 1;
+    st = finish_sync(m);
+    if (st == RD_ERR_DEVICE) return st;
+    if (logits) memcpy(logits, m->logits_host, (size_t)m->d.V * 4);
+    if (next) next[0] = m->state_host->token[0];
+    return st;
+}
+
+static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t batch, int32_t n) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!first) return fail(RD_ERR_INVALID_ARG, "first is NULL");
+    if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
+    if (n < 0) return fail(RD_ERR_INVALID_ARG, "n_steps < 0");
+    if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "steps do not fit the context");
+    if (first[0] < 0 || first[0] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    HIP_TRY(hipSetDevice(m->dev));
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, first[0], 1);
+    HIP_TRY(hipGetLastError());
+    for (int i = 0; i < n; ++i)
+        if ((st = step_enqueue(m))) return st;
+    m->host_pos += n;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_generate(rd_model* m, const int32_t* first, int32_t batch, int32_t n, int32_t* out) {
+    if (!out && n > 0) return fail(RD_ERR_INVALID_ARG, "out_tokens is NULL");
+    rd_status st = generate_enqueue(m, first, batch, n);
+    if (st) return st;
+    if (n == 0) return RD_OK;
+    HIP_TRY(hipMemcpyAsync(m->gen_host, m->A.gen_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->stream));
+    HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    st = finish_sync(m);
+    if (st == RD_ERR_DEVICE) return st;
+    memcpy(out, m->gen_host, (size_t)n * 4);
+    return st;
+}
+
+extern "C" rd_status rd_generate_async(rd_model* m, const int32_t* first, int32_t batch, int32_t n, int32_t* out_dev) {
+    if (!out_dev && n > 0) return fail(RD_ERR_INVALID_ARG, "out_tokens_dev is NULL");
+    rd_status st = generate_enqueue(m, first, batch, n);
+    if (st) return st;
+    if (n > 0)
+        HIP_TRY(hipMemcpyAsync(out_dev, m->A.gen_out, (size_t)n * 4, hipMemcpyDeviceToDevice, m->stream));
+    HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_synchronize(rd_model* m) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    HIP_TRY(hipSetDevice(m->dev));
+    return finish_sync(m);
+}
+
+// ---- debug cache access -------------------------------------------------------
+namespace {
+struct KvRegion {
+    uint8_t* dev;
+    size_t bytes;
+};
+// Regions of (layer, which) in export order.
+int kv_regions(rd_model* m, int layer, int which, KvRegion* r) {
+    const size_t Hk = m->d.Hk, ctx = m->opt.max_context, hd = m->d.hd;
+    const size_t es = m->opt.kv_format == RD_KV_FP16 ? 2 : 1;
+    const size_t lay = (size_t)layer * Hk * ctx * hd * es;
+    r[0] = {(uint8_t*)(which ? m->vc : m->kc) + lay, Hk * ctx * hd * es};
+    if (m->opt.kv_format != RD_KV_INT8_SEG128) return 1;
+    r[1] = {(uint8_t*)(m->stage + ((size_t)layer * 2 + which) * Hk * SEG * hd), Hk * SEG * hd * 2};
+    r[2] = {(uint8_t*)(m->meta + ((size_t)layer * 2 + which) * Hk * m->nseg * 2), Hk * (size_t)m->nseg * 8};
+    return 3;
+}
+}  // namespace
+
+extern "C" rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, void* dst, size_t cap,
+                                        size_t* written) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!dst || seq != 0 || layer < 0 || layer >= m->d.L || which < 0 || which > 1)
+        return fail(RD_ERR_INVALID_ARG, "bad export arguments");
+    KvRegion r[3];
+    const int nr = kv_regions(m, layer, which, r);
+    size_t total = 0;
+    for (int i = 0; i < nr; ++i) total += r[i].bytes;
+    if (cap < total) return fail(RD_ERR_INVALID_ARG, "destination too small: need " + std::to_string(total));
+    HIP_TRY(hipSetDevice(m->dev));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    size_t o = 0;
+    for (int i = 0; i < nr; ++i) {
+        HIP_TRY(hipMemcpy((uint8_t*)dst + o, r[i].dev, r[i].bytes, hipMemcpyDeviceToHost));
+        o += r[i].bytes;
+    }
+    if (written) *written = total;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_debug_import_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, const void* src,
+                                        size_t bytes, int32_t pos) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!src || seq != 0 || layer < 0 || layer >= m->d.L || which < 0 || which > 1 || pos < 0 ||
+        pos > m->opt.max_context)
+        return fail(RD_ERR_INVALID_ARG, "bad import arguments");
+    KvRegion r[3];
+    const int nr = kv_regions(m, layer, which, r);
+    size_t total = 0;
+    for (int i = 0; i < nr; ++i) total += r[i].bytes;
+    if (bytes != total) return fail(RD_ERR_INVALID_ARG, "source must be exactly " + std::to_string(total) + " bytes");
+    HIP_TRY(hipSetDevice(m->dev));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    size_t o = 0;
+    for (int i = 0; i < nr; ++i) {
+        HIP_TRY(hipMemcpy(r[i].dev, (const uint8_t*)src + o, r[i].bytes, hipMemcpyHostToDevice));
+        o += r[i].bytes;
+    }
+    m->host_pos = pos;
+    return RD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// standalone kernels
+// ---------------------------------------------------------------------------
+namespace {
+// Scratch of the standalone attention / argmax entry points, one per device,
+// allocated on first use and kept until the process ends.  Calls that overlap
+// on one device race on it.
+struct Scratch {
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
+    int* cnt = nullptr;     // [Hk max] zero between uses
+    int* pos = nullptr;
+    float* av = nullptr;
+    int* ai = nullptr;
+    int* acnt = nullptr;
+};
+constexpr int SCR_HEADS = 128, SCR_HD = 128, SCR_ARG = 1024;
+std::mutex g_scr_mu;
+Scratch g_scr[64];
+
+hipError_t get_scratch(Scratch** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    Scratch& s = g_scr[dev];
+    if (!s.part_o) {
+        const size_t po = (size_t)SCR_HEADS * MAX_SPLITS * SCR_HD * 4, pml = (size_t)SCR_HEADS * MAX_SPLITS * 8;
+        const size_t tail = SCR_HEADS * 4 + 256 + SCR_ARG * 8 + 256;
+        void* p = nullptr;
+        if ((e = hipMalloc(&p, po + pml + tail)) != hipSuccess) return e;
+        if ((e = hipMemset(p, 0, po + pml + tail)) != hipSuccess) return e;
+        uint8_t* b = (uint8_t*)p;
+        s.part_o = (float*)b;
+        s.part_ml = (float*)(b + po);
+        s.cnt = (int*)(b + po + pml);
+        s.pos = s.cnt + SCR_HEADS;
+        s.av = (float*)(s.pos + 64);
+        s.ai = (int*)(s.av + SCR_ARG);
+        s.acnt = s.ai + SCR_ARG;
+    }
+    *out = &s;
+    return hipSuccess;
+}
+}  // namespace
+
+#define K_TRY(expr)                                                                                  \
+    do {                                                                                             \
+        hipError_t e_ = (expr);                                                                      \
+        if (e_ != hipSuccess) return fail(RD_ERR_DEVICE, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+extern "C" rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t K, int32_t batch,
+                                 void* stream) {
+    if (!W || !x || !y) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (N < 1 || K < 8 || K % 8 || K > 8192) return fail(RD_ERR_INVALID_ARG, "need N >= 1, 8 <= K <= 8192, K % 8 == 0");
+    if (batch != 1) return fail(RD_ERR_UNSUPPORTED, "batch must be 1");
+    if (((uintptr_t)W | (uintptr_t)x) & 15) return fail(RD_ERR_INVALID_ARG, "W and x must be 16-byte aligned");
+    K_TRY(launch_gemv_f16(W, x, y, N, K, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void* Vc, float* out, int32_t H,
+                                      int32_t Hk, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
+                                      void* stream) {
+    if (!q || !Kc || !Vc || !out) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (hd != 64 && hd != 128) return fail(RD_ERR_INVALID_ARG, "hd must be 64 or 128");
+    if (H < 1 || Hk < 1 || H % Hk || H > SCR_HEADS) return fail(RD_ERR_INVALID_ARG, "bad head counts");
+    const int G = H / Hk;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RD_ERR_INVALID_ARG, "n_heads/n_kv_heads must be 1, 2, 4 or 8");
+    if (L < 1 || L > ld) return fail(RD_ERR_INVALID_ARG, "need 1 <= L <= ld");
+    if (splits < 1 || splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "splits out of range");
+    if (((uintptr_t)q | (uintptr_t)Kc | (uintptr_t)Vc) & 15) return fail(RD_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    Scratch* s = nullptr;
+    K_TRY(get_scratch(&s));
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, st, s->pos, L - 1);
+    K_TRY(hipGetLastError());
+    AttnArgs A{};
+    A.q = q;
+    A.out = out;
+    A.kc = const_cast<void*>(Kc);
+    A.vc = const_cast<void*>(Vc);
+    A.part_o = s->part_o;
+    A.part_ml = s->part_ml;
+    A.cnt = s->cnt;
+    A.pos_ptr = s->pos;
+    A.ld = ld;
+    A.nseg = 0;
+    A.H = H;
+    A.Hk = Hk;
+    A.S = splits;
+    A.scale = scale;
+    K_TRY(launch_attention_f16(A, hd, G, st));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* stream) {
+    if ((!in || !out) && n) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    K_TRY(launch_e5m2(in, out, n, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uint8_t* codes, float* meta,
+                                  void* stream) {
+    if (!in || !codes || !meta) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (n_seg < 0 || seg_elems < 8 || seg_elems % 8 || seg_elems > 65536)
+        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, seg_elems a multiple of 8 in [8, 65536]");
+    if (((uintptr_t)in | (uintptr_t)codes) & 15) return fail(RD_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    K_TRY(launch_seg_quant(in, n_seg, seg_elems, codes, meta, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_argmax_f32(const float* v, int32_t n, int32_t* out, void* stream) {
+    if (!v || !out) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (n < 1) return fail(RD_ERR_INVALID_ARG, "n must be >= 1");
+    Scratch* s = nullptr;
+    K_TRY(get_scratch(&s));
+    K_TRY(launch_argmax(v, n, out, s->av, s->ai, s->acnt, (hipStream_t)stream));
+    return RD_OK;
+}

@@ -1,0 +1,143 @@
+"""GPU parity of the step's kernels, called alone through the C ABI, against
+the oracle on identical inputs."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def rd():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import request_decode_amd as rd
+    rd.lib()
+    return rd
+
+
+def dev(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (7, 264), (1000, 2056), (4096, 2048), (6144, 2048), (11264, 2048),
+                                 (2048, 5632), (16384, 4096), (333, 8192)])
+def test_gemv_vs_oracle(rd, orc, N, K):
+    import torch
+    print(f"gemv N={N} K={K}", flush=True)
+    W, X = synth.gemv_inputs(N, K, 1, seed_w=N + K, seed_x=K)
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    Wd, Xd = dev(W), dev(X[0])
+    rd.rd_gemv_f16(Wd.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K)
+    sync()
+    got = y.cpu().numpy().astype(np.float64)
+    ref = orc.gemv(W, X[0].astype(np.float64))
+    # fp16 x fp16 products are exact in fp32; only the fp32 summation rounds:
+    # |err| <= K * 2^-24 * sum|w x| (first-order worst case)
+    mag = np.abs(W.astype(np.float64)) @ np.abs(X[0].astype(np.float64))
+    bound = (K + 2) * 2.0 ** -24 * mag + 1e-30
+    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
+
+
+def _attn_case(H, Hk, hd, L, ld, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, hd)).astype(np.float32)
+    K = (rng.standard_normal((Hk, ld, hd)) * 1.5).astype(np.float16)
+    V = rng.standard_normal((Hk, ld, hd)).astype(np.float16)
+    return q, K, V
+
+
+@pytest.mark.parametrize("H,Hk,hd,L,splits", [(16, 8, 128, 1, 64), (16, 8, 128, 63, 64), (16, 8, 128, 65, 1),
+                                              (16, 8, 128, 768, 64), (16, 8, 128, 768, 7), (16, 8, 128, 5000, 64),
+                                              (4, 4, 64, 32, 64), (4, 4, 64, 1000, 3), (8, 2, 128, 300, 16),
+                                              (16, 2, 64, 200, 5), (16, 8, 128, 32896, 64)])
+def test_attention_vs_oracle(rd, orc, H, Hk, hd, L, splits):
+    import torch
+    print(f"attention H={H} Hk={Hk} hd={hd} L={L} S={splits}", flush=True)
+    ld = L + 37
+    q, K, V = _attn_case(H, Hk, hd, L, ld, seed=L + H)
+    out = torch.empty((H, hd), dtype=torch.float32, device="cuda")
+    qd, Kd, Vd = dev(q), dev(K), dev(V)
+    rd.rd_attention_f16(qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), out.data_ptr(), H, Hk, hd, L, ld,
+                        float(1.0 / np.sqrt(hd)), splits)
+    sync()
+    got = out.cpu().numpy().astype(np.float64)
+    G = H // Hk
+    heads = range(H) if L <= 5000 else (0, 7, 15)
+    for h in heads:
+        g = h // G
+        ref = orc.attention(q[h].astype(np.float64), K[g, :L].astype(np.float64), V[g, :L].astype(np.float64))
+        assert np.allclose(got[h], ref, rtol=2e-5, atol=2e-5), (h, np.abs(got[h] - ref).max())
+
+
+def test_attention_length_one_is_v0(rd):
+    import torch
+    q, K, V = _attn_case(16, 8, 128, 1, 4, seed=5)
+    out = torch.empty((16, 128), dtype=torch.float32, device="cuda")
+    qd, Kd, Vd = dev(q), dev(K), dev(V)
+    rd.rd_attention_f16(qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), out.data_ptr(), 16, 8, 128, 1, 4, 0.088, 64)
+    sync()
+    got = out.cpu().numpy()
+    for h in range(16):
+        assert np.array_equal(got[h], V[h // 2, 0].astype(np.float32))
+
+
+def test_e5m2_exhaustive_bit_exact(rd, orc):
+    import torch
+    h = np.arange(65536, dtype=np.uint16)
+    inp = dev(h.view(np.int16))
+    out = torch.empty(65536, dtype=torch.uint8, device="cuda")
+    rd.rd_e5m2_encode(inp.data_ptr(), out.data_ptr(), 65536)
+    sync()
+    assert np.array_equal(out.cpu().numpy(), orc.e5m2_from_h(h))
+
+
+def test_seg_quant_bit_exact(rd, orc):
+    import torch
+    g = json.load(open(os.path.join(GOLD, "segment_quant_example.json")))
+    rng = np.random.default_rng(11)
+    segs = []
+    for lo, hi in [(g["min"], g["max"]), (g["exact_tie"]["min"], g["exact_tie"]["max"]), (-3, -0.5), (0.2, 9),
+                   (-60000, 60000), (-1e-3, 2e-3), (-0.7, 0.7), (-5, 5)]:
+        x = rng.uniform(lo, hi, 128 * 128).astype(np.float16)
+        x[17] = np.float16(lo)
+        x[-9] = np.float16(hi)
+        segs.append(x)
+    segs.append(rng.standard_normal(128 * 128).astype(np.float16))
+    segs.append(np.full(128 * 128, 0.25, np.float16))
+    data = np.stack(segs)
+    n_seg, n = data.shape
+    inp = dev(data.view(np.int16))
+    codes = torch.empty((n_seg, n), dtype=torch.uint8, device="cuda")
+    meta = torch.empty((n_seg, 2), dtype=torch.float32, device="cuda")
+    rd.rd_seg_quant(inp.data_ptr(), n_seg, n, codes.data_ptr(), meta.data_ptr())
+    sync()
+    c, m = codes.cpu().numpy(), meta.cpu().numpy()
+    for i in range(n_seg):
+        rc, rs, rz = orc.seg_quant(data[i].view(np.uint16))
+        assert m[i, 0] == rs and m[i, 1] == rz, (i, m[i], rs, rz)
+        assert np.array_equal(c[i], rc), i
+    assert m[1, 1] == g["exact_tie"]["zero_point"] and m[0, 1] == g["zero_point_approx"]
+
+
+def test_argmax_exact(rd, orc):
+    import torch
+    rng = np.random.default_rng(3)
+    for n in (1, 5, 255, 4096, 32000, 100003):
+        v = rng.integers(-20, 20, n).astype(np.float32) * np.float32(0.5)
+        vd = dev(v)
+        out = torch.empty(1, dtype=torch.int32, device="cuda")
+        rd.rd_argmax_f32(vd.data_ptr(), n, out.data_ptr())
+        sync()
+        assert int(out.item()) == orc.argmax(v.astype(np.float64)), n
