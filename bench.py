@@ -1,0 +1,194 @@
+"""Decode-speed benchmark of the batch-1 decode step on one MI355X.
+
+Workload (default): the 2B-class dense model (24 layers, d_model 2048, 16
+query heads x 128, 8 KV heads, SwiGLU 5632, vocab 32000, untied LM head,
+fp16 weights N(0, 0.02), gains 1), a 512-token random prompt fed by
+teacher-forced decode steps (untimed), then greedy decode steps with the
+token fed back on the device.  A "step" is one whole decode step (all
+layers, LM head, argmax).  Timed: exactly --steps steps at positions
+511 .. 511+steps-1 (the configuration's 256 steps at context 512..767),
+after --warmup untimed steps over the same positions (rewound afterwards).
+
+With the persistent executor the dominant kernel is the persistent decode
+kernel itself: one launch runs all timed steps, so its algorithmic bytes
+per launch are the sum over those steps of every streamed weight byte plus
+the K/V bytes each step reads.  The prompt is fed with the graph executor,
+so the only persistent launches are the warmup and the timed one (equal
+size: the profiler's average duration for the kernel is the timed launch's).
+
+Prints one JSON line (rank 0, N = 1).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+PROMPT = 512
+
+
+def step_bytes(shape, L: float) -> float:
+    """Algorithmic HBM bytes of one decode step attending to L positions:
+    every streamed weight once (all layer matrices and gains, the final gain,
+    the LM head, one embedding row) plus the fp16 K and V rows read."""
+    D, H, Hk, hd, F, V, NL = (shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
+                              shape.vocab, shape.n_layers)
+    per_layer = ((H + 2 * Hk) * hd * D + D * H * hd + 2 * F * D + D * F + 2 * D) * 2
+    weights = NL * per_layer + (D + V * D + D) * 2
+    kv = NL * 2 * Hk * hd * 2 * L
+    return weights + kv
+
+
+def cpu_baseline(blob, shape, seconds: float):
+    """Oracle tokens/s on the machine's host cores: a short prompt, then decode
+    steps until `seconds` of CPU work have run (at least 3, at most 64)."""
+    cores = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    import oracle
+    import synth
+    om = oracle.OracleModel(blob, 128, kv_format="fp16")
+    toks = synth.prompt(103, 4, shape.vocab)
+    for t in toks[:-1]:
+        om.step([t])
+    t = int(toks[-1])
+    n, t0 = 0, time.perf_counter()
+    while True:
+        _, nxt = om.step([t])
+        t = int(nxt[0])
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= 3) or n >= 64:
+            break
+    om.close()
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"2B model, 3-token prompt then {n} greedy decode steps (positions 3..{3 + n - 1}); "
+                      f"the oracle's per-step cost is dominated by the 2.4 GB of weights, as on the GPU "
+                      f"(KV at L<=768 adds <3%)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=None, help="default: --steps (one equal-size warmup launch)")
+    ap.add_argument("--kv", default="fp16", choices=["fp16", "e5m2", "int8"])
+    ap.add_argument("--executor", default="auto", choices=["auto", "graph", "eager", "persistent"])
+    ap.add_argument("--phase-iters", type=int, default=96)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+              "multi-GPU sharding is designed but not built", file=sys.stderr)
+        sys.exit(2)
+    if args.warmup is None:
+        args.warmup = args.steps
+    if args.steps < 1 or args.steps + PROMPT > 4096 or args.warmup < 0 or args.warmup + PROMPT > 4096:
+        sys.exit("bench.py: --steps/--warmup must keep the context within 4096")
+
+    import torch
+
+    import request_decode_amd as rd
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    shape = synth.SHAPES["2b"]
+    t0 = time.time()
+    blob = synth.make_blob(shape, seed=2)
+    print(f"[bench] blob {blob.size / 1e9:.3f} GB generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    prompt = synth.prompt(103, PROMPT, shape.vocab)
+    ctx = PROMPT + max(args.steps, args.warmup)
+    m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream)
+    executor = m.get_info().executor
+    persistent = executor == rd.RD_EXEC_PERSISTENT
+    if persistent:
+        m.set_executor("graph")          # the prompt goes through the graph executor
+    for t in prompt[:-1]:
+        m.decode_step(int(t), want_logits=False)
+    if persistent:
+        m.set_executor("persistent")
+    first = int(prompt[-1])
+    base = PROMPT - 1
+    out = torch.empty(max(args.steps, args.warmup, 1), dtype=torch.int32, device="cuda")
+    if args.warmup:
+        m.generate(first, args.warmup)
+        m.set_position(base)
+    print(f"[bench] prompt fed, warmup {args.warmup} done", file=sys.stderr, flush=True)
+
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    m.generate_async(first, args.steps, out.data_ptr())
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    m.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / args.steps
+    tok_s = args.steps / (ms / 1e3)
+    Ls = [base + 1 + i for i in range(args.steps)]
+    bytes_run = sum(step_bytes(shape, L) for L in Ls)
+    bytes_step = bytes_run / args.steps
+    gbps = bytes_run / (ms / 1e3) / 1e9
+    print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
+          f"{gbps:.0f} GB/s (wall {wall * 1e3 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+
+    # the gate/up GEMV phase kernel of the graph executor, timed alone,
+    # rotating over the 24 layers so that its weights come from HBM
+    m.set_position(base + args.steps // 2)
+    m.run_phase(3, 0, 24)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    m.run_phase(3, 0, args.phase_iters)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    m.synchronize()
+    k_us = e0.elapsed_time(e1) * 1e3 / args.phase_iters
+    k_bytes = (2 * shape.d_ff * shape.d_model + shape.d_model) * 2
+    k_gbps = k_bytes / (k_us * 1e-6) / 1e9
+    print(f"[bench] gate/up phase kernel: {k_us:.2f} us/launch, {k_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    m.close()
+
+    if persistent:
+        roof = {"bound": "hbm", "kernel": "k_persist (whole decode steps, one launch for all timed steps)",
+                "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_launch": int(bytes_run), "us_per_launch": round(ms * 1e3, 1)}
+    else:
+        roof = {"bound": "hbm", "kernel": "k_gateup (RMSNorm + gate/up GEMV + SwiGLU)",
+                "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_launch": k_bytes, "us_per_launch": round(k_us, 3)}
+    res = {
+        "metric": "batch-1 decode tokens/s (2B-class fp16 model, 512-token prompt + 256 greedy steps)",
+        "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic: seeded N(0,0.02) fp16 weights, uniform random prompt ids",
+        "config": {"workload": "2b-dense-decode", "layers": 24, "d_model": 2048, "heads": 16, "kv_heads": 8,
+                   "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": 1,
+                   "kv_cache": args.kv, "executor": ["auto", "eager", "graph", "persistent"][executor],
+                   "positions": [base, base + args.steps - 1]},
+        "hbm_gbps": round(gbps, 1), "mbu": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": int(bytes_step),
+        "roofline": roof,
+        "gateup_phase_kernel": {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(blob, shape, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -166,6 +166,40 @@ rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer, int32_t wh
 rd_status rd_debug_import_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, const void* src,
                              size_t bytes, int32_t pos);
 
+/* Switch the executor of a live model (the cache and position are kept):
+ * EAGER and GRAPH are always available; PERSISTENT only where the model
+ * was created with AUTO or PERSISTENT and its shape has a persistent kernel.
+ * Errors: INVALID_ARG, UNSUPPORTED. */
+rd_status rd_set_executor(rd_model* m, int32_t executor);
+
+/* Rewind every sequence to position pos <= the current position; rows at
+ * pos and later become unreachable and are rewritten by the next steps.
+ * With the INT8 cache pos must be a multiple of 128 or lie in the segment
+ * still open (rows of an older open segment are gone once sealed).
+ * Errors: INVALID_ARG. */
+rd_status rd_set_position(rd_model* m, int32_t pos);
+
+/* Enqueue `iters` launches of one phase kernel of the step, exactly as the
+ * step launches it, for layers (layer + i) % n_layers, at the current
+ * position: phase 0 = RMSNorm+QKV+RoPE+append (layers >= 1 variant),
+ * 1 = split-K attention + merge, 2 = output projection + residual,
+ * 3 = RMSNorm + gate/up + SwiGLU, 4 = down projection + residual.  For
+ * timing single kernels on the model's stream; it overwrites activations
+ * and the current cache row, so call rd_set_position before decoding again.
+ * Errors: INVALID_ARG, DEVICE. */
+rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t layer, int32_t iters);
+
+/* One decode step of `token` with the persistent executor, recording an
+ * event trace of workgroup 0: ts (host, cap uint64 words) receives
+ * [n, code_0, clock_0, code_1, clock_1, ...] with clock the constant 100 MHz
+ * wall clock and code = 10 * phase + point (phase 0 QKV, 1 attention,
+ * 2 output projection, 3 gate/up, 4 down, 5 LM head; point 0 barrier wait
+ * done, 1 input staged, 2 phase work done, 3 arrival counted, 4 next weight
+ * loads issued; 99 kernel start, 98 end).  *n receives the event count
+ * (at most (cap-1)/2).  Synchronises.  Errors: UNSUPPORTED for other
+ * executors, INVALID_ARG, CONTEXT_FULL, DEVICE. */
+rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n);
+
 const char* rd_last_error(void);
 
 /* ---- kernels of the step, callable alone (device pointers) ------------------
@@ -204,6 +238,16 @@ rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* strea
  * meta: device f32 [n_seg][2] (scale, zp).  seg_elems <= 65536. */
 rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uint8_t* codes, float* meta,
                        void* stream);
+
+/* Average latency in microseconds of one grid barrier (one workgroup per
+ * CU), measured over n back-to-back barriers with HIP events on the null
+ * stream of `device` ("Real-time LLM inference on standard GPUs", loss
+ * table: grid synchronisation between phases).  mode selects the scheme:
+ * 0 two-level counter tree with resets and a generation word, 1 one
+ * monotonic counter, 2 monotonic two-level counter tree, 3 packed
+ * per-workgroup epoch flags polled by every workgroup, 4 the same with one
+ * flag per cache line.  Errors: INVALID_ARG, DEVICE. */
+rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t mode, float* us_per_barrier);
 
 /* *out = index of the largest of v[0..n) (lowest index on ties).
  * v: device f32 [n]; out: device i32 [1]. */

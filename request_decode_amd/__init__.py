@@ -69,12 +69,17 @@ SIGNATURES = [
     ("rd_synchronize", _I32, [_VP]),
     ("rd_debug_export_kv", _I32, [_VP, _I32, _I32, _I32, _VP, _SZ, C.POINTER(_SZ)]),
     ("rd_debug_import_kv", _I32, [_VP, _I32, _I32, _I32, _VP, _SZ, _I32]),
+    ("rd_set_position", _I32, [_VP, _I32]),
+    ("rd_set_executor", _I32, [_VP, _I32]),
+    ("rd_debug_run_phase", _I32, [_VP, _I32, _I32, _I32]),
+    ("rd_debug_trace_step", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
     ("rd_last_error", C.c_char_p, []),
     ("rd_gemv_f16", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
     ("rd_seg_quant", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
     ("rd_argmax_f32", _I32, [_VP, _I32, _VP, _VP]),
+    ("rd_debug_barrier_probe", _I32, [_I32, _I32, _I32, _FP]),
 ]
 
 _lib = None
@@ -130,6 +135,7 @@ class Model:
         o.attn_splits = attn_splits
         blob = np.ascontiguousarray(blob, dtype=np.uint8)
         h = _VP()
+        self._destroy = L.rd_model_destroy
         check(L.rd_model_create(blob.ctypes.data, blob.size, C.byref(o), C.byref(h)))
         self._h = h
         self.info = self.get_info()
@@ -137,9 +143,10 @@ class Model:
         self.kv_format = kv_format
 
     def close(self):
-        if getattr(self, "_h", None):
-            lib().rd_model_destroy(self._h)
+        h = getattr(self, "_h", None)
+        if h:
             self._h = None
+            self._destroy(h)   # held on the instance: usable during interpreter shutdown
 
     __del__ = close
 
@@ -155,6 +162,25 @@ class Model:
         p = C.c_int32()
         check(lib().rd_get_position(self._h, C.byref(p)))
         return p.value
+
+    def set_position(self, pos: int):
+        check(lib().rd_set_position(self._h, pos))
+
+    def set_executor(self, executor: str):
+        check(lib().rd_set_executor(self._h, EXECUTORS[executor]))
+        self.info = self.get_info()
+
+    def run_phase(self, phase: int, layer: int, iters: int):
+        check(lib().rd_debug_run_phase(self._h, phase, layer, iters))
+
+    def trace_step(self, token: int, max_events: int = 4096):
+        """Event trace of one persistent step: (codes, clocks in 10 ns ticks)."""
+        cap = 1 + 2 * max_events
+        ts = np.zeros(cap, np.uint64)
+        n = C.c_int32()
+        check(lib().rd_debug_trace_step(self._h, token, ts.ctypes.data_as(C.POINTER(C.c_uint64)), cap, C.byref(n)))
+        ev = ts[1:1 + 2 * n.value].reshape(-1, 2).astype(np.int64)
+        return ev[:, 0], ev[:, 1]
 
     def decode_step(self, token: int, want_logits: bool = True, allow_numeric: bool = False):
         t, tp = _i32([token])
@@ -237,3 +263,9 @@ def rd_seg_quant(inp: int, n_seg: int, seg_elems: int, codes: int, meta: int, st
 
 def rd_argmax_f32(v: int, n: int, out: int, stream: int = 0):
     check(lib().rd_argmax_f32(v, n, out, stream or None))
+
+
+def rd_debug_barrier_probe(device: int = 0, n: int = 10000, mode: int = 0) -> float:
+    us = C.c_float()
+    check(lib().rd_debug_barrier_probe(device, n, mode, C.byref(us)))
+    return us.value

@@ -143,6 +143,12 @@ struct rd_model {
 
     hipGraph_t graph = nullptr;
     hipGraphExec_t gexec = nullptr;
+
+    // persistent executor
+    int* bar = nullptr;             // grid-barrier words (zero between launches)
+    LayerW* layers_dev = nullptr;   // per-layer weight pointers on the device
+    int nwg = 0;                    // workgroups of the cooperative launch
+    unsigned gen = 0;               // barrier generation the next launch starts from
 };
 
 static rd_status dev_fail(rd_model* m, const char* what, hipError_t e) {
@@ -185,6 +191,8 @@ void free_model(rd_model* m) {
     (void)hipFree(m->stage);
     (void)hipFree(m->meta);
     (void)hipFree(m->act);
+    (void)hipFree(m->bar);
+    (void)hipFree(m->layers_dev);
     if (m->gen_host) (void)hipHostFree(m->gen_host);
     if (m->logits_host) (void)hipHostFree(m->logits_host);
     if (m->state_host) (void)hipHostFree(m->state_host);
@@ -193,7 +201,29 @@ void free_model(rd_model* m) {
     delete m;
 }
 
+// Watchdog of the persistent kernel's barrier waits: polls of about 60 ns.
+constexpr int kSpinLimit = 1 << 24;
+
+// One cooperative launch decoding n steps from the current device state.
+rd_status persistent_enqueue(rd_model* m, int n, int out_base, unsigned long long* trace = nullptr,
+                             int trace_cap = 0) {
+    PersistArgs P{};
+    P.trace = trace;
+    P.trace_cap = trace_cap;
+    P.layers = m->layers_dev;
+    P.bar = m->bar;
+    P.gen0 = m->gen;
+    P.pos0 = m->host_pos;
+    P.n_steps = n;
+    P.out_base = out_base;
+    P.spin_limit = kSpinLimit;
+    HIP_TRY(launch_persistent(m->A, P, m->nwg, m->stream));
+    m->gen += persistent_barriers(m->d.L, n);
+    return RD_OK;
+}
+
 rd_status step_enqueue(rd_model* m) {
+    if (m->opt.executor == RD_EXEC_PERSISTENT) return persistent_enqueue(m, 1, 0);
     if (m->opt.executor == RD_EXEC_EAGER) {
         HIP_TRY(launch_step(m->A, m->stream));
         return RD_OK;
@@ -235,8 +265,6 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     if (opt.kv_format < RD_KV_FP16 || opt.kv_format > RD_KV_INT8_SEG128)
         return fail(RD_ERR_INVALID_ARG, "bad kv_format");
     if (opt.executor < RD_EXEC_AUTO || opt.executor > RD_EXEC_PERSISTENT) return fail(RD_ERR_INVALID_ARG, "bad executor");
-    if (opt.executor == RD_EXEC_PERSISTENT) return fail(RD_ERR_UNSUPPORTED, "persistent executor not built");
-    if (opt.executor == RD_EXEC_AUTO) opt.executor = RD_EXEC_GRAPH;
     if (opt.attn_splits < 0 || opt.attn_splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "attn_splits out of range");
 
     BlobDims d;
@@ -385,7 +413,8 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     const size_t o_x = carve(D * 4), o_q = carve(H * hd * 4), o_a = carve(H * hd * 4), o_m = carve(F * 4);
     const size_t o_logits = carve(V * 4);
     const size_t o_po = carve(H * MAX_SPLITS * hd * 4), o_pml = carve(H * MAX_SPLITS * 2 * 4);
-    const size_t o_cnt = carve(Hk * 4), o_av = carve(n_lm_wg * 4), o_ai = carve(n_lm_wg * 4), o_ac = carve(4);
+    const int n_arg = n_lm_wg > 1024 ? n_lm_wg : 1024;   // argmax partials: LM-head or persistent grid
+    const size_t o_cnt = carve(Hk * 4), o_av = carve(n_arg * 4), o_ai = carve(n_arg * 4), o_ac = carve(64 * 4);
     const size_t o_st = carve(sizeof(StepState)), o_gen = carve(ctx * 4);
     const size_t o_rope = carve(ctx * (hd / 2) * sizeof(float2));
     CREATE_TRY(hipMalloc(&m->act, a));
@@ -420,6 +449,25 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     A.st = (StepState*)(X + o_st); A.gen_out = (int*)(X + o_gen);
     A.rope = (const float2*)(X + o_rope);
     A.kc = m->kc; A.vc = m->vc; A.stage = m->stage; A.meta = m->meta; A.nseg = m->nseg;
+
+    // ---- executor: the persistent kernel where its shape is built, else the graph
+    if (opt.executor == RD_EXEC_AUTO || opt.executor == RD_EXEC_PERSISTENT) {
+        int nwg = 0;
+        if (persistent_supported(A) && persistent_max_grid(A, m->dev, &nwg) == hipSuccess && nwg > 0 &&
+            nwg <= n_arg) {
+            CREATE_TRY(hipMalloc(&m->bar, BAR_WORDS * sizeof(int)));
+            CREATE_TRY(hipMemset(m->bar, 0, BAR_WORDS * sizeof(int)));
+            CREATE_TRY(hipMalloc(&m->layers_dev, m->layers.size() * sizeof(LayerW)));
+            CREATE_TRY(hipMemcpy(m->layers_dev, m->layers.data(), m->layers.size() * sizeof(LayerW),
+                                 hipMemcpyHostToDevice));
+            m->nwg = nwg;
+            m->opt.executor = RD_EXEC_PERSISTENT;
+        } else if (opt.executor == RD_EXEC_PERSISTENT) {
+            return bail(fail(RD_ERR_UNSUPPORTED, "no persistent kernel is built for this model shape"));
+        } else {
+            m->opt.executor = RD_EXEC_GRAPH;
+        }
+    }
 #undef CREATE_TRY
     *out = m;
     return RD_OK;
@@ -453,8 +501,77 @@ extern "C" rd_status rd_get_position(const rd_model* m, int32_t* pos) {
     return RD_OK;
 }
 
+extern "C" rd_status rd_set_executor(rd_model* m, int32_t executor) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (executor != RD_EXEC_EAGER && executor != RD_EXEC_GRAPH && executor != RD_EXEC_PERSISTENT)
+        return fail(RD_ERR_INVALID_ARG, "executor must be EAGER, GRAPH or PERSISTENT");
+    if (executor == RD_EXEC_PERSISTENT && !m->bar)
+        return fail(RD_ERR_UNSUPPORTED, "this model has no persistent kernel");
+    m->opt.executor = executor;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_set_position(rd_model* m, int32_t pos) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (pos < 0 || pos > m->host_pos) return fail(RD_ERR_INVALID_ARG, "position must be in [0, current]");
+    if (m->opt.kv_format == RD_KV_INT8_SEG128 && pos % SEG != 0 && pos / SEG != m->host_pos / SEG)
+        return fail(RD_ERR_INVALID_ARG, "INT8 cache: rewind only to a segment start or inside the open segment");
+    m->host_pos = pos;
+    return RD_OK;
+}
+
+static rd_status finish_sync(rd_model* m);
+
+extern "C" rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n_out) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!ts || !n_out) return fail(RD_ERR_INVALID_ARG, "NULL argument");
+    if (m->opt.executor != RD_EXEC_PERSISTENT) return fail(RD_ERR_UNSUPPORTED, "tracing needs the persistent executor");
+    if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
+    if (token < 0 || token >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (cap < 3) return fail(RD_ERR_INVALID_ARG, "trace capacity must be >= 3");
+    const int events = (cap - 1) / 2;
+    const size_t words = 1 + 2 * (size_t)events;
+    HIP_TRY(hipSetDevice(m->dev));
+    unsigned long long* dev = nullptr;
+    HIP_TRY(hipMalloc(&dev, words * 8));
+    HIP_TRY(hipMemset(dev, 0, words * 8));
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, token, 1);
+    HIP_TRY(hipGetLastError());
+    if ((st = persistent_enqueue(m, 1, 0, dev, events))) {
+        (void)hipFree(dev);
+        return st;
+    }
+    HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    m->host_pos += 1;
+    st = finish_sync(m);
+    HIP_TRY(hipMemcpy(ts, dev, words * 8, hipMemcpyDeviceToHost));
+    (void)hipFree(dev);
+    *n_out = (int32_t)ts[0];
+    return st;
+}
+
+extern "C" rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t layer, int32_t iters) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (phase < 0 || phase > 4 || layer < 0 || layer >= m->d.L || iters < 0)
+        return fail(RD_ERR_INVALID_ARG, "bad phase/layer/iters");
+    if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
+    HIP_TRY(hipSetDevice(m->dev));
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, 0, 1);
+    HIP_TRY(hipGetLastError());
+    for (int i = 0; i < iters; ++i) HIP_TRY(launch_phase(m->A, phase, (layer + i) % m->d.L, m->stream));
+    return RD_OK;
+}
+
 static rd_status finish_sync(rd_model* m) {
     HIP_TRY(hipStreamSynchronize(m->stream));
+    if (m->state_host->err & ERR_BARRIER) {
+        m->poisoned = true;
+        return fail(RD_ERR_DEVICE, "a grid barrier of the persistent kernel timed out");
+    }
     if (m->state_host->err & ERR_TOKEN) return fail(RD_ERR_NUMERIC, "token id out of range seen on the device");
     if (m->state_host->err & ERR_NONFINITE) return fail(RD_ERR_NUMERIC, "non-finite logit");
     return RD_OK;
@@ -493,6 +610,16 @@ static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t bat
     HIP_TRY(hipSetDevice(m->dev));
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, first[0], 1);
     HIP_TRY(hipGetLastError());
+    if (m->opt.executor == RD_EXEC_PERSISTENT) {
+        // whole runs of steps in one launch, in chunks that keep one kernel short
+        constexpr int kChunk = 512;
+        for (int done = 0; done < n; done += kChunk) {
+            const int c = n - done < kChunk ? n - done : kChunk;
+            if ((st = persistent_enqueue(m, c, done))) return st;
+            m->host_pos += c;
+        }
+        return RD_OK;
+    }
     for (int i = 0; i < n; ++i)
         if ((st = step_enqueue(m))) return st;
     m->host_pos += n;
@@ -704,6 +831,21 @@ extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg
         return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, seg_elems a multiple of 8 in [8, 65536]");
     if (((uintptr_t)in | (uintptr_t)codes) & 15) return fail(RD_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
     K_TRY(launch_seg_quant(in, n_seg, seg_elems, codes, meta, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t mode, float* us) {
+    if (!us || n < 1 || n > (1 << 20)) return fail(RD_ERR_INVALID_ARG, "need us != NULL and 1 <= n <= 2^20");
+    if (mode < 0 || mode > 6) return fail(RD_ERR_INVALID_ARG, "mode must be 0..6");
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
+        return fail(RD_ERR_INVALID_ARG, "bad device");
+    K_TRY(hipSetDevice(device));
+    hipDeviceProp_t prop;
+    K_TRY(hipGetDeviceProperties(&prop, device));
+    int errbits = 0;
+    K_TRY(barrier_probe(prop.multiProcessorCount, n, mode, us, &errbits));
+    if (errbits & ERR_BARRIER) return fail(RD_ERR_DEVICE, "a probe barrier timed out");
     return RD_OK;
 }
 

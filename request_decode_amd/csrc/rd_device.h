@@ -57,12 +57,46 @@ __device__ __forceinline__ _Float16 e5m2_decode(uint8_t e) {
 }
 __device__ __forceinline__ uint16_t f2h_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
-// ---- agent-scope communication -----------------------------------------------
-__device__ __forceinline__ int atomic_add_acqrel(int* p, int v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_relaxed(int* p, int v) {
+// ---- cross-workgroup exchange inside one kernel --------------------------------
+// The L2 is per XCD, so data one workgroup hands to another must not sit in
+// a non-coherent L2 line.  An agent-scope release/acquire fence would write
+// back and invalidate the whole L2 of the XCD (buffer_wbl2 / buffer_inv),
+// far too costly once per workgroup.  Instead the exchanged words are
+// written and read with agent-scope (sc1) relaxed atomic stores and loads,
+// which are coherent across XCDs on their own; the only ordering needed is
+// that a workgroup's stores have completed (vmcnt drained) before its
+// arrival is counted, and that the reader's loads are issued after it saw
+// the final count.
+__device__ __forceinline__ void st_agent(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding vector-memory operations completed.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Count this workgroup's arrival on *cnt after all of its threads' st_agent
+// stores completed; true in every thread of the workgroup that arrives
+// last of `expected`.  The last one resets the counter for the next use
+// (which must come after a kernel boundary).
+__device__ __forceinline__ bool arrive_last(int* cnt, int expected) {
+    __shared__ int s_last;
+    drain_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old == expected - 1);
+        if (s_last) st_agent(cnt, 0);
+    }
+    __syncthreads();
+    return s_last != 0;
 }
 
 }  // namespace rd

@@ -77,8 +77,42 @@ struct StepArgs {
     int nseg;
 };
 
+// Persistent executor (rd_persistent.hip).
+enum { ERR_BARRIER = 4 };
+constexpr int BAR_SUB = 16;                       // barrier sub-counters
+constexpr int BAR_STRIDE = 32;                    // ints between barrier words (128-byte lines)
+constexpr int BAR_FLAGS = (BAR_SUB + 3) * BAR_STRIDE;       // per-workgroup flag words start here
+constexpr int BAR_MAX_WG = 1024;
+constexpr int BAR_WORDS = BAR_FLAGS + BAR_MAX_WG * BAR_STRIDE;
+struct PersistArgs {
+    const LayerW* layers;     // device copy of the per-layer weight pointers
+    int* bar;                 // [BAR_WORDS]: sub-counters, top counter, generation, abort flag
+    unsigned gen0;            // barrier generation when the launch starts
+    int pos0;                 // position of the first step
+    int n_steps;              // steps decoded by this launch
+    int out_base;             // gen_out index of the first step's token
+    int spin_limit;           // polls before a barrier wait gives up (watchdog)
+    unsigned long long* trace;  // optional event trace of workgroup 0: [0] = count, then
+                                // (code, wall clock at 100 MHz) pairs
+    int trace_cap;              // events the trace buffer holds
+};
+// Trace event codes: 10 * phase + point; phases 0 QKV, 1 attention, 2 output
+// projection, 3 gate/up, 4 down, 5 LM head; points 0 barrier wait done,
+// 1 input staged, 2 phase work done, 3 arrival counted, 4 next loads issued.
+enum { TR_WAIT = 0, TR_STAGED = 1, TR_DONE = 2, TR_ARRIVED = 3, TR_ISSUED = 4 };
+// Barriers one launch of n steps passes.
+inline unsigned persistent_barriers(int n_layers, int n_steps) {
+    return (unsigned)(n_steps * 5 * n_layers + (n_steps - 1));
+}
+bool persistent_supported(const StepArgs& A);
+hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, hipStream_t s);
+hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg);
+hipError_t barrier_probe(int nwg, int n, int mode, float* us, int* errbits);
+
 // Host launchers (rd_kernels.hip).
+int kch_for(int K);
 hipError_t launch_step(const StepArgs& A, hipStream_t s);
+hipError_t launch_phase(const StepArgs& A, int phase, int layer, hipStream_t s);
 hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, hipStream_t s);
 hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s);
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);

@@ -60,7 +60,7 @@ def teacher_forced(rd, orc, blob, shape, prompt, n_decode, kv="fp16", executor="
     return worst, graded, n, np.stack(gl_all)
 
 
-@pytest.mark.parametrize("executor", ["eager", "graph"])
+@pytest.mark.parametrize("executor", ["eager", "graph", "persistent"])
 def test_tiny_teacher_forced(rd, orc, executor):
     shape = synth.SHAPES["tiny"]
     blob = synth.make_blob(shape, seed=1)
@@ -75,30 +75,62 @@ def test_executors_bit_identical(rd):
     blob = synth.make_blob(shape, seed=1)
     prompt = synth.prompt(101, 40, shape.vocab)
     out = {}
-    for ex in ("eager", "graph"):
+    for ex in ("eager", "graph", "persistent"):
         m = rd.Model(blob, max_context=64, executor=ex)
         out[ex] = np.stack([m.decode_step(int(t))[0] for t in prompt])
         m.close()
     assert np.array_equal(out["eager"], out["graph"])
+    assert np.array_equal(out["graph"], out["persistent"])
 
 
 GQA2 = synth.ModelShape(n_layers=2, d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, d_ff=1408, vocab=1000)
 
 
-def test_gqa_two_layers_teacher_forced(rd, orc):
+@pytest.mark.parametrize("executor", ["graph", "persistent"])
+def test_gqa_two_layers_teacher_forced(rd, orc, executor):
     blob = synth.make_blob(GQA2, seed=7)
     prompt = synth.prompt(9, 70, GQA2.vocab)
-    worst, graded, n, _ = teacher_forced(rd, orc, blob, GQA2, prompt, 20)
-    print(f"gqa2: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+    worst, graded, n, _ = teacher_forced(rd, orc, blob, GQA2, prompt, 20, executor=executor)
+    print(f"gqa2 {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
 
 
+@pytest.mark.parametrize("executor", ["graph", "persistent"])
 @pytest.mark.parametrize("kv", ["e5m2", "int8"])
-def test_tiny_quantized_kv_teacher_forced(rd, orc, kv):
+def test_tiny_quantized_kv_teacher_forced(rd, orc, kv, executor):
     shape = synth.SHAPES["tiny"]
     blob = synth.make_blob(shape, seed=1)
     prompt = synth.prompt(102, 280, shape.vocab)   # crosses two INT8 segment seals
-    worst, graded, n, _ = teacher_forced(rd, orc, blob, shape, prompt, 20, kv=kv)
-    print(f"tiny {kv}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+    worst, graded, n, _ = teacher_forced(rd, orc, blob, shape, prompt, 20, kv=kv, executor=executor)
+    print(f"tiny {kv} {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+
+
+@pytest.mark.parametrize("shape_name,kv", [("tiny", "fp16"), ("tiny", "e5m2"), ("tiny", "int8"),
+                                           ("gqa2", "int8"), ("gqa2", "e5m2")])
+def test_persistent_multistep_matches_graph(rd, shape_name, kv):
+    """One persistent launch decoding 300 greedy steps (crossing INT8 seals,
+    E5M2 rows that share cache lines) gives the same tokens, final logits and
+    cache bytes as the graph executor, which synchronises at every kernel
+    boundary.  Detects stale-cache and ordering races in the persistent path."""
+    shape = synth.SHAPES["tiny"] if shape_name == "tiny" else GQA2
+    blob = synth.make_blob(shape, seed=5)
+    prompt = synth.prompt(106, 20, shape.vocab)
+    res = {}
+    for ex in ("graph", "persistent"):
+        m = rd.Model(blob, max_context=400, kv_format=kv, executor=ex)
+        assert m.get_info().executor == rd.EXECUTORS[ex]
+        for t in prompt[:-1]:
+            m.decode_step(int(t), want_logits=False)
+        toks = m.generate(int(prompt[-1]), 300)
+        lg, nxt = m.decode_step(int(toks[-1]))
+        caches = [m.export_kv(l, w) for l in range(shape.n_layers) for w in (0, 1)]
+        res[ex] = (toks, lg, nxt, caches)
+        m.close()
+    a, b = res["graph"], res["persistent"]
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1], b[1]) and a[2] == b[2]
+    for ca, cb in zip(a[3], b[3]):
+        for k in ca:
+            assert np.array_equal(ca[k], cb[k]), k
 
 
 def test_int8_seal_bytes_bit_exact(rd, orc):
@@ -185,14 +217,16 @@ def blob2b():
     return synth.make_blob(synth.SHAPES["2b"], seed=2)
 
 
-def test_2b_short_teacher_forced(rd, orc, blob2b):
+@pytest.mark.parametrize("executor", ["graph", "persistent"])
+def test_2b_short_teacher_forced(rd, orc, blob2b, executor):
     shape = synth.SHAPES["2b"]
     prompt = synth.prompt(103, 12, shape.vocab)
-    worst, graded, n, _ = teacher_forced(rd, orc, blob2b, shape, prompt, 4)
-    print(f"2b short: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+    worst, graded, n, _ = teacher_forced(rd, orc, blob2b, shape, prompt, 4, executor=executor)
+    print(f"2b short {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
 
 
-def test_2b_full_size_sampled(rd, orc, blob2b):
+@pytest.mark.parametrize("executor", ["graph", "persistent"])
+def test_2b_full_size_sampled(rd, orc, blob2b, executor):
     """The 512-token prompt + 256 greedy steps run at full size; the oracle
     checks (a) layer-0 K/V rows at sampled positions (they depend on their
     own token only) and (b) the last step's logits computed from the GPU's
@@ -201,7 +235,8 @@ def test_2b_full_size_sampled(rd, orc, blob2b):
     P, N = 512, 256
     prompt = synth.prompt(103, P, shape.vocab)
     ctx = P + N
-    gm = rd.Model(blob2b, max_context=ctx, executor="graph")
+    gm = rd.Model(blob2b, max_context=ctx, executor=executor)
+    assert gm.get_info().executor == rd.EXECUTORS[executor]
     for t in prompt[:-1]:
         gm.decode_step(int(t), want_logits=False)
     gen = gm.generate(int(prompt[-1]), N)               # steps at positions P-1 .. ctx-2
