@@ -192,13 +192,21 @@ rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t layer, int32_t 
 /* One decode step of `token` with the persistent executor, recording an
  * event trace of workgroup 0: ts (host, cap uint64 words) receives
  * [n, code_0, clock_0, code_1, clock_1, ...] with clock the constant 100 MHz
- * wall clock and code = 10 * phase + point (phase 0 QKV, 1 attention,
- * 2 output projection, 3 gate/up, 4 down, 5 LM head; point 0 barrier wait
- * done, 1 input staged, 2 phase work done, 3 arrival counted, 4 next weight
- * loads issued; 99 kernel start, 98 end).  *n receives the event count
+ * wall clock and code = 10 * phase + point (phase 0 QKV, 1 attention split,
+ * 2 merge of a query head, 3 output projection, 4 gate/up, 5 down, 6 LM
+ * head; point 0 input received, 1 input staged, 2 rows reduced, 3 output
+ * published; 99 kernel start, 98 end).  *n receives the event count
  * (at most (cap-1)/2).  Synchronises.  Errors: UNSUPPORTED for other
  * executors, INVALID_ARG, CONTEXT_FULL, DEVICE. */
 rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n);
+
+/* The same trace for every workgroup of the persistent launch: ts (host)
+ * holds n_wg regions of cap uint64 words, region w laid out as above for
+ * workgroup w (the clock is one wall clock shared by all CUs, so regions
+ * can be compared); *n_wg receives the workgroup count.  ts must hold
+ * (workgroups of the launch) * cap words: the count is the device's CU
+ * count.  Errors as rd_debug_trace_step. */
+rd_status rd_debug_trace_step_all(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n_wg);
 
 const char* rd_last_error(void);
 

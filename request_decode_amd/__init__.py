@@ -73,6 +73,7 @@ SIGNATURES = [
     ("rd_set_executor", _I32, [_VP, _I32]),
     ("rd_debug_run_phase", _I32, [_VP, _I32, _I32, _I32]),
     ("rd_debug_trace_step", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
+    ("rd_debug_trace_step_all", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
     ("rd_last_error", C.c_char_p, []),
     ("rd_gemv_f16", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
@@ -182,6 +183,22 @@ class Model:
         ev = ts[1:1 + 2 * n.value].reshape(-1, 2).astype(np.int64)
         return ev[:, 0], ev[:, 1]
 
+    def trace_step_all(self, token: int, n_wg: int = 1024, max_events: int = 1024):
+        """Event traces of every workgroup of one persistent step: a list, per
+        workgroup, of (codes, clocks in 10 ns ticks); n_wg: at least the
+        device's CU count (the buffer is sized for it)."""
+        cap = 1 + 2 * max_events
+        ts = np.zeros(cap * n_wg, np.uint64)
+        n = C.c_int32()
+        check(lib().rd_debug_trace_step_all(self._h, token, ts.ctypes.data_as(C.POINTER(C.c_uint64)), cap,
+                                            C.byref(n)))
+        out = []
+        for w in range(n.value):
+            r = ts[w * cap:(w + 1) * cap]
+            ev = r[1:1 + 2 * int(r[0])].reshape(-1, 2).astype(np.int64)
+            out.append((ev[:, 0], ev[:, 1]))
+        return out
+
     def decode_step(self, token: int, want_logits: bool = True, allow_numeric: bool = False):
         t, tp = _i32([token])
         nxt, np_ = _i32([0])
@@ -265,7 +282,7 @@ def rd_argmax_f32(v: int, n: int, out: int, stream: int = 0):
     check(lib().rd_argmax_f32(v, n, out, stream or None))
 
 
-def rd_debug_barrier_probe(device: int = 0, n: int = 10000, mode: int = 0) -> float:
+def rd_debug_barrier_probe(device: int = 0, n: int = 10000, mode: int = 1) -> float:
     us = C.c_float()
     check(lib().rd_debug_barrier_probe(device, n, mode, C.byref(us)))
     return us.value

@@ -13,6 +13,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -145,10 +146,9 @@ struct rd_model {
     hipGraphExec_t gexec = nullptr;
 
     // persistent executor
-    int* bar = nullptr;             // grid-barrier words (zero between launches)
-    LayerW* layers_dev = nullptr;   // per-layer weight pointers on the device
-    int nwg = 0;                    // workgroups of the cooperative launch
-    unsigned gen = 0;               // barrier generation the next launch starts from
+    long long layer_stride = 0;     // bytes between consecutive layers' weight blocks
+    int nwg = 0;                    // workgroups of the cooperative launch (0: not available)
+    uint32_t tag = 0;               // exchange tag base of the next launch
 };
 
 static rd_status dev_fail(rd_model* m, const char* what, hipError_t e) {
@@ -191,8 +191,6 @@ void free_model(rd_model* m) {
     (void)hipFree(m->stage);
     (void)hipFree(m->meta);
     (void)hipFree(m->act);
-    (void)hipFree(m->bar);
-    (void)hipFree(m->layers_dev);
     if (m->gen_host) (void)hipHostFree(m->gen_host);
     if (m->logits_host) (void)hipHostFree(m->logits_host);
     if (m->state_host) (void)hipHostFree(m->state_host);
@@ -201,24 +199,25 @@ void free_model(rd_model* m) {
     delete m;
 }
 
-// Watchdog of the persistent kernel's barrier waits: polls of about 60 ns.
-constexpr int kSpinLimit = 1 << 24;
+// Watchdog of the persistent kernel's waits: polls of about a microsecond.
+constexpr int kSpinLimit = 1 << 21;
 
 // One cooperative launch decoding n steps from the current device state.
 rd_status persistent_enqueue(rd_model* m, int n, int out_base, unsigned long long* trace = nullptr,
-                             int trace_cap = 0) {
+                             int trace_cap = 0, int trace_all = 0) {
     PersistArgs P{};
     P.trace = trace;
     P.trace_cap = trace_cap;
-    P.layers = m->layers_dev;
-    P.bar = m->bar;
-    P.gen0 = m->gen;
+    P.trace_all = trace_all;
+    P.layer0 = m->layers[0];
+    P.layer_stride = m->layer_stride;
+    P.tag0 = m->tag;
     P.pos0 = m->host_pos;
     P.n_steps = n;
     P.out_base = out_base;
     P.spin_limit = kSpinLimit;
     HIP_TRY(launch_persistent(m->A, P, m->nwg, m->stream));
-    m->gen += persistent_barriers(m->d.L, n);
+    m->tag += persistent_tags(m->d.L, n);
     return RD_OK;
 }
 
@@ -281,7 +280,12 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     m->dev = opt.device;
     m->d = d;
     m->opt = opt;
-    m->S = opt.attn_splits ? opt.attn_splits : 64;
+    // Default key splits per kv-head: one attention task per CU over all
+    // kv-heads, at most 64 (the persistent kernel gives each task a workgroup).
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, opt.device) != hipSuccess || cus < 1)
+        cus = 1;
+    m->S = opt.attn_splits ? opt.attn_splits : std::max(1, std::min(64, cus / (int)d.Hk));
     auto bail = [&](rd_status st) {
         std::string keep = g_err;
         free_model(m);
@@ -412,9 +416,13 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     };
     const size_t o_x = carve(D * 4), o_q = carve(H * hd * 4), o_a = carve(H * hd * 4), o_m = carve(F * 4);
     const size_t o_logits = carve(V * 4);
-    const size_t o_po = carve(H * MAX_SPLITS * hd * 4), o_pml = carve(H * MAX_SPLITS * 2 * 4);
-    const int n_arg = n_lm_wg > 1024 ? n_lm_wg : 1024;   // argmax partials: LM-head or persistent grid
-    const size_t o_cnt = carve(Hk * 4), o_av = carve(n_arg * 4), o_ai = carve(n_arg * 4), o_ac = carve(64 * 4);
+    const size_t S = m->S;
+    const size_t o_part = carve(H * S * (hd + 2) * 4);
+    const int n_arg = n_lm_wg;   // argmax partials of the LM-head kernel
+    const size_t o_av = carve(n_arg * 4), o_ai = carve(n_arg * 4), o_ac = carve(64 * 4);
+    // exchange words of the persistent executor
+    const size_t o_xb1 = carve(D * 8), o_xb2 = carve(D * 8), o_qb = carve(Nqkv * 8), o_pb = carve(H * S * (hd + 2) * 8);
+    const size_t o_ab = carve(H * hd * 8), o_mb = carve(F * 8), o_lb = carve(1024 * 8), o_abort = carve(64);
     const size_t o_st = carve(sizeof(StepState)), o_gen = carve(ctx * 4);
     const size_t o_rope = carve(ctx * (hd / 2) * sizeof(float2));
     CREATE_TRY(hipMalloc(&m->act, a));
@@ -443,8 +451,10 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     A.layers = m->layers.data();
     A.x = (float*)(X + o_x); A.q = (float*)(X + o_q); A.a = (float*)(X + o_a); A.m = (float*)(X + o_m);
     A.logits = (float*)(X + o_logits);
-    A.part_o = (float*)(X + o_po); A.part_ml = (float*)(X + o_pml);
-    A.cnt = (int*)(X + o_cnt);
+    A.part = (float*)(X + o_part);
+    A.xb1 = (uint64_t*)(X + o_xb1); A.xb2 = (uint64_t*)(X + o_xb2); A.qb = (uint64_t*)(X + o_qb);
+    A.pb = (uint64_t*)(X + o_pb); A.ab = (uint64_t*)(X + o_ab); A.mb = (uint64_t*)(X + o_mb);
+    A.lb = (uint64_t*)(X + o_lb); A.abort_word = (int*)(X + o_abort);
     A.arg_val = (float*)(X + o_av); A.arg_idx = (int*)(X + o_ai); A.arg_cnt = (int*)(X + o_ac);
     A.st = (StepState*)(X + o_st); A.gen_out = (int*)(X + o_gen);
     A.rope = (const float2*)(X + o_rope);
@@ -453,13 +463,12 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     // ---- executor: the persistent kernel where its shape is built, else the graph
     if (opt.executor == RD_EXEC_AUTO || opt.executor == RD_EXEC_PERSISTENT) {
         int nwg = 0;
-        if (persistent_supported(A) && persistent_max_grid(A, m->dev, &nwg) == hipSuccess && nwg > 0 &&
-            nwg <= n_arg) {
-            CREATE_TRY(hipMalloc(&m->bar, BAR_WORDS * sizeof(int)));
-            CREATE_TRY(hipMemset(m->bar, 0, BAR_WORDS * sizeof(int)));
-            CREATE_TRY(hipMalloc(&m->layers_dev, m->layers.size() * sizeof(LayerW)));
-            CREATE_TRY(hipMemcpy(m->layers_dev, m->layers.data(), m->layers.size() * sizeof(LayerW),
-                                 hipMemcpyHostToDevice));
+        if (persistent_supported(A) && persistent_max_grid(A, m->dev, &nwg) == hipSuccess && nwg > 0) {
+            // the persistent kernel finds layer l's weights layer_stride bytes past layer 0's
+            m->layer_stride = NL > 1 ? (long long)(o_layer[6] - o_layer[0]) : 0;
+            for (size_t l = 1; l < NL; ++l)
+                if (o_layer[6 * l] - o_layer[0] != l * (size_t)m->layer_stride)
+                    return bail(fail(RD_ERR_DEVICE, "weight image is not layer-periodic"));
             m->nwg = nwg;
             m->opt.executor = RD_EXEC_PERSISTENT;
         } else if (opt.executor == RD_EXEC_PERSISTENT) {
@@ -506,7 +515,7 @@ extern "C" rd_status rd_set_executor(rd_model* m, int32_t executor) {
     if (st) return st;
     if (executor != RD_EXEC_EAGER && executor != RD_EXEC_GRAPH && executor != RD_EXEC_PERSISTENT)
         return fail(RD_ERR_INVALID_ARG, "executor must be EAGER, GRAPH or PERSISTENT");
-    if (executor == RD_EXEC_PERSISTENT && !m->bar)
+    if (executor == RD_EXEC_PERSISTENT && !m->nwg)
         return fail(RD_ERR_UNSUPPORTED, "this model has no persistent kernel");
     m->opt.executor = executor;
     return RD_OK;
@@ -524,7 +533,7 @@ extern "C" rd_status rd_set_position(rd_model* m, int32_t pos) {
 
 static rd_status finish_sync(rd_model* m);
 
-extern "C" rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n_out) {
+static rd_status trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int all, int32_t* n_out) {
     rd_status st = check_model(m);
     if (st) return st;
     if (!ts || !n_out) return fail(RD_ERR_INVALID_ARG, "NULL argument");
@@ -533,24 +542,41 @@ extern "C" rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* t
     if (token < 0 || token >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
     if (cap < 3) return fail(RD_ERR_INVALID_ARG, "trace capacity must be >= 3");
     const int events = (cap - 1) / 2;
-    const size_t words = 1 + 2 * (size_t)events;
+    const size_t words = (1 + 2 * (size_t)events) * (all ? (size_t)m->nwg : 1);
     HIP_TRY(hipSetDevice(m->dev));
     unsigned long long* dev = nullptr;
     HIP_TRY(hipMalloc(&dev, words * 8));
     HIP_TRY(hipMemset(dev, 0, words * 8));
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, token, 1);
     HIP_TRY(hipGetLastError());
-    if ((st = persistent_enqueue(m, 1, 0, dev, events))) {
+    if ((st = persistent_enqueue(m, 1, 0, dev, events, all))) {
         (void)hipFree(dev);
         return st;
     }
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     m->host_pos += 1;
     st = finish_sync(m);
-    HIP_TRY(hipMemcpy(ts, dev, words * 8, hipMemcpyDeviceToHost));
+    if (all) {
+        // compact each workgroup's region to the caller's stride of cap words
+        std::vector<uint64_t> h(words);
+        HIP_TRY(hipMemcpy(h.data(), dev, words * 8, hipMemcpyDeviceToHost));
+        for (int w = 0; w < m->nwg; ++w)
+            memcpy(ts + (size_t)w * cap, h.data() + (size_t)w * (1 + 2 * (size_t)events), (1 + 2 * (size_t)events) * 8);
+        *n_out = m->nwg;
+    } else {
+        HIP_TRY(hipMemcpy(ts, dev, words * 8, hipMemcpyDeviceToHost));
+        *n_out = (int32_t)ts[0];
+    }
     (void)hipFree(dev);
-    *n_out = (int32_t)ts[0];
     return st;
+}
+
+extern "C" rd_status rd_debug_trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n_out) {
+    return trace_step(m, token, ts, cap, 0, n_out);
+}
+
+extern "C" rd_status rd_debug_trace_step_all(rd_model* m, int32_t token, uint64_t* ts, int32_t cap, int32_t* n_wg) {
+    return trace_step(m, token, ts, cap, 1, n_wg);
 }
 
 extern "C" rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t layer, int32_t iters) {
@@ -568,9 +594,9 @@ extern "C" rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t laye
 
 static rd_status finish_sync(rd_model* m) {
     HIP_TRY(hipStreamSynchronize(m->stream));
-    if (m->state_host->err & ERR_BARRIER) {
+    if (m->state_host->err & ERR_STALL) {
         m->poisoned = true;
-        return fail(RD_ERR_DEVICE, "a grid barrier of the persistent kernel timed out");
+        return fail(RD_ERR_DEVICE, "a wait of the persistent kernel timed out");
     }
     if (m->state_host->err & ERR_TOKEN) return fail(RD_ERR_NUMERIC, "token id out of range seen on the device");
     if (m->state_host->err & ERR_NONFINITE) return fail(RD_ERR_NUMERIC, "non-finite logit");
@@ -728,9 +754,7 @@ namespace {
 // allocated on first use and kept until the process ends.  Calls that overlap
 // on one device race on it.
 struct Scratch {
-    float* part_o = nullptr;
-    float* part_ml = nullptr;
-    int* cnt = nullptr;     // [Hk max] zero between uses
+    float* part = nullptr;  // [heads][MAX_SPLITS][hd+2]
     int* pos = nullptr;
     float* av = nullptr;
     int* ai = nullptr;
@@ -747,17 +771,15 @@ hipError_t get_scratch(Scratch** out) {
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lk(g_scr_mu);
     Scratch& s = g_scr[dev];
-    if (!s.part_o) {
-        const size_t po = (size_t)SCR_HEADS * MAX_SPLITS * SCR_HD * 4, pml = (size_t)SCR_HEADS * MAX_SPLITS * 8;
-        const size_t tail = SCR_HEADS * 4 + 256 + SCR_ARG * 8 + 256;
+    if (!s.part) {
+        const size_t po = (size_t)SCR_HEADS * MAX_SPLITS * (SCR_HD + 2) * 4;
+        const size_t tail = 256 + SCR_ARG * 8 + 256;
         void* p = nullptr;
-        if ((e = hipMalloc(&p, po + pml + tail)) != hipSuccess) return e;
-        if ((e = hipMemset(p, 0, po + pml + tail)) != hipSuccess) return e;
+        if ((e = hipMalloc(&p, po + tail)) != hipSuccess) return e;
+        if ((e = hipMemset(p, 0, po + tail)) != hipSuccess) return e;
         uint8_t* b = (uint8_t*)p;
-        s.part_o = (float*)b;
-        s.part_ml = (float*)(b + po);
-        s.cnt = (int*)(b + po + pml);
-        s.pos = s.cnt + SCR_HEADS;
+        s.part = (float*)b;
+        s.pos = (int*)(b + po);
         s.av = (float*)(s.pos + 64);
         s.ai = (int*)(s.av + SCR_ARG);
         s.acnt = s.ai + SCR_ARG;
@@ -802,11 +824,9 @@ extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void
     AttnArgs A{};
     A.q = q;
     A.out = out;
-    A.kc = const_cast<void*>(Kc);
-    A.vc = const_cast<void*>(Vc);
-    A.part_o = s->part_o;
-    A.part_ml = s->part_ml;
-    A.cnt = s->cnt;
+    A.kc = Kc;
+    A.vc = Vc;
+    A.part = s->part;
     A.pos_ptr = s->pos;
     A.ld = ld;
     A.nseg = 0;
@@ -836,7 +856,7 @@ extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg
 
 extern "C" rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t mode, float* us) {
     if (!us || n < 1 || n > (1 << 20)) return fail(RD_ERR_INVALID_ARG, "need us != NULL and 1 <= n <= 2^20");
-    if (mode < 0 || mode > 6) return fail(RD_ERR_INVALID_ARG, "mode must be 0..6");
+    if (mode < 0 || mode > 1) return fail(RD_ERR_INVALID_ARG, "mode must be 0 or 1");
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
         return fail(RD_ERR_INVALID_ARG, "bad device");
@@ -845,7 +865,7 @@ extern "C" rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t m
     K_TRY(hipGetDeviceProperties(&prop, device));
     int errbits = 0;
     K_TRY(barrier_probe(prop.multiProcessorCount, n, mode, us, &errbits));
-    if (errbits & ERR_BARRIER) return fail(RD_ERR_DEVICE, "a probe barrier timed out");
+    if (errbits & ERR_STALL) return fail(RD_ERR_DEVICE, "a probe wait timed out");
     return RD_OK;
 }
 

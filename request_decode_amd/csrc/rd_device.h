@@ -13,6 +13,19 @@ typedef unsigned u2v __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
+// The wave's index in its workgroup as a wave-uniform (scalar) value, so that
+// addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+// The lane index, passed through an empty asm so that values derived from it
+// are computed where they are used: in a long persistent loop the compiler
+// would otherwise hoist every lane-dependent address out of the loop and keep
+// it live across the whole body, spilling registers.
+__device__ __forceinline__ int lane_id() {
+    int l = (int)(threadIdx.x & 63);
+    asm volatile("" : "+v"(l));
+    return l;
+}
+
 // ---- loads ----------------------------------------------------------------
 // Weights are read exactly once per step and never reused inside it, so they
 // are fetched with the non-temporal hint (no point keeping them in L2/MALL).
@@ -25,17 +38,52 @@ __device__ __forceinline__ u2v ld8(const void* p) { return *reinterpret_cast<con
 __device__ __forceinline__ h8 as_h8(u4v u) { return __builtin_bit_cast(h8, u); }
 
 // ---- wave reductions ----------------------------------------------------------
-// Butterfly over the 64 lanes: every lane ends with the full result.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// DPP lane exchange (no LDS round trip, unlike a ds_bpermute shuffle):
+// 0xB1 / 0x4E swap neighbours / pairs inside each quad, 0x124 / 0x128 rotate
+// a row of 16 lanes by 4 / 8, 0x141 mirrors each half-row of 8 lanes, 0x150
+// broadcasts lane 0 of each row to the whole row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Sum of each row of 16 lanes, valid in lane 0 of the row (the other lanes
+// hold the same terms associated differently).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);
+    v += dpp_f<0x128>(v);
     return v;
 }
-// Sum over aligned groups of `n` lanes (n a power of two <= 64).
+// Sum over the 64 lanes: one association order, the same value in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return ((readlane_f(v, 0) + readlane_f(v, 16)) + readlane_f(v, 32)) + readlane_f(v, 48);
+}
+// Sum over aligned groups of N lanes (N = 8 or 16), the same bits in every
+// lane of a group.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+    if constexpr (N == 16) {
+        return dpp_f<0x150>(row16_sum(v));
+    } else {
+        v += dpp_f<0xB1>(v);
+        v += dpp_f<0x4E>(v);
+        return v + dpp_f<0x141>(v);
+    }
+}
+__device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
-    for (int o = N / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, WAVE));
     return v;
 }
 
@@ -56,21 +104,22 @@ __device__ __forceinline__ _Float16 e5m2_decode(uint8_t e) {
     return __builtin_bit_cast(_Float16, (uint16_t)((uint16_t)e << 8));
 }
 __device__ __forceinline__ uint16_t f2h_bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h_bits2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 // ---- cross-workgroup exchange inside one kernel --------------------------------
 // The L2 is per XCD, so data one workgroup hands to another must not sit in
 // a non-coherent L2 line.  An agent-scope release/acquire fence would write
-// back and invalidate the whole L2 of the XCD (buffer_wbl2 / buffer_inv),
-// far too costly once per workgroup.  Instead the exchanged words are
-// written and read with agent-scope (sc1) relaxed atomic stores and loads,
-// which are coherent across XCDs on their own; the only ordering needed is
-// that a workgroup's stores have completed (vmcnt drained) before its
-// arrival is counted, and that the reader's loads are issued after it saw
-// the final count.
+// back and invalidate the whole L2 of the XCD, far too costly per exchange.
+// Instead the exchanged words are written and read with agent-scope (sc1)
+// relaxed atomic stores and loads, which are coherent across XCDs on their
+// own.
 __device__ __forceinline__ void st_agent(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_agent(const float* p) {
@@ -79,13 +128,17 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 __device__ __forceinline__ int ld_agent(const int* p) {
     return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until this wave's outstanding vector-memory operations completed.
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this wave's outstanding vector-memory operations completed
+// (loads returned, stores acknowledged at the coherence point).
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Count this workgroup's arrival on *cnt after all of its threads' st_agent
-// stores completed; true in every thread of the workgroup that arrives
-// last of `expected`.  The last one resets the counter for the next use
-// (which must come after a kernel boundary).
+// Count this workgroup's arrival on *cnt after all of its threads' stores
+// completed; true in every thread of the workgroup that arrives last of
+// `expected`.  The last one resets the counter for the next use (which must
+// come after a kernel boundary).
 __device__ __forceinline__ bool arrive_last(int* cnt, int expected) {
     __shared__ int s_last;
     drain_vmem();

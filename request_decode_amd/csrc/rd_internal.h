@@ -8,10 +8,10 @@ namespace rd {
 
 constexpr int SEG = 128;       // tokens per INT8 KV segment
 constexpr int MAX_SPLITS = 256;
-constexpr int WG = 256;        // threads per workgroup of every kernel (4 waves)
+constexpr int WG = 256;        // threads per workgroup of the kernel-per-phase executor (4 waves)
 
 enum KvFmt { KV_FP16 = 0, KV_E5M2 = 1, KV_INT8 = 2 };
-enum ErrBits { ERR_TOKEN = 1, ERR_NONFINITE = 2 };
+enum ErrBits { ERR_TOKEN = 1, ERR_NONFINITE = 2, ERR_STALL = 4 };
 
 // Per-step scalars live on the device so that a captured step is static.
 struct StepState {
@@ -32,18 +32,19 @@ struct LayerW {
     const _Float16* g_ffn;  // [D]
 };
 
+// Attention of one layer (or of the standalone attention entry point).
 struct AttnArgs {
     const float* q;          // [H][hd] post-RoPE queries
     float* out;              // [H][hd] attention output
-    void* kc;                // this layer's K: [Hk][ld][hd] fp16 | e5m2 | u8 codes
-    void* vc;                // this layer's V
+    const void* kc;          // this layer's K: [Hk][ld][hd] fp16 | e5m2 | u8 codes
+    const void* vc;          // this layer's V
     uint16_t* kst;           // INT8: [Hk][128][hd] fp16 open-segment rows of K
     uint16_t* vst;
     float* kmeta;            // INT8: [Hk][nseg][2] (scale, zp)
     float* vmeta;
-    float* part_o;           // [H][MAX_SPLITS][hd]
-    float* part_ml;          // [H][MAX_SPLITS][2]
-    int* cnt;                // [Hk] arrival counters (zero between uses)
+    void* kcw;               // INT8: writable code rows of K and V (sealed by the merge)
+    void* vcw;
+    float* part;             // [H][S][hd+2] split partials: o[hd], m, l
     const int* pos_ptr;      // L = *pos_ptr + 1
     int ld, nseg, H, Hk, S;
     float scale;
@@ -55,18 +56,16 @@ struct StepArgs {
     const _Float16* embed;
     const _Float16* g_final;
     const _Float16* lm_head;
-    const LayerW* layers;    // host array (used by the host launcher only)
+    const LayerW* layers;    // host array (used by the host launchers only)
     float* x;                // [D] residual stream
     float* q;                // [H*hd]
     float* a;                // [H*hd]
     float* m;                // [F]
     float* logits;           // [V]
-    float* part_o;
-    float* part_ml;
-    int* cnt;                // [Hk]
+    float* part;             // [H][S][hd+2]
     float* arg_val;          // [n LM-head workgroups]
     int* arg_idx;
-    int* arg_cnt;            // [1]
+    int* arg_cnt;            // [1 + 16]
     StepState* st;
     int* gen_out;            // [max_ctx]
     const float2* rope;      // [max_ctx][hd/2] (cos, sin)
@@ -75,35 +74,66 @@ struct StepArgs {
     uint16_t* stage;         // INT8: [n_layers][2][Hk][128][hd]
     float* meta;             // INT8: [n_layers][2][Hk][nseg][2]
     int nseg;
+    // exchange words of the persistent executor: (tag << 32) | fp32 bits
+    uint64_t* xb1;           // [D] residual stream after the down projection
+    uint64_t* xb2;           // [D] residual stream after the output projection
+    uint64_t* qb;            // [(H+2Hk)*hd] rotated q, then the new K and V rows as stored
+    uint64_t* pb;            // [H][S][hd+2] attention split partials
+    uint64_t* ab;            // [H*hd] attention output
+    uint64_t* mb;            // [F] SwiGLU output
+    uint64_t* lb;            // [workgroups] argmax: (value bits << 32) | (index << 12) | tag12
+    int* abort_word;         // set when a wait of the persistent kernel gives up
 };
 
+// The attention view of layer l of the step's buffers.
+__host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
+    AttnArgs T{};
+    const size_t lay = (size_t)l * A.Hk * A.max_ctx * A.hd;
+    const size_t es = A.kvfmt == KV_FP16 ? 2 : 1;
+    T.q = A.q;
+    T.out = A.a;
+    T.kc = reinterpret_cast<uint8_t*>(A.kc) + lay * es;
+    T.vc = reinterpret_cast<uint8_t*>(A.vc) + lay * es;
+    T.kcw = reinterpret_cast<uint8_t*>(A.kc) + lay * es;
+    T.vcw = reinterpret_cast<uint8_t*>(A.vc) + lay * es;
+    if (A.kvfmt == KV_INT8) {
+        T.kst = A.stage + ((size_t)l * 2 + 0) * A.Hk * SEG * A.hd;
+        T.vst = A.stage + ((size_t)l * 2 + 1) * A.Hk * SEG * A.hd;
+        T.kmeta = A.meta + ((size_t)l * 2 + 0) * A.Hk * A.nseg * 2;
+        T.vmeta = A.meta + ((size_t)l * 2 + 1) * A.Hk * A.nseg * 2;
+    }
+    T.part = A.part;
+    T.pos_ptr = &A.st->pos;
+    T.ld = A.max_ctx;
+    T.nseg = A.nseg;
+    T.H = A.H;
+    T.Hk = A.Hk;
+    T.S = A.S;
+    T.scale = A.scale;
+    return T;
+}
+
 // Persistent executor (rd_persistent.hip).
-enum { ERR_BARRIER = 4 };
-constexpr int BAR_SUB = 16;                       // barrier sub-counters
-constexpr int BAR_STRIDE = 32;                    // ints between barrier words (128-byte lines)
-constexpr int BAR_FLAGS = (BAR_SUB + 3) * BAR_STRIDE;       // per-workgroup flag words start here
-constexpr int BAR_MAX_WG = 1024;
-constexpr int BAR_WORDS = BAR_FLAGS + BAR_MAX_WG * BAR_STRIDE;
 struct PersistArgs {
-    const LayerW* layers;     // device copy of the per-layer weight pointers
-    int* bar;                 // [BAR_WORDS]: sub-counters, top counter, generation, abort flag
-    unsigned gen0;            // barrier generation when the launch starts
+    LayerW layer0;            // layer 0's weights; layer l's lie layer_stride bytes further per layer
+    long long layer_stride;
+    uint32_t tag0;            // exchange tag base: step s, layer l uses tag0 + s*(n_layers+1) + l + 1
     int pos0;                 // position of the first step
     int n_steps;              // steps decoded by this launch
     int out_base;             // gen_out index of the first step's token
-    int spin_limit;           // polls before a barrier wait gives up (watchdog)
-    unsigned long long* trace;  // optional event trace of workgroup 0: [0] = count, then
-                                // (code, wall clock at 100 MHz) pairs
-    int trace_cap;              // events the trace buffer holds
+    int spin_limit;           // polls before a wait gives up (watchdog)
+    unsigned long long* trace;  // optional event trace of workgroup 0 (or of every workgroup,
+                                // trace_all): per workgroup [count, then (code, wall clock at
+                                // 100 MHz) pairs], 1 + 2*trace_cap words each
+    int trace_cap;              // events one workgroup's trace holds
+    int trace_all;
 };
-// Trace event codes: 10 * phase + point; phases 0 QKV, 1 attention, 2 output
-// projection, 3 gate/up, 4 down, 5 LM head; points 0 barrier wait done,
-// 1 input staged, 2 phase work done, 3 arrival counted, 4 next loads issued.
-enum { TR_WAIT = 0, TR_STAGED = 1, TR_DONE = 2, TR_ARRIVED = 3, TR_ISSUED = 4 };
-// Barriers one launch of n steps passes.
-inline unsigned persistent_barriers(int n_layers, int n_steps) {
-    return (unsigned)(n_steps * 5 * n_layers + (n_steps - 1));
-}
+// Tags one launch of n steps consumes.
+inline uint32_t persistent_tags(int n_layers, int n_steps) { return (uint32_t)n_steps * (uint32_t)(n_layers + 1); }
+// Trace event codes: 10 * phase + point; phases 0 QKV, 1 attention, 2 merge,
+// 3 output projection, 4 gate/up, 5 down, 6 LM head; points 0 input received,
+// 1 input staged, 2 rows reduced, 3 output published.
+enum { TR_RECV = 0, TR_STAGED = 1, TR_DONE = 2, TR_PUB = 3 };
 bool persistent_supported(const StepArgs& A);
 hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, hipStream_t s);
 hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg);

@@ -25,7 +25,7 @@ namespace rd {
 // the GEMV epilogue with both halves of the pair in the same wave.
 template <int KCH, bool EMB, int KVF>
 __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = lane_id(), wid = wave_id();
     const int D = A.D;
     const int N = (A.H + 2 * A.Hk) * A.hd;
     const int row0 = (blockIdx.x * 4 + wid) * 2;
@@ -49,30 +49,107 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
     rmsnorm_regs<KCH>(xr, Lw.g_attn, D, A.eps);
     if (row0 >= N) return;
     float acc[2];
-    dot_loaded<2, KCH>(w, xr, acc);
-    if (lane == 0) qkv_epilogue<KVF, false>(A, layer, pos, row0, acc[0], acc[1]);
+    dot_rows<2, KCH>(w, xr, acc);
+    if (lane == 0) {
+        const QkvPair o = qkv_pair(A.hd, A.H, A.Hk, row0, acc[0], acc[1], A.rope + (size_t)pos * (A.hd / 2));
+        if (o.kind == 0) {
+            A.q[o.head * A.hd + o.d0] = o.y0;
+            A.q[o.head * A.hd + o.d1] = o.y1;
+        } else {
+            const int which = o.kind == 2;
+            kv_put<KVF, false>(A, layer, which, o.head, pos, o.d0, o.y0);
+            kv_put<KVF, false>(A, layer, which, o.head, pos, o.d1, o.y1);
+        }
+    }
 }
 
-// ---- phase 2: split-K attention; the last split of each head group merges --------
-// Workgroup (g, s): kv-head g, key range s, all G query heads of the group
-// (the K/V rows are read once for the group).  Splits past the end of the
-// context exit at once and do not arrive.
+// ---- phase 2a: split-K attention partials, one wave per (kv-head, split) ---------
+// The wave reads each K/V row of its key range once for all G query heads of
+// the group.  Tasks past the splits in use at this position exit at once.
 template <int HD, int G, int KVF>
-__global__ __launch_bounds__(WG) void k_attn(AttnArgs A) {
-    const int g = blockIdx.x / A.S, s = blockIdx.x % A.S;
-    const int pos = *A.pos_ptr;
+__global__ __launch_bounds__(WG) void k_attn(AttnArgs T) {
+    using Geo = AttnGeo<HD>;
+    const int pos = *T.pos_ptr, L = pos + 1;
     int chunk, nact;
-    split_plan(pos + 1, A.S, chunk, nact);
-    if (s >= nact) return;
-    attn_split<HD, G, KVF, false>(A, g, s, chunk, pos);
-    attn_arrive<HD, G, KVF, false>(A, g, nact, pos);
+    split_plan(L, T.S, chunk, nact);
+    const int t = blockIdx.x * (WG / WAVE) + wave_id();
+    if (t >= T.Hk * nact) return;
+    const int g = t / nact, s = t % nact;
+    const int lane = lane_id(), j = lane % Geo::LPR;
+    const float qs = T.scale * LOG2E;
+    float qv[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
+    AttnAcc<HD, G> acc;
+    acc.clear();
+    const int p0 = s * chunk, p1 = min(L, p0 + chunk), open0 = pos / SEG * SEG;
+    for (int pb = p0; pb < p1; pb += Geo::BATCH) {
+        KvRaw kr[Geo::U], vr[Geo::U];
+        kv_batch_raw<HD, KVF, false>(T, g, pb, p0, p1, open0, kr, vr);
+        float kf[Geo::U][8], vf[Geo::U][8];
+        bool valid[Geo::U];
+        kv_batch_cvt<HD, KVF>(pb, p1, kr, vr, kf, vf, valid);
+        acc.batch(qv, kf, vf, valid);
+    }
+    acc.finish();
+    if (lane < Geo::LPR) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float* dst = T.part + ((size_t)(g * G + h) * T.S + s) * (HD + 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[j * 8 + i] = acc.o[h][i];
+            if (lane == 0) {
+                dst[HD] = acc.m[h];
+                dst[HD + 1] = acc.l[h];
+            }
+        }
+    }
+}
+
+// ---- phase 2b: log-sum-exp merge, one wave per (query head, 64 dims); on the
+// step that fills an INT8 segment the first merge wave of each kv-head seals
+// it (after every split of this step has read the open segment).
+template <int HD, int G, int KVF>
+__global__ __launch_bounds__(WG) void k_merge(AttnArgs T) {
+    using Geo = AttnGeo<HD>;
+    const int pos = *T.pos_ptr;
+    int chunk, nact;
+    split_plan(pos + 1, T.S, chunk, nact);
+    const int t = blockIdx.x * (WG / WAVE) + wave_id();
+    if (t >= T.H * Geo::NPART) return;
+    const int h = t / Geo::NPART, part = t % Geo::NPART, lane = lane_id();
+    const float* base = T.part + (size_t)h * T.S * (HD + 2);
+    float ms[MERGE_NC], ls[MERGE_NC];
+#pragma unroll
+    for (int c = 0; c < MERGE_NC; ++c) {
+        const int s = c * 64 + lane;
+        ms[c] = s < nact ? base[(size_t)s * (HD + 2) + HD] : -INFINITY;
+        ls[c] = s < nact ? base[(size_t)s * (HD + 2) + HD + 1] : 0.f;
+    }
+    const MergeW mw = merge_weights(nact, ms, ls);
+    const int d = part * 64 + lane;
+    float num = 0.f;
+#pragma unroll
+    for (int c = 0; c < MERGE_NC; ++c) {
+        if (c * 64 >= nact) break;
+        float ov[64];
+#pragma unroll
+        for (int k = 0; k < 64; ++k) ov[k] = c * 64 + k < nact ? base[(size_t)(c * 64 + k) * (HD + 2) + d] : 0.f;
+        merge_acc<64>(num, c, mw, ov);
+    }
+    T.out[h * HD + d] = num / mw.den;
+    if constexpr (KVF == KV_INT8) {
+        if ((pos + 1) % SEG == 0 && part == 0 && h % G == 0) seal_head<HD, false>(T, h / G, pos);
+    }
 }
 
 // ---- phases 3 and 5: GEMV + residual add (x[row] += W[row,:] . in) -------------
 template <int KCH, int R>
 __global__ __launch_bounds__(WG) void k_resid(const float* __restrict__ in, int K, const _Float16* __restrict__ W,
                                               float* __restrict__ x, int N) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = lane_id(), wid = wave_id();
     const int row0 = (blockIdx.x * 4 + wid) * R;
     u4v w[R][KCH];
     load_rows<R, KCH>(W, K, row0, max(0, min(R, N - row0)), w);
@@ -80,7 +157,7 @@ __global__ __launch_bounds__(WG) void k_resid(const float* __restrict__ in, int 
     load_x_f32<KCH>(in, K, xr);
     if (row0 >= N) return;
     float acc[R];
-    dot_loaded<R, KCH>(w, xr, acc);
+    dot_rows<R, KCH>(w, xr, acc);
     if (lane == 0)
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -90,7 +167,7 @@ __global__ __launch_bounds__(WG) void k_resid(const float* __restrict__ in, int 
 // ---- phase 4: RMSNorm + gate/up GEMV + SwiGLU (m_i = silu(gate_i) * up_i) -------
 template <int KCH>
 __global__ __launch_bounds__(WG) void k_gateup(StepArgs A, LayerW Lw) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = lane_id(), wid = wave_id();
     const int row0 = (blockIdx.x * 4 + wid) * 2;
     u4v w[2][KCH];
     load_rows<2, KCH>(Lw.wgu, A.D, row0, row0 < 2 * A.F ? 2 : 0, w);
@@ -99,11 +176,8 @@ __global__ __launch_bounds__(WG) void k_gateup(StepArgs A, LayerW Lw) {
     rmsnorm_regs<KCH>(xr, Lw.g_ffn, A.D, A.eps);
     if (row0 >= 2 * A.F) return;
     float acc[2];
-    dot_loaded<2, KCH>(w, xr, acc);
-    if (lane == 0) {
-        const float gt = acc[0];
-        A.m[row0 >> 1] = gt / (1.0f + expf(-gt)) * acc[1];
-    }
+    dot_rows<2, KCH>(w, xr, acc);
+    if (lane == 0) A.m[row0 >> 1] = silu_mul(acc[0], acc[1]);
 }
 
 // ---- phase 6: final RMSNorm + LM head + greedy argmax on the device ---------------
@@ -112,7 +186,7 @@ __global__ __launch_bounds__(WG) void k_gateup(StepArgs A, LayerW Lw) {
 constexpr int LM_ROWS = 16;
 template <int KCH>
 __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = lane_id(), wid = wave_id();
     const int rbeg = (blockIdx.x * 4 + wid) * LM_ROWS;
     const int rend = min(A.V, rbeg + LM_ROWS);
     u4v wa[4][KCH], wb[4][KCH];
@@ -123,7 +197,7 @@ __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
     Best b{-INFINITY, INT_MAX};
     auto consume = [&](const u4v (&w)[4][KCH], int r0) {
         float acc[4];
-        dot_loaded<4, KCH>(w, xr, acc);
+        dot_rows<4, KCH>(w, xr, acc);
         if (lane == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -158,7 +232,7 @@ __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
 template <int KCH, int R>
 __global__ __launch_bounds__(WG) void k_gemv_f16(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
                                                  float* __restrict__ y, int N, int K) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = lane_id(), wid = wave_id();
     const int row0 = (blockIdx.x * 4 + wid) * R;
     u4v w[R][KCH];
     load_rows<R, KCH>(W, K, row0, max(0, min(R, N - row0)), w);
@@ -166,7 +240,7 @@ __global__ __launch_bounds__(WG) void k_gemv_f16(const _Float16* __restrict__ W,
     load_x_f16<KCH>(x, K, xr);
     if (row0 >= N) return;
     float acc[R];
-    dot_loaded<R, KCH>(w, xr, acc);
+    dot_rows<R, KCH>(w, xr, acc);
     if (lane == 0)
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -177,10 +251,11 @@ __global__ __launch_bounds__(WG) void k_e5m2(const uint16_t* __restrict__ in, ui
     for (size_t i = (size_t)blockIdx.x * WG + threadIdx.x; i < n; i += (size_t)gridDim.x * WG) out[i] = e5m2_encode(in[i]);
 }
 
-__global__ __launch_bounds__(WG) void k_seg_quant(const uint16_t* __restrict__ in, int seg_elems,
-                                                  uint8_t* __restrict__ codes, float* __restrict__ meta) {
+// One wave per segment (the seal of the decode step, called alone).
+__global__ __launch_bounds__(WAVE) void k_seg_quant(const uint16_t* __restrict__ in, int seg_elems,
+                                                   uint8_t* __restrict__ codes, float* __restrict__ meta) {
     const size_t off = (size_t)blockIdx.x * seg_elems;
-    quantize_segment<false>(in + off, seg_elems, codes + off, meta + (size_t)blockIdx.x * 2);
+    seal_segment<false>(in + off, seg_elems, codes + off, meta + (size_t)blockIdx.x * 2);
 }
 
 __global__ __launch_bounds__(WG) void k_argmax(const float* __restrict__ v, int n, int* out, float* pv, int* pi,
@@ -218,11 +293,14 @@ namespace {
 
 template <int KVF>
 hipError_t launch_attn_t(const AttnArgs& A, int hd, int G, hipStream_t s) {
-    dim3 grid(A.Hk * A.S), block(WG);
-#define RD_ATT(HDv, Gv)                                                  \
-    if (hd == HDv && G == Gv) {                                          \
-        hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, block, 0, s, A); \
-        return hipGetLastError();                                        \
+    const int wpb = WG / WAVE;
+    dim3 grid((A.Hk * A.S + wpb - 1) / wpb), block(WG);
+    dim3 mgrid((A.H * (hd / 64) + wpb - 1) / wpb);
+#define RD_ATT(HDv, Gv)                                                        \
+    if (hd == HDv && G == Gv) {                                                \
+        hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, block, 0, s, A);      \
+        hipLaunchKernelGGL((k_merge<HDv, Gv, KVF>), mgrid, block, 0, s, A);    \
+        return hipGetLastError();                                              \
     }
     RD_ATT(128, 1) RD_ATT(128, 2) RD_ATT(128, 4) RD_ATT(128, 8)
     RD_ATT(64, 1) RD_ATT(64, 2) RD_ATT(64, 4) RD_ATT(64, 8)
@@ -345,7 +423,7 @@ hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,
                             hipStream_t s) {
     if (n_seg == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_seg_quant, dim3(n_seg), dim3(WG), 0, s, in, seg_elems, codes, meta);
+    hipLaunchKernelGGL(k_seg_quant, dim3(n_seg), dim3(WAVE), 0, s, in, seg_elems, codes, meta);
     return hipGetLastError();
 }
 

@@ -1,452 +1,836 @@
 // Persistent decode-step executor for gfx950: one cooperative launch runs
-// whole decode steps, one workgroup per CU, with device-side grid barriers
-// between the phases instead of kernel boundaries.
+// whole decode steps, one workgroup per CU, with no grid barrier at all.
 //
 // Why: at batch 1 a phase streams only 8-46 MB, so a kernel per phase pays
 // its launch, ramp-up, first-byte latency and drain every time, and the
 // memory stream stops at each boundary ("Real-time LLM inference on
 // standard GPUs: 3,000 tokens/s per request", table of microsecond losses:
 // kernel boundaries and grid synchronisation; the fix it names is a single
-// resident program with the next phase's loads issued across the sync).
+// resident program whose weight prefetch overlaps the compute sections).
 //
-// Memory-level parallelism: with one 4-wave workgroup per CU, HBM stays busy
-// only if every wave keeps tens of KiB of loads outstanding.  Each GEMV
-// phase is therefore a RowStream: a ring of DEPTH register buffers, each a
-// task of R rows; reducing task t is followed at once by issuing task
-// t + 4*DEPTH into the freed buffer.  The weights never depend on
-// activations, so each barrier is split into arrive and wait and the next
-// phase's whole ring is issued in between; the gate/up ring is issued even
-// earlier, before the attention -> output-projection barrier, so that its
-// 32 MB stream runs under the latency-bound attention and projection.
+// Dataflow instead of barriers.  Every vector one phase hands to the next
+// (the residual stream after each projection, the rotated q with the new
+// K/V row, the attention partials and output, the SwiGLU output, the argmax
+// candidates) is published as 64-bit words that carry the value in the low
+// half and a tag naming the (step, layer) in the high half, written with one
+// agent-coherent store each.  A consumer polls exactly the words it needs
+// until every tag matches; a word is never torn, so seeing the tag means
+// seeing the value, and the data arrives in the same round trip that
+// signals it.  Only words still missing are fetched again.  Each object has
+// one buffer: the next write of any object causally follows every read of
+// its previous contents (every phase needs the whole output of the one
+// before it), so no reader can meet a newer tag than the one it waits for.
 //
-// Data produced and consumed inside the launch (residual stream, q, the
-// attention output, SwiGLU output, partials, the new K/V row) is written
-// with agent-coherent stores and read with agent-coherent loads, staged once
-// per workgroup in LDS; see rd_device.h.
+// Roles inside a workgroup (4 waves, one per SIMD: the control wave has a
+// SIMD and its whole register file to itself).  A wave's vector-memory
+// counter completes in order, so a load the critical path waits on would sit
+// behind every weight load the same wave has in flight; the roles are split:
+//   - waves 1..3 (stream) only move and reduce weights.  Each owns a ring of
+//     RING 1 KiB slots in LDS and a cursor over the weight rows it reduces,
+//     in the order it reduces them, across phases, layers and steps.  Loads
+//     go straight from HBM into the ring (global_load_lds_dwordx4,
+//     non-temporal: no VGPRs held, nothing kept in L2), RING slots ahead of
+//     the row being reduced, so the ring keeps filling with the next
+//     phases' rows while the control wave waits for inputs or attends.
+//   - wave 0 (control) polls each phase's input, stages it into LDS (with
+//     the RMSNorm where the phase has one), runs every epilogue from the row
+//     sums (RoPE and the KV append, residual adds, SwiGLU, logits, argmax),
+//     the workgroup's attention split (its K/V rows fetched while the QKV
+//     rows stream) and, in some workgroups, the merge of one query head.
+//
+// Every arithmetic step is the one the kernel-per-phase executor performs
+// (rd_phases.h), in the same order, so both executors give identical bits.
+#include <algorithm>
+
 #include "rd_phases.h"
 
 namespace rd {
 
 namespace {
 
-// ---- grid barrier -------------------------------------------------------------
-// Arrival: every workgroup's stores are drained, then thread 0 counts on
-// sub-counter blockIdx % BAR_SUB; the last of a sub-group counts on the top
-// counter; the last overall resets the counters and publishes the next
-// generation.  Waiting: thread 0 polls the generation word.  A spin limit
-// turns a barrier that never completes into an error flag and an abort that
-// lets every wave run to the end of the kernel.
-__device__ __forceinline__ void grid_arrive(const PersistArgs& P, unsigned gen) {
-    drain_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* bar = P.bar;
-        const int nwg = gridDim.x, id = blockIdx.x;
-        const int sub = id % BAR_SUB;
-        const int members = (nwg - 1 - sub) / BAR_SUB + 1, groups = min(nwg, BAR_SUB);
-        if (__hip_atomic_fetch_add(&bar[sub * BAR_STRIDE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            members - 1) {
-            st_agent(&bar[sub * BAR_STRIDE], 0);
-            drain_vmem();
-            if (__hip_atomic_fetch_add(&bar[BAR_SUB * BAR_STRIDE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                groups - 1) {
-                st_agent(&bar[BAR_SUB * BAR_STRIDE], 0);
-                drain_vmem();
-                st_agent(&bar[(BAR_SUB + 1) * BAR_STRIDE], (int)(gen + 1));
-            }
-        }
-    }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+constexpr int NSW = 3;                  // stream waves per workgroup (waves 1..3)
+constexpr int PWG = (NSW + 1) * WAVE;   // threads per workgroup
+constexpr int UNIT = 1024;              // bytes per ring slot: 16 per lane, one chunk of one row
+constexpr int RING = 40;                // ring slots per stream wave
+constexpr int PART_MAX = 512;           // row sums a workgroup holds per phase
+constexpr int OWN_MAX = 64;             // residual-stream rows a workgroup owns
+constexpr int NPF = 2;                  // attention batches fetched during the QKV phase
+constexpr int LB_MAX = 1024;            // workgroups (argmax candidates)
+
+// buf[i] with a 32-bit byte offset on a scalar base (one VGPR per address).
+__device__ __forceinline__ const uint64_t* word_at(const uint64_t* buf, int i) {
+    return reinterpret_cast<const uint64_t*>(reinterpret_cast<const char*>(buf) + (uint32_t)i * 8u);
 }
 
-__device__ __forceinline__ void grid_wait(const PersistArgs& P, unsigned& gen, int* err) {
-    if (threadIdx.x == 0) {
-        const int* genw = &P.bar[(BAR_SUB + 1) * BAR_STRIDE];
-        int* abort = &P.bar[(BAR_SUB + 2) * BAR_STRIDE];
-        const unsigned target = gen + 1;
-        int n = 0;
-        while ((int)((unsigned)ld_agent(genw) - target) < 0) {
-            __builtin_amdgcn_s_sleep(1);
-            if ((++n & 255) == 0) {
-                if (ld_agent(abort)) break;
-                if (n > P.spin_limit) {
-                    st_agent(abort, 1);
-                    atomicOr(err, ERR_BARRIER);
-                    break;
-                }
-            }
-        }
-    }
-    __syncthreads();
-    gen += 1;
+// Workgroup barrier that orders LDS only.  The waves of a workgroup share
+// nothing but LDS (the staged input, the row sums, the trace counter; each
+// ring is read only by the wave that fills it), so a barrier waits for this
+// wave's LDS operations and nothing else.  __syncthreads() would also wait
+// for every outstanding global load: a stream wave would drain its whole
+// ring at each phase boundary and lose the prefetch.  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
+    return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
 }
-
-// ---- alternative barrier schemes (measured by the barrier probe) ------------------
-// Epoch e = the barrier's 1-based index since the words were zeroed; all
-// counters and flags only grow, so nothing is reset on the critical path.
-//   1: one counter, every workgroup adds 1 and polls it until e * nwg;
-//   2: BAR_SUB sub-counters (id % BAR_SUB); a sub-group's last arrival adds 1
-//      to the top counter; every workgroup polls the top until e * groups;
-//   3: flags: workgroup b stores e into word b of a packed array; every
-//      workgroup's threads poll all flags (one each) until all reach e;
-//   4: as 3 with each flag on its own 128-byte line.
-template <int MODE>
-__device__ __forceinline__ void bar_arrive(const PersistArgs& P, unsigned gen) {
-    if constexpr (MODE == 0) {
-        grid_arrive(P, gen);
-        return;
-    }
-    drain_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int* bar = P.bar;
-        const unsigned e = gen + 1;
-        const int nwg = gridDim.x, id = blockIdx.x;
-        if constexpr (MODE == 1) {
-            __hip_atomic_fetch_add(&bar[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if constexpr (MODE == 2) {
-            const int sub = id % BAR_SUB;
-            const unsigned members = (unsigned)((nwg - 1 - sub) / BAR_SUB + 1);
-            const unsigned old =
-                (unsigned)__hip_atomic_fetch_add(&bar[sub * BAR_STRIDE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (old + 1u == e * members)
-                __hip_atomic_fetch_add(&bar[BAR_SUB * BAR_STRIDE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else if constexpr (MODE == 3 || MODE == 5 || MODE == 6) {
-            st_agent(&bar[BAR_FLAGS + id], (int)e);
-        } else {
-            st_agent(&bar[BAR_FLAGS + id * BAR_STRIDE], (int)e);
-        }
-    }
+__device__ __forceinline__ void publish(uint64_t* p, float v, uint32_t tag) { st_agent(p, tagged(v, tag)); }
+__device__ __forceinline__ uint32_t tag_of(const StepArgs& A, const PersistArgs& P, int step, int layer) {
+    return P.tag0 + (uint32_t)step * (uint32_t)(A.n_layers + 1) + (uint32_t)layer + 1u;
 }
+// 12-bit tag of the argmax words: never 0, so zero-filled words never match.
+__device__ __forceinline__ uint32_t tag12(uint32_t tag) { return tag % 4095u + 1u; }
 
-template <int MODE>
-__device__ __forceinline__ void bar_wait(const PersistArgs& P, unsigned& gen, int* err) {
-    if constexpr (MODE == 0) {
-        grid_wait(P, gen, err);
-        return;
-    }
-    const unsigned e = gen + 1;
-    const int nwg = gridDim.x;
-    int* abort = &P.bar[(BAR_SUB + 2) * BAR_STRIDE];
-    if constexpr (MODE == 1 || MODE == 2) {
-        if (threadIdx.x == 0) {
-            const int* w = MODE == 1 ? &P.bar[0] : &P.bar[BAR_SUB * BAR_STRIDE];
-            const unsigned target = MODE == 1 ? e * (unsigned)nwg : e * (unsigned)min(nwg, BAR_SUB);
-            int n = 0;
-            while ((int)((unsigned)ld_agent(w) - target) < 0) {
-                __builtin_amdgcn_s_sleep(1);
-                if ((++n & 255) == 0) {
-                    if (ld_agent(abort)) break;
-                    if (n > P.spin_limit) {
-                        st_agent(abort, 1);
-                        atomicOr(err, ERR_BARRIER);
-                        break;
-                    }
+// ---- waiting ------------------------------------------------------------------
+// Every wait counts its polls; past the spin limit it raises the abort word
+// and an error bit, and every wait that sees the abort word gives up too, so
+// a launch always runs to its end.
+struct Waiter {
+    int* abort_word;
+    int* err;
+    int limit, n;
+    __device__ __forceinline__ bool again() {   // false: give up
+        if ((++n & 63) == 0) {
+            if (ld_agent(abort_word)) return false;
+            if (n > limit) {
+                if (lane_id() == 0) {
+                    st_agent(abort_word, 1);
+                    atomicOr(err, ERR_STALL);
                 }
+                return false;
             }
         }
-        __syncthreads();
-    } else if constexpr (MODE == 5 || MODE == 6) {
-        // wave 0 alone polls the packed flags, two per 8-byte load, and votes
-        if (threadIdx.x < WAVE) {
-            int n = 0;
-            while (true) {
-                int ok = 1;
-                for (int i = threadIdx.x * 2; i < nwg; i += 2 * WAVE) {
-                    const uint64_t v = xld64<true>(reinterpret_cast<const uint64_t*>(&P.bar[BAR_FLAGS + i]));
-                    ok &= (int)((unsigned)v - e) >= 0;
-                    if (i + 1 < nwg) ok &= (int)((unsigned)(v >> 32) - e) >= 0;
-                }
-                if (__ballot(ok) == ~0ull) break;
-                if constexpr (MODE == 5) __builtin_amdgcn_s_sleep(1);
-                if ((++n & 255) == 0) {
-                    if (ld_agent(abort)) break;
-                    if (n > P.spin_limit) {
-                        if (threadIdx.x == 0) {
-                            st_agent(abort, 1);
-                            atomicOr(err, ERR_BARRIER);
-                        }
-                        break;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-    } else {
-        const int stride = MODE == 3 ? 1 : BAR_STRIDE;
-        int n = 0;
-        while (true) {
-            int ok = 1;
-            for (int i = threadIdx.x; i < nwg; i += WG)
-                ok &= (int)((unsigned)ld_agent(&P.bar[BAR_FLAGS + i * stride]) - e) >= 0;
-            if (__syncthreads_and(ok)) break;
-            __builtin_amdgcn_s_sleep(1);
-            if ((++n & 255) == 0) {
-                if (__syncthreads_or(threadIdx.x == 0 ? ld_agent(abort) : 0)) break;
-                if (n > P.spin_limit) {
-                    if (threadIdx.x == 0) {
-                        st_agent(abort, 1);
-                        atomicOr(err, ERR_BARRIER);
-                    }
-                    break;
-                }
-            }
-        }
-    }
-    gen += 1;
-}
-
-// The scheme the decode kernel uses: measured on MI355X with one workgroup
-// per CU, packed epoch flags polled by every thread took 1.4 us per barrier,
-// the two-level counter tree 2.3-2.6 us, a single counter 3.8 us.
-constexpr int BAR_MODE = 3;
-
-// Task range of this workgroup when T tasks are spread evenly over gridDim.x.
-__device__ __forceinline__ void wg_range(int T, int& beg, int& end) {
-    beg = (int)((long long)T * blockIdx.x / gridDim.x);
-    end = (int)((long long)T * (blockIdx.x + 1) / gridDim.x);
-}
-
-// A wave's share of one GEMV phase: task t = rows [t*R, t*R+R) of the
-// row-major [N, K] matrix W; this workgroup's tasks are a contiguous range
-// and its waves take every 4th; DEPTH tasks are in flight per wave.
-template <int R, int KCH, int DEPTH>
-struct RowStream {
-    u4v buf[DEPTH][R][KCH];
-    const _Float16* W;
-    int K, N, t0, tend;
-
-    __device__ __forceinline__ void issue(int d, int t) {
-        load_rows<R, KCH>(W, K, t * R, t < tend ? min(R, N - t * R) : 0, buf[d]);
-    }
-    // Issue this wave's first DEPTH tasks of a phase of T tasks.
-    __device__ __forceinline__ void start(const _Float16* W_, int K_, int N_, int T) {
-        W = W_;
-        K = K_;
-        N = N_;
-        int beg;
-        wg_range(T, beg, tend);
-        t0 = beg + (int)(threadIdx.x >> 6);
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) issue(d, t0 + 4 * d);
-    }
-    // Reduce every task against the register-resident input xr, in order,
-    // refilling each buffer as soon as it is consumed.
-    template <class Epi>
-    __device__ __forceinline__ void run(const float (&xr)[KCH][8], Epi&& epi) {
-        for (int base = t0; base < tend; base += 4 * DEPTH) {
-#pragma unroll
-            for (int d = 0; d < DEPTH; ++d) {
-                const int t = base + 4 * d;
-                if (t < tend) {
-                    float acc[R];
-                    dot_loaded<R, KCH>(buf[d], xr, acc);
-                    epi(t, acc);
-                    issue(d, t + 4 * DEPTH);
-                }
-            }
-        }
+        return true;
     }
 };
 
-}  // namespace
+// Poll NW words per lane (word idx(k) where act(k)) until each carries tag;
+// val[k] receives the values (0 where !act(k)).  A word is fetched again
+// only while the copy in hand still has an old tag; inactive words start as
+// received.
+template <int NW, class IDX, class ACT>
+__device__ __forceinline__ void poll_words(Waiter& wt, const uint64_t* buf, IDX&& idx, ACT&& act, uint32_t tag,
+                                           float (&val)[NW]) {
+    const uint64_t done = (uint64_t)tag << 32;
+    uint64_t v[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) v[k] = act(k) ? 0ull : done;
+    wt.n = 0;
+    while (true) {
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+            if ((uint32_t)(v[k] >> 32) != tag) v[k] = ld_agent(word_at(buf, idx(k)));
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) all &= (uint32_t)(v[k] >> 32) == tag;
+        if (__all(all)) break;
+        if (!wt.again()) break;
+    }
+#pragma unroll
+    for (int k = 0; k < NW; ++k) val[k] = __uint_as_float((uint32_t)v[k]);
+}
 
-// Ring depths, sized to the work per wave at the 2B-class shapes with one
-// workgroup per CU (1024 waves): QKV 2 tasks, output projection 1, gate/up
-// 5-6, down 2, LM head ~8; every wave's whole QKV, O and down share is in
-// flight at once, gate/up and LM head keep 32 KiB in flight per wave.
-template <int KD, int KA, int KF, int HD, int G, int KVF>
-__global__ __launch_bounds__(WG) void k_persist(StepArgs A, PersistArgs P) {
-    constexpr int KMAX = KF > KD ? (KF > KA ? KF : KA) : (KD > KA ? KD : KA);
-    constexpr int DQ = 2, DO = 2, DG = 4, DD = 2, DL = 2;
-    __shared__ __attribute__((aligned(16))) float s_vec[KMAX * 512];
-    const int lane = threadIdx.x & 63;
-    const int D = A.D, F = A.F, V = A.V;
-    const int Nqkv = (A.H + 2 * A.Hk) * A.hd, Na = A.H * A.hd;
-    unsigned gen = P.gen0;
-    int* err = &A.st->err;
-    int n_ev = 0;
-    auto TR = [&](int code) {
-        if (P.trace && blockIdx.x == 0 && threadIdx.x == 0 && n_ev < P.trace_cap) {
-            P.trace[1 + 2 * n_ev] = (unsigned long long)code;
-            P.trace[2 + 2 * n_ev] = wall_clock64();
-            P.trace[0] = (unsigned long long)++n_ev;
+// Poll a K-element vector published in the GEMV input layout (lane l, chunk
+// c: elements (c*64+l)*8..+7) into registers, in one round trip.
+template <int KCH>
+__device__ __forceinline__ void poll_vec(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float (&xr)[KCH][8]) {
+    const int lane = lane_id();
+    float val[KCH * 8];
+    auto col = [&](int k) { return ((k / 8) * 64 + lane) * 8 + k % 8; };
+    poll_words<KCH * 8>(wt, buf, col, [&](int k) { return col(k) < K; }, tag, val);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xr[c][i] = val[c * 8 + i];
+}
+
+template <int KCH>
+__device__ __forceinline__ void regs_to_lds(float* s, int K, const float (&xr)[KCH][8]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        if (col < K) {
+            *reinterpret_cast<float4*>(s + col) = make_float4(xr[c][0], xr[c][1], xr[c][2], xr[c][3]);
+            *reinterpret_cast<float4*>(s + col + 4) = make_float4(xr[c][4], xr[c][5], xr[c][6], xr[c][7]);
         }
-    };
-    TR(99);
+    }
+}
 
-    int tok = A.st->token[0];
-    if (tok < 0 || tok >= V) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, ERR_TOKEN);
-        tok = 0;
+// ---- event trace -----------------------------------------------------------------
+// Lane 0 of the control wave and of stream wave 0 append (code, wall clock)
+// events to the workgroup's region; the count lives in LDS and is written
+// out by the control wave at the end of the launch.
+__device__ __attribute__((noinline)) void trace_event(unsigned long long* tb, int cap, int* s_nev, int code) {
+    if (lane_id() == 0) {
+        const int i = atomicAdd(s_nev, 1);
+        if (i < cap) {
+            tb[1 + 2 * i] = (unsigned long long)code;
+            tb[2 + 2 * i] = wall_clock64();
+        }
+    }
+}
+struct Tracer {
+    unsigned long long* tb;   // this workgroup's region, or null
+    int cap;
+    int* s_nev;
+    __device__ __forceinline__ void operator()(int code) const {
+        if (tb) trace_event(tb, cap, s_nev, code);
+    }
+};
+__device__ __forceinline__ Tracer make_tracer(const PersistArgs& P, int* s_nev) {
+    Tracer t{nullptr, 0, s_nev};
+    if (P.trace && (P.trace_all || blockIdx.x == 0)) {
+        t.tb = P.trace + (P.trace_all ? (size_t)blockIdx.x * (1 + 2 * (size_t)P.trace_cap) : 0);
+        t.cap = P.trace_cap;
+    }
+    return t;
+}
+
+// ---- weight schedule ------------------------------------------------------------
+// Rows [r0, r1) of this workgroup when N rows are dealt to the grid in tasks
+// of rpt consecutive rows (T * blockIdx < 2^32 for every shape built).
+__device__ __forceinline__ void wg_rows(int N, int rpt, int& r0, int& r1) {
+    const unsigned T = (unsigned)(N / rpt), b = blockIdx.x, n = gridDim.x;
+    r0 = (int)(T * b / n) * rpt;
+    r1 = (int)(T * (b + 1) / n) * rpt;
+}
+
+// Phase ph of a step: 4 per layer (QKV, output projection, gate/up, down),
+// then the LM head.  RoPE pairs and gate/up pairs stay in one workgroup.
+struct PhaseGeo {
+    const _Float16* W;
+    int K, kch;
+    int r0, r1;   // this workgroup's rows
+};
+// Layer l's copy of a weight whose layer-0 copy is at p0: the weight image
+// repeats one layer block at a fixed stride, so every weight address is
+// scalar arithmetic on kernel arguments.
+__device__ __forceinline__ const _Float16* layer_w(const PersistArgs& P, const _Float16* p0, int l) {
+    return reinterpret_cast<const _Float16*>(reinterpret_cast<const char*>(p0) + (long long)l * P.layer_stride);
+}
+
+template <int KD, int KA, int KF>
+__device__ __forceinline__ PhaseGeo phase_geo(const StepArgs& A, const PersistArgs& P, int ph) {
+    PhaseGeo g;
+    if (ph == 4 * A.n_layers) {
+        g.W = A.lm_head; g.K = A.D; g.kch = KD;
+        wg_rows(A.V, 1, g.r0, g.r1);
+    } else {
+        const int l = ph >> 2;
+        switch (ph & 3) {
+            case 0:
+                g.W = layer_w(P, P.layer0.wqkv, l); g.K = A.D; g.kch = KD;
+                wg_rows((A.H + 2 * A.Hk) * A.hd, 2, g.r0, g.r1);
+                break;
+            case 1: g.W = layer_w(P, P.layer0.wo, l); g.K = A.H * A.hd; g.kch = KA; wg_rows(A.D, 1, g.r0, g.r1); break;
+            case 2: g.W = layer_w(P, P.layer0.wgu, l); g.K = A.D; g.kch = KD; wg_rows(2 * A.F, 2, g.r0, g.r1); break;
+            default: g.W = layer_w(P, P.layer0.wd, l); g.K = A.F; g.kch = KF; wg_rows(A.D, 1, g.r0, g.r1); break;
+        }
+    }
+    return g;
+}
+__device__ __forceinline__ void wave_rows(const PhaseGeo& g, int sw, int& ra, int& rb) {
+    const int n = g.r1 - g.r0;
+    ra = g.r0 + n * sw / NSW;
+    rb = g.r0 + n * (sw + 1) / NSW;
+}
+
+// A stream wave's load cursor: the next 1 KiB chunk to request and the ring
+// slot it goes to.  Past the last row of the launch it keeps requesting the
+// first rows of the LM head (never reduced), so that exactly RING requests
+// are always outstanding or landed beyond the slot being read and every wait
+// is the same constant.
+// The wave's rows of each of the five phase kinds (QKV, output projection,
+// gate/up, down, LM head) are the same in every layer and step; they are
+// computed once, so moving to the next phase is a table lookup.
+// FK (every K a multiple of 512): a wave's rows of one phase are one
+// contiguous byte range of whole 1 KiB chunks, so the cursor is a pointer
+// and a count of chunks left in the range.  Otherwise rows end inside a
+// chunk: the cursor walks (row, chunk) and lanes past K read the chunk's
+// first 16 bytes (in bounds), masked when reduced.
+// a[k] for a wave-uniform k through selects: a private array indexed at run
+// time would live in scratch memory.
+__device__ __forceinline__ int pick5(const int (&a)[5], int k) {
+    return k == 0 ? a[0] : k == 1 ? a[1] : k == 2 ? a[2] : k == 3 ? a[3] : a[4];
+}
+
+template <int KD, int KA, int KF, bool FK>
+struct Feeder {
+    const char* p;   // FK: next chunk; else: start of the current row
+    int left;        // FK: chunks left in the current range
+    int K, kch, c, row, rend;   // !FK
+    int ph, step, slot;
+    unsigned char* ring;
+    int ra[5], nr[5], r0[5];    // per phase kind: this wave's first row and row count, the workgroup's first row
+
+    __device__ __forceinline__ void init(const StepArgs& A, const PersistArgs& P, int sw) {
+        for (int k = 0; k < 5; ++k) {
+            const PhaseGeo g = phase_geo<KD, KA, KF>(A, P, k == 4 ? 4 * A.n_layers : k);
+            int a, b;
+            wave_rows(g, sw, a, b);
+            ra[k] = a;
+            nr[k] = b - a;
+            r0[k] = g.r0;
+        }
+    }
+    __device__ __forceinline__ void seek(const StepArgs& A, const PersistArgs& P) {
+        const int NP = 4 * A.n_layers + 1;
+        while (true) {
+            if (ph == NP) {
+                ph = 0;
+                if (++step >= P.n_steps) {
+                    p = reinterpret_cast<const char*>(A.lm_head);
+                    left = INT_MAX;
+                    K = A.D;
+                    kch = KD;
+                    c = 0;
+                    row = 0;
+                    rend = INT_MAX;
+                    return;
+                }
+            }
+            const int k = ph == NP - 1 ? 4 : (ph & 3), l = ph >> 2;
+            const int nrk = pick5(nr, k), rak = pick5(ra, k);
+            if (nrk > 0) {
+                const _Float16* W;
+                switch (k) {
+                    case 0: W = layer_w(P, P.layer0.wqkv, l); K = A.D; kch = KD; break;
+                    case 1: W = layer_w(P, P.layer0.wo, l); K = A.H * A.hd; kch = KA; break;
+                    case 2: W = layer_w(P, P.layer0.wgu, l); K = A.D; kch = KD; break;
+                    case 3: W = layer_w(P, P.layer0.wd, l); K = A.F; kch = KF; break;
+                    default: W = A.lm_head; K = A.D; kch = KD; break;
+                }
+                p = reinterpret_cast<const char*>(W + (size_t)rak * K);
+                left = nrk * kch;
+                c = 0;
+                row = rak;
+                rend = rak + nrk;
+                return;
+            }
+            ++ph;
+        }
+    }
+    __device__ __forceinline__ void issue(const StepArgs& A, const PersistArgs& P) {
+        // cache policy 2: non-temporal (every weight byte is read once per step)
+        if constexpr (FK) {
+            __builtin_amdgcn_global_load_lds((glb_void*)(p + (uint32_t)lane_id() * 16u),
+                                             (lds_void*)(ring + slot * UNIT), 16, 0, 2);
+            p += UNIT;
+            slot = slot + 1 == RING ? 0 : slot + 1;
+            if (--left == 0) {
+                ++ph;
+                seek(A, P);
+            }
+        } else {
+            unsigned off = (unsigned)lane_id() * 16u;
+            if (c * 1024 + (int)off >= 2 * K) off = 0;
+            __builtin_amdgcn_global_load_lds((glb_void*)(p + c * 1024 + off), (lds_void*)(ring + slot * UNIT), 16, 0,
+                                             2);
+            slot = slot + 1 == RING ? 0 : slot + 1;
+            if (++c == kch) {
+                c = 0;
+                p += 2 * K;
+                if (++row == rend) {
+                    ++ph;
+                    seek(A, P);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void start(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* r) {
+        ring = r;
+        init(A, P, sw);
+        ph = 0;
+        step = 0;
+        slot = 0;
+        seek(A, P);
+        for (int i = 0; i < RING; ++i) issue(A, P);
+    }
+};
+
+// Reduce the next NR rows (KCH chunks each) of the wave's stream against the
+// register-resident input xr: wait for their slots, read them, refill them,
+// then the dot products of dot_rows.
+template <int NR, int KCH, bool FK, class F>
+__device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const PersistArgs& P, int sw,
+                                             unsigned char* ring, const float (&xr)[KCH][8], int K,
+                                             float (&out)[NR]) {
+    static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
+    const int lane = lane_id();
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
+    u4v w[NR][KCH];
+    int s = f.slot;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            w[r][c] = *reinterpret_cast<const u4v*>(ring + s * UNIT + lane * 16);
+            s = s + 1 == RING ? 0 : s + 1;
+        }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slots read before they are refilled
+    for (int i = 0; i < NR * KCH; ++i) f.issue(A, P);
+    if constexpr (!FK) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            if ((c * 64 + lane) * 8 >= K)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) w[r][c] = u4v{0u, 0u, 0u, 0u};
+    }
+    dot_rows<NR, KCH>(w, xr, out);
+}
+
+// A stream wave's share of GEMV phase ph, between the workgroup barriers
+// that bracket it: its rows' sums into s_part.
+template <int KCH, int KD, int KA, int KF, bool FK, class F>
+__device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const PersistArgs& P, int sw,
+                                             unsigned char* ring, const float* s_r, float* s_part, int ph,
+                                             const Tracer& tr) {
+    constexpr int NR = KCH <= 4 ? 2 : 1;
+    lds_barrier();   // input staged
+    const int kind = ph == 4 * A.n_layers ? 4 : (ph & 3);
+    if (sw == 0) tr(100 + 10 * kind);
+    const int K = kind == 1 ? A.H * A.hd : kind == 3 ? A.F : A.D;
+    const int ra = pick5(f.ra, kind), rb = ra + pick5(f.nr, kind), r0 = pick5(f.r0, kind);
+    if (ra < rb) {
+        float xr[KCH][8];
+        load_x_f32<KCH>(s_r, K, xr);
+        int r = ra;
+        for (; r + NR <= rb; r += NR) {
+            float v[NR];
+            consume_rows<NR, KCH, FK>(f, A, P, sw, ring, xr, K, v);
+            if (sw == 0 && r == ra) tr(101 + 10 * kind);
+            if (lane_id() == 0)
+#pragma unroll
+                for (int k = 0; k < NR; ++k) s_part[r + k - r0] = v[k];
+        }
+        if (r < rb) {
+            float v[1];
+            consume_rows<1, KCH, FK>(f, A, P, sw, ring, xr, K, v);
+            if (lane_id() == 0) s_part[r - r0] = v[0];
+        }
+    }
+    if (sw == 0) tr(102 + 10 * kind);
+    lds_barrier();   // row sums complete
+}
+
+template <int KD, int KA, int KF, bool FK>
+__device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* ring,
+                                            const float* s_r, float* s_part, int* s_nev) {
+    const Tracer tr = make_tracer(P, s_nev);
+    Feeder<KD, KA, KF, FK> f;
+    f.start(A, P, sw, ring);
+    const int NL = A.n_layers;
+    for (int step = 0; step < P.n_steps; ++step) {
+        for (int l = 0; l < NL; ++l) {
+            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr);
+            stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr);
+            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr);
+            stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr);
+        }
+        stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr);
+    }
+    drain_vmem();   // the trailing ring requests land before the wave ends
+    lds_barrier();   // matches the control wave's last barrier (trace count)
+}
+
+// ---- control wave ---------------------------------------------------------------------
+template <int KD, int KA, int KF, int HD, int G, int KVF, int SMAX>
+__device__ __forceinline__ void control_role(const StepArgs& A, const PersistArgs& P, float* s_r,
+                                             const float* s_part, float* s_own, int* s_nev) {
+    using Geo = AttnGeo<HD>;
+    constexpr int U = Geo::U, LPR = Geo::LPR, RPW = Geo::RPW;
+    const int lane = lane_id(), NL = A.n_layers, b = blockIdx.x, nwg = gridDim.x;
+    Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
+    const Tracer TR = make_tracer(P, s_nev);
+    TR(99);
+    auto check_token = [&](int t) {
+        if (t < 0 || t >= A.V) {
+            if (b == 0 && lane == 0) atomicOr(&A.st->err, ERR_TOKEN);
+            t = 0;
+        }
+        return t;
+    };
+    int tok = check_token(A.st->token[0]);
+    const int Nq = A.H * HD, Nk = A.Hk * HD;
+    // merge task of this workgroup: query head hm, 64 dims from part*64
+    const int nmt = A.H * Geo::NPART, mstride = nwg / nmt;
+    const int mt = (b % mstride == 0 && b / mstride < nmt) ? b / mstride : -1;
+    const int hm = mt / Geo::NPART, mpart = mt % Geo::NPART;
+    int qr0, qr1, dr0, dr1, gr0, gr1, lr0, lr1;
+    {
+        const PhaseGeo gq = phase_geo<KD, KA, KF>(A, P, 0), gd = phase_geo<KD, KA, KF>(A, P, 1),
+                       gg = phase_geo<KD, KA, KF>(A, P, 2), gl = phase_geo<KD, KA, KF>(A, P, 4 * NL);
+        qr0 = gq.r0; qr1 = gq.r1; dr0 = gd.r0; dr1 = gd.r1; gr0 = gg.r0; gr1 = gg.r1; lr0 = gl.r0; lr1 = gl.r1;
     }
 
-    RowStream<2, KD, DQ> sq;
-    sq.start(P.layers[0].wqkv, D, Nqkv, Nqkv / 2);
-
     for (int step = 0; step < P.n_steps; ++step) {
-        const int pos = P.pos0 + step;
-        for (int l = 0; l < A.n_layers; ++l) {
-            const LayerW Lw = P.layers[l];
+        const int pos = P.pos0 + step, L = pos + 1;
+        int chunk, nact;
+        split_plan(L, A.S, chunk, nact);
+        const int open0 = pos / SEG * SEG;
+        const int t = b < A.Hk * nact ? b : -1;
+        const int g = t / nact, s = t % nact;
+        const int p0 = s * chunk, p1 = min(L, p0 + chunk);
+        const float2* rope = A.rope + (size_t)pos * (HD / 2);
+        // (cos, sin) of the RoPE pair each lane rotates in the QKV epilogue
+        float2 cs_lane = make_float2(1.f, 0.f);
+        if (2 * lane < qr1 - qr0) cs_lane = rope[((qr0 + 2 * lane) % HD) >> 1];
+        // gains of the first RMSNorm (later ones are loaded while the wait before
+        // them is pending, so that their latency hides in the wait)
+        u4v gain[KD];
+        load_gain<KD>(P.layer0.g_attn, A.D, gain);
+        for (int l = 0; l < NL; ++l) {
+            const uint32_t tag = tag_of(A, P, step, l);
+            const AttnArgs T = attn_args(A, l);
             // ---------------- RMSNorm + QKV + RoPE + KV append ----------------
             {
                 float xr[KD][8];
                 if (l == 0) {
-                    load_x_f16<KD>(A.embed + (size_t)tok * D, D, xr);
+                    const _Float16* e = A.embed + (size_t)tok * A.D;
+                    load_x_f16<KD>(e, A.D, xr);
+                    for (int i = lane; i < dr1 - dr0; i += WAVE) s_own[i] = (float)e[dr0 + i];
                 } else {
-                    stage_vec<true, KD * 512>(s_vec, A.x, D);
-                    load_x_f32<KD>(s_vec, D, xr);
+                    poll_vec<KD>(wt, A.xb1, A.D, tag_of(A, P, step, l - 1), xr);
                 }
-                rmsnorm_regs<KD>(xr, Lw.g_attn, D, A.eps);
-                TR(0 + TR_STAGED);
-                sq.run(xr, [&](int t, const float (&acc)[2]) {
-                    if (lane == 0) qkv_epilogue<KVF, true>(A, l, pos, 2 * t, acc[0], acc[1]);
-                });
+                TR(0 + TR_RECV);
+                rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
+                regs_to_lds<KD>(s_r, A.D, xr);
             }
+            TR(0 + TR_STAGED);
+            lds_barrier();
+            // While the QKV rows stream: this workgroup's first K/V rows of its split.
+            KvRaw kr[NPF][U], vr[NPF][U];
+#pragma unroll
+            for (int bb = 0; bb < NPF; ++bb) {
+                const int pb = p0 + bb * Geo::BATCH;
+                if (t >= 0 && pb < p1) kv_batch_raw<HD, KVF, true>(T, g, pb, p0, p1, open0, kr[bb], vr[bb]);
+            }
+            lds_barrier();
             TR(0 + TR_DONE);
-            RowStream<2, KA, DO> so;
-            bar_arrive<BAR_MODE>(P, gen);
-            TR(0 + TR_ARRIVED);
-            so.start(Lw.wo, Na, D, D / 2);
-            TR(0 + TR_ISSUED);
-            bar_wait<BAR_MODE>(P, gen, err);
-            TR(10 + TR_WAIT);
-            // ---------------- attention (split-K, LSE merge, INT8 seal) ----------------
-            {
-                const AttnArgs T = attn_args(A, l);
-                int chunk, nact;
-                split_plan(pos + 1, A.S, chunk, nact);
-                for (int t = blockIdx.x; t < A.Hk * nact; t += gridDim.x) {
-                    const int g = t / nact, s = t % nact;
-                    attn_split<HD, G, KVF, true>(T, g, s, chunk, pos);
-                    attn_arrive<HD, G, KVF, true>(T, g, nact, pos);
+            // On the step that seals an INT8 segment the merge reads the open
+            // segment, this step's row included: that row is stored before the
+            // q/k/v words that lead to the merge are published.
+            const bool seal_step = KVF == KV_INT8 && (pos + 1) % SEG == 0;
+            for (int q = lane; 2 * q < qr1 - qr0; q += WAVE) {
+                const float2 cs = q == lane ? cs_lane : rope[((qr0 + 2 * q) % HD) >> 1];
+                const QkvPair o = qkv_pair(HD, A.H, A.Hk, qr0 + 2 * q, s_part[2 * q], s_part[2 * q + 1], &cs,
+                                           true);
+                if (o.kind == 0) {
+                    publish(&A.qb[o.head * HD + o.d0], o.y0, tag);
+                    publish(&A.qb[o.head * HD + o.d1], o.y1, tag);
+                } else {
+                    const int which = o.kind == 2;
+                    uint64_t* dst = A.qb + Nq + which * Nk + o.head * HD;
+                    const float s0 = kv_put<KVF, true>(A, l, which, o.head, pos, o.d0, o.y0);
+                    const float s1 = kv_put<KVF, true>(A, l, which, o.head, pos, o.d1, o.y1);
+                    if (seal_step) drain_vmem();
+                    publish(&dst[o.d0], s0, tag);
+                    publish(&dst[o.d1], s1, tag);
                 }
             }
-            TR(10 + TR_DONE);
-            RowStream<2, KD, DG> sg;
-            bar_arrive<BAR_MODE>(P, gen);
-            TR(10 + TR_ARRIVED);
-            sg.start(Lw.wgu, D, 2 * F, F);
-            TR(10 + TR_ISSUED);
-            bar_wait<BAR_MODE>(P, gen, err);
-            TR(20 + TR_WAIT);
+            TR(0 + TR_PUB);
+            // ---------------- attention split ----------------
+            if (t >= 0) {
+                const int lane = lane_id(), j = lane % LPR, slot = lane / LPR;
+                const bool has_new = p1 == L;
+                constexpr int NQ = G * 8 + 16;
+                float val[NQ];
+#pragma unroll
+                for (int k = 0; k < NQ; ++k) val[k] = 0.f;
+                // q of the group's heads, then the new K and V rows of kv-head g
+                auto qidx = [&](int k) {
+                    return k < G * 8 ? (g * G + k / 8) * HD + j * 8 + k % 8
+                                     : Nq + (k - G * 8) / 8 * Nk + g * HD + j * 8 + k % 8;
+                };
+                // the lanes of slot 0 poll; the other slots take their copy (same dims)
+                poll_words<NQ>(wt, A.qb, qidx, [&](int k) { return slot == 0 && (k < G * 8 || has_new); }, tag, val);
+#pragma unroll
+                for (int k = 0; k < NQ; ++k) val[k] = __shfl(val[k], j, WAVE);
+                TR(10 + TR_RECV);
+                float qv[G][8];
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) qv[h][i] = val[h * 8 + i] * (A.scale * LOG2E);
+                AttnAcc<HD, G> acc;
+                acc.clear();
+                // converted rows, with row pos (not yet visible in the cache) from the exchange
+                auto run_batch = [&](int pb, const KvRaw (&kk)[U], const KvRaw (&vv)[U]) {
+                    float kf[U][8], vf[U][8];
+                    bool valid[U];
+                    kv_batch_cvt<HD, KVF>(pb, p1, kk, vv, kf, vf, valid);
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        if (batch_row<HD>(pb, u, slot) == pos)
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                kf[u][i] = val[G * 8 + i];
+                                vf[u][i] = val[G * 8 + 8 + i];
+                            }
+                    acc.batch(qv, kf, vf, valid);
+                };
+#pragma unroll
+                for (int bb = 0; bb < NPF; ++bb) {
+                    const int pb = p0 + bb * Geo::BATCH;
+                    if (pb < p1) run_batch(pb, kr[bb], vr[bb]);
+                }
+                for (int pb = p0 + NPF * Geo::BATCH; pb < p1; pb += Geo::BATCH) {
+                    KvRaw kk[U], vv[U];
+                    kv_batch_raw<HD, KVF, true>(T, g, pb, p0, p1, open0, kk, vv);
+                    run_batch(pb, kk, vv);
+                }
+                acc.finish();
+                if (lane < LPR) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        uint64_t* dst = A.pb + ((size_t)(g * G + h) * A.S + s) * (HD + 2);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) publish(&dst[j * 8 + i], acc.o[h][i], tag);
+                        if (lane == 0) {
+                            publish(&dst[HD], acc.m[h], tag);
+                            publish(&dst[HD + 1], acc.l[h], tag);
+                        }
+                    }
+                }
+                TR(10 + TR_PUB);
+            }
+            // ---------------- merge of one query head ----------------
+            if (mt >= 0) {
+                const int lane = lane_id();
+                const uint64_t* base = A.pb + (size_t)hm * A.S * (HD + 2);
+                // o of splits 0..SMAX-1 at this lane's dim, then (m, l) of split `lane`
+                constexpr int NM = SMAX + 2;
+                float val[NM];
+#pragma unroll
+                for (int k = 0; k < NM; ++k) val[k] = k == SMAX ? -INFINITY : 0.f;
+                auto midx = [&](int k) {
+                    return k < SMAX ? k * (HD + 2) + mpart * 64 + lane : lane * (HD + 2) + HD + (k - SMAX);
+                };
+                poll_words<NM>(wt, base, midx, [&](int k) { return k < SMAX ? k < nact : lane < nact; }, tag, val);
+                TR(20 + TR_RECV);
+                float ms[MERGE_NC], ls[MERGE_NC];
+#pragma unroll
+                for (int c = 0; c < MERGE_NC; ++c) {
+                    ms[c] = c == 0 ? val[SMAX] : -INFINITY;
+                    ls[c] = c == 0 ? val[SMAX + 1] : 0.f;
+                }
+                const MergeW mw = merge_weights(nact, ms, ls);
+                float ov[64];
+#pragma unroll
+                for (int k = 0; k < 64; ++k) ov[k] = k < SMAX ? val[k] : 0.f;
+                float num = 0.f;
+                merge_acc<SMAX>(num, 0, mw, ov);
+                publish(&A.ab[hm * HD + mpart * 64 + lane], num / mw.den, tag);
+                if constexpr (KVF == KV_INT8) {
+                    if ((pos + 1) % SEG == 0 && mpart == 0 && hm % G == 0) {
+                        seal_head<HD, true>(T, hm / G, pos);
+                        drain_vmem();
+                    }
+                }
+                TR(20 + TR_PUB);
+            }
             // ---------------- output projection + residual ----------------
             {
                 float xr[KA][8];
-                stage_vec<true, KA * 512>(s_vec, A.a, Na);
-                load_x_f32<KA>(s_vec, Na, xr);
-                TR(20 + TR_STAGED);
-                so.run(xr, [&](int t, const float (&acc)[2]) {
-                    if (lane == 0) {
-#pragma unroll
-                        for (int r = 0; r < 2; ++r) {
-                            const int row = 2 * t + r;
-                            const float base = (l == 0) ? (float)A.embed[(size_t)tok * D + row] : ld_agent(&A.x[row]);
-                            st_agent(&A.x[row], base + acc[r]);
-                        }
-                    }
-                });
+                poll_vec<KA>(wt, A.ab, A.H * HD, tag, xr);
+                TR(30 + TR_RECV);
+                regs_to_lds<KA>(s_r, A.H * HD, xr);
             }
-            TR(20 + TR_DONE);
-            bar_arrive<BAR_MODE>(P, gen);
-            TR(20 + TR_ARRIVED);
-            bar_wait<BAR_MODE>(P, gen, err);
-            TR(30 + TR_WAIT);
+            lds_barrier();
+            lds_barrier();
+            TR(30 + TR_DONE);
+            for (int i = lane; i < dr1 - dr0; i += WAVE) {
+                const float xn = s_own[i] + s_part[i];
+                s_own[i] = xn;
+                publish(&A.xb2[dr0 + i], xn, tag);
+            }
+            TR(30 + TR_PUB);
+            load_gain<KD>(layer_w(P, P.layer0.g_ffn, l), A.D, gain);
             // ---------------- RMSNorm + gate/up + SwiGLU ----------------
             {
                 float xr[KD][8];
-                stage_vec<true, KD * 512>(s_vec, A.x, D);
-                load_x_f32<KD>(s_vec, D, xr);
-                rmsnorm_regs<KD>(xr, Lw.g_ffn, D, A.eps);
-                TR(30 + TR_STAGED);
-                sg.run(xr, [&](int t, const float (&acc)[2]) {
-                    if (lane == 0) st_agent(&A.m[t], acc[0] / (1.0f + expf(-acc[0])) * acc[1]);
-                });
+                poll_vec<KD>(wt, A.xb2, A.D, tag, xr);
+                TR(40 + TR_RECV);
+                rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
+                regs_to_lds<KD>(s_r, A.D, xr);
             }
-            TR(30 + TR_DONE);
-            RowStream<1, KF, DD> sd;
-            bar_arrive<BAR_MODE>(P, gen);
-            TR(30 + TR_ARRIVED);
-            sd.start(Lw.wd, F, D, D);
-            TR(30 + TR_ISSUED);
-            bar_wait<BAR_MODE>(P, gen, err);
-            TR(40 + TR_WAIT);
+            lds_barrier();
+            lds_barrier();
+            TR(40 + TR_DONE);
+            for (int q = lane; 2 * q < gr1 - gr0; q += WAVE)
+                publish(&A.mb[gr0 / 2 + q], silu_mul(s_part[2 * q], s_part[2 * q + 1]), tag);
+            TR(40 + TR_PUB);
             // ---------------- down projection + residual ----------------
             {
                 float xr[KF][8];
-                stage_vec<true, KF * 512>(s_vec, A.m, F);
-                load_x_f32<KF>(s_vec, F, xr);
-                TR(40 + TR_STAGED);
-                sd.run(xr, [&](int t, const float (&acc)[1]) {
-                    if (lane == 0) st_agent(&A.x[t], ld_agent(&A.x[t]) + acc[0]);
-                });
+                poll_vec<KF>(wt, A.mb, A.F, tag, xr);
+                TR(50 + TR_RECV);
+                regs_to_lds<KF>(s_r, A.F, xr);
             }
-            TR(40 + TR_DONE);
-            bar_arrive<BAR_MODE>(P, gen);
-            TR(40 + TR_ARRIVED);
-            if (l + 1 < A.n_layers) {
-                sq.start(P.layers[l + 1].wqkv, D, Nqkv, Nqkv / 2);
-                TR(40 + TR_ISSUED);
-                bar_wait<BAR_MODE>(P, gen, err);
-                TR(0 + TR_WAIT);
+            lds_barrier();
+            lds_barrier();
+            TR(50 + TR_DONE);
+            // This layer's cache rows are stored (acknowledged) before the
+            // residual stream that every later reader depends on is published.
+            drain_vmem();
+            for (int i = lane; i < dr1 - dr0; i += WAVE) {
+                const float xn = s_own[i] + s_part[i];
+                s_own[i] = xn;
+                publish(&A.xb1[dr0 + i], xn, tag);
             }
+            TR(50 + TR_PUB);
+            load_gain<KD>(l + 1 < NL ? layer_w(P, P.layer0.g_attn, l + 1) : A.g_final, A.D, gain);
         }
         // ---------------- final RMSNorm + LM head + argmax ----------------
         {
-            RowStream<4, KD, DL> sl;
-            sl.start(A.lm_head, D, V, (V + 3) / 4);
-            TR(40 + TR_ISSUED);
-            bar_wait<BAR_MODE>(P, gen, err);
-            TR(50 + TR_WAIT);
             float xr[KD][8];
-            stage_vec<true, KD * 512>(s_vec, A.x, D);
-            load_x_f32<KD>(s_vec, D, xr);
-            rmsnorm_regs<KD>(xr, A.g_final, D, A.eps);
-            TR(50 + TR_STAGED);
-            Best b{-INFINITY, INT_MAX};
-            sl.run(xr, [&](int t, const float (&acc)[4]) {
-                if (lane == 0) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 4 * t + r;
-                        if (row < V) {
-                            A.logits[row] = acc[r];
-                            if (!isfinite(acc[r])) atomicOr(err, ERR_NONFINITE);
-                            b = better(b, Best{acc[r], row});
-                        }
-                    }
-                }
-            });
-            TR(50 + TR_DONE);
-            b = block_best(b);
-            Best fin;
-            if (argmax_finish(b, blockIdx.x, gridDim.x, A.arg_val, A.arg_idx, A.arg_cnt, &fin) &&
-                threadIdx.x == 0) {
-                st_agent(&A.st->token[0], fin.i);
-                A.gen_out[P.out_base + step] = fin.i;
-                if (step + 1 == P.n_steps) {
-                    A.st->pos = P.pos0 + P.n_steps;
-                    A.st->n_gen = P.out_base + P.n_steps;
-                }
+            poll_vec<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), xr);
+            TR(60 + TR_RECV);
+            rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
+            regs_to_lds<KD>(s_r, A.D, xr);
+        }
+        lds_barrier();
+        lds_barrier();
+        TR(60 + TR_DONE);
+        const uint32_t ltag = tag12(tag_of(A, P, step, NL));
+        {
+            Best bst{-INFINITY, INT_MAX};
+            for (int i = lane; i < lr1 - lr0; i += WAVE) {
+                const float v = s_part[i];
+                A.logits[lr0 + i] = v;
+                if (!isfinite(v)) atomicOr(&A.st->err, ERR_NONFINITE);
+                bst = better(bst, Best{v, lr0 + i});
+            }
+            bst = wave_best(bst);
+            if (lane == 0) {
+                const uint32_t ix = bst.i == INT_MAX ? 0xFFFFFu : (uint32_t)bst.i;
+                st_agent(&A.lb[b], ((uint64_t)__float_as_uint(bst.v) << 32) | ((uint64_t)ix << 12) | ltag);
             }
         }
-        if (step + 1 < P.n_steps) {
-            bar_arrive<BAR_MODE>(P, gen);
-            sq.start(P.layers[0].wqkv, D, Nqkv, Nqkv / 2);
-            bar_wait<BAR_MODE>(P, gen, err);
-            tok = ld_agent(&A.st->token[0]);
+        // every workgroup reads all candidates: the next step's token
+        {
+            constexpr int NW = LB_MAX / WAVE;
+            const int lane = lane_id();
+            Best bst{-INFINITY, INT_MAX};
+            bool need[NW];
+#pragma unroll
+            for (int k = 0; k < NW; ++k) need[k] = k * WAVE + lane < nwg;
+            wt.n = 0;
+            while (true) {
+                uint64_t v[NW];
+#pragma unroll
+                for (int k = 0; k < NW; ++k)
+                    if (need[k]) v[k] = ld_agent(word_at(A.lb, k * WAVE + lane));
+                bool all = true;
+#pragma unroll
+                for (int k = 0; k < NW; ++k)
+                    if (need[k]) {
+                        if ((uint32_t)(v[k] & 0xFFFu) == ltag) {
+                            const uint32_t ix = (uint32_t)(v[k] >> 12) & 0xFFFFFu;
+                            bst = better(bst, Best{__uint_as_float((uint32_t)(v[k] >> 32)),
+                                                   ix == 0xFFFFFu ? INT_MAX : (int)ix});
+                            need[k] = false;
+                        } else {
+                            all = false;
+                        }
+                    }
+                if (__all(all)) break;
+                if (!wt.again()) break;
+            }
+            bst = wave_best(bst);
+            tok = check_token(bst.i);
+        }
+        TR(60 + TR_PUB);
+        if (b == 0 && lane == 0) {
+            A.gen_out[P.out_base + step] = tok;
+            if (step + 1 == P.n_steps) {
+                A.st->token[0] = tok;
+                A.st->pos = P.pos0 + P.n_steps;
+                A.st->n_gen = P.out_base + P.n_steps;
+            }
         }
     }
     TR(98);
+    lds_barrier();   // every wave's events are recorded
+    if (TR.tb && lane == 0) TR.tb[0] = (unsigned long long)min(*s_nev, TR.cap);
 }
 
-// n back-to-back grid barriers and nothing else (barrier latency probe).
-template <int MODE>
-__global__ __launch_bounds__(WG) void k_barrier_probe(PersistArgs P, int n, int* err) {
-    unsigned gen = P.gen0;
-    for (int i = 0; i < n; ++i) {
-        bar_arrive<MODE>(P, gen);
-        bar_wait<MODE>(P, gen, err);
+}  // namespace
+
+// FK: every K (d_model, n_heads*head_dim, d_ff) is exactly its chunk count x 512.
+// Both roles pass the same sequence of workgroup barriers: two per GEMV phase
+// (input staged; row sums complete).
+template <int KD, int KA, int KF, int HD, int G, int KVF, bool FK, int SMAX>
+__global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
+    constexpr int KIN = KF > KA ? (KF > KD ? KF : KD) : (KA > KD ? KA : KD);
+    __shared__ __attribute__((aligned(16))) unsigned char s_ring[NSW * RING * UNIT];
+    __shared__ __attribute__((aligned(16))) float s_r[KIN * 512];   // the phase's GEMV input
+    __shared__ float s_part[PART_MAX];                             // row sums of the phase
+    __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
+    __shared__ int s_nev;                                          // trace events recorded
+    const int wid = wave_id();
+    if (threadIdx.x == 0) s_nev = 0;
+    lds_barrier();
+    if (wid == 0)
+        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, &s_nev);
+    else
+        stream_role<KD, KA, KF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, &s_nev);
+}
+
+// ---- exchange latency probe ------------------------------------------------------------
+// mode 0: every workgroup raises its epoch flag, one wave polls all flags,
+// then the workgroup reads N plain (agent-coherent) words; mode 1: every
+// workgroup publishes its share of N tagged words and polls all N (the
+// decode kernel's scheme; rounds alternate between two buffers, because
+// back-to-back rounds of one object, unlike the decode step's phases, are not
+// separated by a read of everyone's output).  N = 2048 words, n rounds.
+__global__ __launch_bounds__(WG) void k_xchg_probe(uint64_t* words, int* flags, int n, int mode, StepArgs A,
+                                                   int spin_limit) {
+    constexpr int N = 2048;
+    const int lane = lane_id(), b = blockIdx.x, nwg = gridDim.x, per = N / nwg;
+    Waiter wt{A.abort_word, &A.st->err, spin_limit, 0};
+    float acc = 0.f;
+    for (int r = 0; r < n; ++r) {
+        const uint32_t tag = (uint32_t)r + 1u;
+        if (threadIdx.x < WAVE) {
+            if (mode == 0) {
+                for (int i = lane; i < per; i += WAVE)
+                    st_agent(reinterpret_cast<float*>(words) + b * per + i, (float)r);
+                drain_vmem();
+                if (lane == 0) st_agent(&flags[b], (int)tag);
+                wt.n = 0;
+                while (true) {
+                    bool ok = true;
+                    int f[LB_MAX / WAVE];
+#pragma unroll
+                    for (int k = 0; k < LB_MAX / WAVE; ++k)
+                        if (k * WAVE + lane < nwg) f[k] = ld_agent(&flags[k * WAVE + lane]);
+#pragma unroll
+                    for (int k = 0; k < LB_MAX / WAVE; ++k)
+                        if (k * WAVE + lane < nwg) ok &= (int)((uint32_t)f[k] - tag) >= 0;
+                    if (__all(ok) || !wt.again()) break;
+                }
+                float v[N / WAVE];
+#pragma unroll
+                for (int k = 0; k < N / WAVE; ++k) v[k] = ld_agent(reinterpret_cast<const float*>(words) + k * WAVE + lane);
+#pragma unroll
+                for (int k = 0; k < N / WAVE; ++k) acc += v[k];
+            } else {
+                uint64_t* buf = words + (r & 1) * N;
+                for (int i = lane; i < per; i += WAVE) publish(&buf[b * per + i], (float)r, tag);
+                float xr[4][8];
+                poll_vec<4>(wt, buf, N, tag, xr);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc += xr[c][0];
+            }
+        }
+        lds_barrier();
     }
+    if (acc == -1.0f) A.x[0] = acc;   // keeps the loads alive
 }
 
 // ---- host side ------------------------------------------------------------------------
@@ -454,6 +838,8 @@ namespace {
 struct Shape {
     int KD, KA, KF, HD, G;
 };
+// Most key splits per kv-head each instantiation merges (the default split
+// count is CUs / n_kv_heads, at most 64).
 // Instantiated shapes: the 2B-class model, the 1-layer tiny model, and a
 // small GQA model used by the tests.
 constexpr Shape kShapes[] = {{4, 4, 11, 128, 2}, {1, 1, 2, 64, 1}, {1, 1, 4, 64, 4}};
@@ -465,91 +851,103 @@ bool same(const Shape& a, const Shape& b) {
     return a.KD == b.KD && a.KA == b.KA && a.KF == b.KF && a.HD == b.HD && a.G == b.G;
 }
 
-template <int KD, int KA, int KF, int HD, int G>
+template <int KD, int KA, int KF, int HD, int G, bool FK, int SMAX>
 const void* kernel_for_fmt(int kvfmt) {
     switch (kvfmt) {
-        case KV_FP16: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_FP16>;
-        case KV_E5M2: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_E5M2>;
-        case KV_INT8: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_INT8>;
+        case KV_FP16: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_FP16, FK, SMAX>;
+        case KV_E5M2: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_E5M2, FK, SMAX>;
+        case KV_INT8: return (const void*)&k_persist<KD, KA, KF, HD, G, KV_INT8, FK, SMAX>;
     }
     return nullptr;
 }
 
-const void* kernel_for(const StepArgs& A) {
+const void* kernel_for(const StepArgs& A, int* smax) {
     const Shape s = shape_of(A);
-    if (same(s, kShapes[0])) return kernel_for_fmt<4, 4, 11, 128, 2>(A.kvfmt);
-    if (same(s, kShapes[1])) return kernel_for_fmt<1, 1, 2, 64, 1>(A.kvfmt);
-    if (same(s, kShapes[2])) return kernel_for_fmt<1, 1, 4, 64, 4>(A.kvfmt);
+    const bool full = A.D == s.KD * 512 && A.H * A.hd == s.KA * 512 && A.F == s.KF * 512;
+    if (same(s, kShapes[0]) && full) { *smax = 32; return kernel_for_fmt<4, 4, 11, 128, 2, true, 32>(A.kvfmt); }
+    if (same(s, kShapes[1])) { *smax = 64; return kernel_for_fmt<1, 1, 2, 64, 1, false, 64>(A.kvfmt); }
+    if (same(s, kShapes[2])) { *smax = 64; return kernel_for_fmt<1, 1, 4, 64, 4, false, 64>(A.kvfmt); }
     return nullptr;
 }
+
+// Most rows one workgroup reduces in a phase when the rows are dealt to nwg
+// workgroups in tasks of rpt.
+int rows_per_wg(int N, int rpt, int nwg) { return ((N / rpt + nwg - 1) / nwg) * rpt; }
 }  // namespace
 
-bool persistent_supported(const StepArgs& A) { return kernel_for(A) != nullptr; }
+bool persistent_supported(const StepArgs& A) {
+    int smax = 0;
+    return kernel_for(A, &smax) != nullptr && A.S <= smax;
+}
 
 hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg) {
-    const void* k = kernel_for(A);
-    if (!k) return hipErrorInvalidValue;
+    int smax = 0;
+    const void* k = kernel_for(A, &smax);
+    if (!k || A.S > smax) return hipErrorInvalidValue;
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess) return e;
     int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, WG, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, PWG, 0);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorInvalidConfiguration;
-    *nwg = prop.multiProcessorCount;   // one workgroup per CU
+    const int n = prop.multiProcessorCount;   // one workgroup per CU
+    const int most = std::max(std::max(rows_per_wg((A.H + 2 * A.Hk) * A.hd, 2, n), rows_per_wg(2 * A.F, 2, n)),
+                              std::max(rows_per_wg(A.D, 1, n), rows_per_wg(A.V, 1, n)));
+    // every attention task and merge task needs a workgroup of its own
+    const int ntask = A.Hk * A.S, nmerge = A.H * (A.hd / 64);
+    if (most > PART_MAX || rows_per_wg(A.D, 1, n) > OWN_MAX || n > LB_MAX || ntask > n || nmerge > n ||
+        A.V >= (1 << 20))
+        return hipErrorInvalidConfiguration;
+    *nwg = n;
     return hipSuccess;
 }
 
 hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, hipStream_t s) {
-    const void* k = kernel_for(A);
-    if (!k) return hipErrorInvalidValue;
+    int smax = 0;
+    const void* k = kernel_for(A, &smax);
+    if (!k || A.S > smax) return hipErrorInvalidValue;
+    if (P.n_steps < 1) return hipErrorInvalidValue;
     StepArgs a = A;
     PersistArgs p = P;
     void* args[] = {&a, &p};
-    return hipLaunchCooperativeKernel(k, dim3(nwg), dim3(WG), args, 0, s);
+    return hipLaunchCooperativeKernel(k, dim3(nwg), dim3(PWG), args, 0, s);
 }
 
 hipError_t barrier_probe(int nwg, int n, int mode, float* us, int* errbits) {
-    int* bar = nullptr;
-    int* err = nullptr;
-    hipEvent_t e0, e1;
+    if (nwg < 1 || nwg > LB_MAX || 2048 % nwg != 0 || (mode != 0 && mode != 1)) return hipErrorInvalidValue;
+    uint8_t* buf = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
     hipError_t e;
-    const void* kern = nullptr;
-    switch (mode) {
-        case 0: kern = (const void*)&k_barrier_probe<0>; break;
-        case 1: kern = (const void*)&k_barrier_probe<1>; break;
-        case 2: kern = (const void*)&k_barrier_probe<2>; break;
-        case 3: kern = (const void*)&k_barrier_probe<3>; break;
-        case 4: kern = (const void*)&k_barrier_probe<4>; break;
-        case 5: kern = (const void*)&k_barrier_probe<5>; break;
-        case 6: kern = (const void*)&k_barrier_probe<6>; break;
-        default: return hipErrorInvalidValue;
-    }
-    if (nwg < 1 || nwg > BAR_MAX_WG) return hipErrorInvalidValue;
-    if ((e = hipMalloc(&bar, BAR_WORDS * sizeof(int) + 256)) != hipSuccess) return e;
-    err = bar + BAR_WORDS;
-    if ((e = hipMemset(bar, 0, BAR_WORDS * sizeof(int) + 256)) != hipSuccess) goto out;
+    const size_t bytes = 2 * 2048 * 8 + LB_MAX * 4 + sizeof(StepState) + 256;
+    if ((e = hipMalloc(&buf, bytes)) != hipSuccess) return e;
+    if ((e = hipMemset(buf, 0, bytes)) != hipSuccess) goto out;
     (void)hipEventCreate(&e0);
     (void)hipEventCreate(&e1);
     {
-        PersistArgs P{};
-        P.bar = bar;
-        P.spin_limit = 1 << 24;
-        int nn = n;
-        void* args[] = {&P, &nn, &err};
+        uint64_t* words = reinterpret_cast<uint64_t*>(buf);
+        int* flags = reinterpret_cast<int*>(buf + 2 * 2048 * 8);
+        StepArgs A{};
+        A.st = reinterpret_cast<StepState*>(buf + 2 * 2048 * 8 + LB_MAX * 4);
+        A.abort_word = &A.st->pad;
+        A.x = reinterpret_cast<float*>(buf + bytes - 256);
+        int nn = n, md = mode, spin = 1 << 22;
+        void* args[] = {&words, &flags, &nn, &md, &A, &spin};
         (void)hipEventRecord(e0, nullptr);
-        e = hipLaunchCooperativeKernel(kern, dim3(nwg), dim3(WG), args, 0, nullptr);
+        e = hipLaunchCooperativeKernel((const void*)&k_xchg_probe, dim3(nwg), dim3(WG), args, 0, nullptr);
         (void)hipEventRecord(e1, nullptr);
         if (e == hipSuccess) e = hipEventSynchronize(e1);
         float ms = 0.f;
         (void)hipEventElapsedTime(&ms, e0, e1);
         *us = ms * 1000.0f / (float)n;
-        (void)hipMemcpy(errbits, err, sizeof(int), hipMemcpyDeviceToHost);
+        StepState st{};
+        (void)hipMemcpy(&st, A.st, sizeof st, hipMemcpyDeviceToHost);
+        *errbits = st.err;
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
 out:
-    (void)hipFree(bar);
+    (void)hipFree(buf);
     return e;
 }
 
