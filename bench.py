@@ -72,6 +72,50 @@ def cpu_baseline(blob, shape, seconds: float):
                       f"(KV at L<=768 adds <3%)"}
 
 
+GEMV_SHAPES = [(16384, 4096), (6144, 2048), (4096, 2048), (11264, 2048), (2048, 5632)]
+COLD_BYTES = 768 << 20   # > 2x the 256 MB last-level (MALL) cache
+
+
+def gemv_microbench(rd, torch, stream, iters: int = 3):
+    """The weight-streaming GEMV alone: y = W x (fp16 in, fp32 out) at batch
+    1 and 8 on the listed shapes.  Cold cache: launches rotate over distinct
+    copies of W totalling >= 768 MiB, so every launch streams W from HBM.
+    Each launch is bracketed by its own pair of events on the launch stream;
+    reported: mean duration and algorithmic GB/s (W + x + y bytes)."""
+    import synth
+    out = []
+    for N, K in GEMV_SHAPES:
+        W, X = synth.gemv_inputs(N, K, 8, seed_w=2, seed_x=3)
+        wbytes = N * K * 2
+        ncopy = max(2, -(-COLD_BYTES // wbytes))
+        Wd = torch.from_numpy(W).to("cuda")
+        copies = [Wd] + [Wd.clone() for _ in range(ncopy - 1)]
+        Xd = torch.from_numpy(X).to("cuda")
+        y = torch.empty((8, N), dtype=torch.float32, device="cuda")
+        row = {"N": N, "K": K, "weight_bytes": wbytes, "copies": ncopy}
+        for batch in (1, 8):
+            for c in copies:    # warm the code path, touch every copy once
+                rd.rd_gemv_f16(c.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch, stream.cuda_stream)
+            torch.cuda.synchronize()
+            n = ncopy * iters
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for i in range(n):
+                evs[i][0].record(stream)
+                rd.rd_gemv_f16(copies[i % ncopy].data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch,
+                               stream.cuda_stream)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / n
+            nbytes = wbytes + batch * K * 2 + batch * N * 4
+            gbps = nbytes / (us * 1e-6) / 1e9
+            row[f"b{batch}"] = {"us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            print(f"[bench] gemv [{N},{K}] batch {batch}: {us:.2f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        del copies, Wd
+        torch.cuda.empty_cache()
+        out.append(row)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +126,7 @@ def main():
     ap.add_argument("--phase-iters", type=int, default=96)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV microbench")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
@@ -159,6 +204,7 @@ def main():
     k_gbps = k_bytes / (k_us * 1e-6) / 1e9
     print(f"[bench] gate/up phase kernel: {k_us:.2f} us/launch, {k_gbps:.0f} GB/s", file=sys.stderr, flush=True)
     m.close()
+    gemv = None if args.no_gemv else gemv_microbench(rd, torch, stream)
 
     if persistent:
         roof = {"bound": "hbm", "kernel": "k_persist (whole decode steps, one launch for all timed steps)",
@@ -171,7 +217,7 @@ def main():
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                 "bytes_per_launch": k_bytes, "us_per_launch": round(k_us, 3)}
     res = {
-        "metric": "batch-1 decode tokens/s (2B-class fp16 model, 512-token prompt + 256 greedy steps)",
+        "metric": "batch-1 decode tokens/s + achieved HBM GB/s (MBU %) on 2B-class fp16 model",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16",
@@ -185,6 +231,8 @@ def main():
         "roofline": roof,
         "gateup_phase_kernel": {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)},
     }
+    if gemv is not None:
+        res["gemv_microbench"] = gemv
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(blob, shape, args.cpu_seconds)
     print(json.dumps(res), flush=True)

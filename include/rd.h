@@ -215,11 +215,17 @@ const char* rd_last_error(void);
  * stream (NULL = the null stream), asynchronously.  Argument errors return
  * INVALID_ARG before anything is enqueued. */
 
-/* y[b][n] = sum_k W[n][k] * x[b][k], fp16 inputs, fp32 accumulate and output.
- * W: device fp16 row-major [N][K]; x: device fp16 [batch][K]; y: device f32
- * [batch][N].  K a multiple of 8 and <= 16384, batch 1.  Weight-streaming GEMV
- * ("Real-time LLM inference on standard GPUs", section on memory bandwidth:
- * about 1 FLOP per weight byte at fp16). */
+/* y[b][n] = sum_k W[n][k] * x[b][k], fp16 inputs, fp32 accumulate and output:
+ * the decode step's weight-streaming matrix-vector product measured alone
+ * ("Real-time LLM inference on standard GPUs: 3,000 tokens/s per request",
+ * section on memory bandwidth: about 1 FLOP per weight byte at fp16 and
+ * batch 1, 8 at batch 8).  W: device fp16 row-major [N][K]; x: device fp16
+ * [batch][K]; y: device f32 [batch][N].  batch 1: K a multiple of 8,
+ * 8 <= K <= 8192, a streaming kernel with the step's own per-row dot
+ * product (same bits as the step's GEMVs).  batch 8: K a multiple of 64,
+ * 64 <= K <= 8192, a thin GEMM on the matrix cores (16x16x32 fp16 MFMA
+ * tiles, rows 8..15 of the tile unused).  W and x 16-byte aligned.  Nothing
+ * is allocated; the launch is asynchronous on `stream`. */
 rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t K, int32_t batch, void* stream);
 
 /* Single-query attention of n_heads query heads over one sequence's cache

@@ -798,10 +798,16 @@ hipError_t get_scratch(Scratch** out) {
 extern "C" rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t K, int32_t batch,
                                  void* stream) {
     if (!W || !x || !y) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
-    if (N < 1 || K < 8 || K % 8 || K > 8192) return fail(RD_ERR_INVALID_ARG, "need N >= 1, 8 <= K <= 8192, K % 8 == 0");
-    if (batch != 1) return fail(RD_ERR_UNSUPPORTED, "batch must be 1");
+    if (batch != 1 && batch != 8) return fail(RD_ERR_UNSUPPORTED, "batch must be 1 or 8");
+    if (batch == 1 && (N < 1 || K < 8 || K % 8 || K > 8192))
+        return fail(RD_ERR_INVALID_ARG, "batch 1 needs N >= 1, 8 <= K <= 8192, K % 8 == 0");
+    if (batch == 8 && (N < 1 || K < 64 || K % 64 || K > 8192))
+        return fail(RD_ERR_INVALID_ARG, "batch 8 needs N >= 1, 64 <= K <= 8192, K % 64 == 0");
     if (((uintptr_t)W | (uintptr_t)x) & 15) return fail(RD_ERR_INVALID_ARG, "W and x must be 16-byte aligned");
-    K_TRY(launch_gemv_f16(W, x, y, N, K, (hipStream_t)stream));
+    int dev = 0, ncu = 0;
+    K_TRY(hipGetDevice(&dev));
+    K_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    K_TRY(launch_gemv_f16(W, x, y, N, K, batch, ncu, (hipStream_t)stream));
     return RD_OK;
 }
 

@@ -143,7 +143,7 @@ hipError_t barrier_probe(int nwg, int n, int mode, float* us, int* errbits);
 int kch_for(int K);
 hipError_t launch_step(const StepArgs& A, hipStream_t s);
 hipError_t launch_phase(const StepArgs& A, int phase, int layer, hipStream_t s);
-hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, hipStream_t s);
+hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, int batch, int ncu, hipStream_t s);
 hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s);
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,

@@ -228,25 +228,7 @@ __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
     }
 }
 
-// ---- standalone kernels (microbench / unit parity) --------------------------------
-template <int KCH, int R>
-__global__ __launch_bounds__(WG) void k_gemv_f16(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
-                                                 float* __restrict__ y, int N, int K) {
-    const int lane = lane_id(), wid = wave_id();
-    const int row0 = (blockIdx.x * 4 + wid) * R;
-    u4v w[R][KCH];
-    load_rows<R, KCH>(W, K, row0, max(0, min(R, N - row0)), w);
-    float xr[KCH][8];
-    load_x_f16<KCH>(x, K, xr);
-    if (row0 >= N) return;
-    float acc[R];
-    dot_rows<R, KCH>(w, xr, acc);
-    if (lane == 0)
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            if (row0 + r < N) y[row0 + r] = acc[r];
-}
-
+// ---- standalone kernels (unit parity) --------------------------------------------
 __global__ __launch_bounds__(WG) void k_e5m2(const uint16_t* __restrict__ in, uint8_t* __restrict__ out, size_t n) {
     for (size_t i = (size_t)blockIdx.x * WG + threadIdx.x; i < n; i += (size_t)gridDim.x * WG) out[i] = e5m2_encode(in[i]);
 }
@@ -390,21 +372,6 @@ hipError_t launch_step(const StepArgs& A, hipStream_t s) {
         }
     dim3 grid(lm_head_workgroups(A.V)), block(WG);
     RD_KCH_SWITCH(kch_for(A.D), hipLaunchKernelGGL((k_lmhead<KC>), grid, block, 0, s, A))
-    return hipGetLastError();
-}
-
-hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, hipStream_t s) {
-    const int kch = kch_for(K);
-    if (kch <= 0) return hipErrorInvalidValue;
-    if (kch >= 8) {
-        dim3 grid((N + 7) / 8), block(WG);
-        RD_KCH_SWITCH(kch, hipLaunchKernelGGL((k_gemv_f16<KC, 2>), grid, block, 0, s,
-                                              (const _Float16*)W, (const _Float16*)x, y, N, K))
-    } else {
-        dim3 grid((N + 15) / 16), block(WG);
-        RD_KCH_SWITCH(kch, hipLaunchKernelGGL((k_gemv_f16<KC, 4>), grid, block, 0, s,
-                                              (const _Float16*)W, (const _Float16*)x, y, N, K))
-    }
     return hipGetLastError();
 }
 

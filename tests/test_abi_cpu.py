@@ -100,6 +100,17 @@ def test_null_arguments(rd):
     L.rd_model_destroy(None)   # NULL-safe
 
 
+def test_gemv_argument_checks(rd):
+    # Rejected before anything touches a device: fake aligned pointers.
+    L, p = rd.lib(), C.c_void_p(256)
+    assert L.rd_gemv_f16(p, p, p, 16, 64, 3, None) == rd.RD_ERR_UNSUPPORTED
+    assert L.rd_gemv_f16(p, p, p, 16, 72, 8, None) == rd.RD_ERR_INVALID_ARG      # K % 64
+    assert L.rd_gemv_f16(p, p, p, 16, 8256, 8, None) == rd.RD_ERR_INVALID_ARG    # K > 8192
+    assert L.rd_gemv_f16(p, p, p, 0, 64, 8, None) == rd.RD_ERR_INVALID_ARG
+    assert L.rd_gemv_f16(p, p, p, 16, 12, 1, None) == rd.RD_ERR_INVALID_ARG      # K % 8
+    assert L.rd_gemv_f16(p, C.c_void_p(258), p, 16, 64, 1, None) == rd.RD_ERR_INVALID_ARG  # alignment
+
+
 def test_blob_layout_matches_shapes():
     s = synth.SHAPES["2b"]
     lay, total = synth.blob_layout(s)

@@ -31,23 +31,40 @@ def sync():
     torch.cuda.synchronize()
 
 
+def _gemv_check(rd, orc, N, K, batch):
+    import torch
+    print(f"gemv N={N} K={K} batch={batch}", flush=True)
+    W, X = synth.gemv_inputs(N, K, batch, seed_w=N + K, seed_x=K + batch)
+    y = torch.full((batch, N), float("nan"), dtype=torch.float32, device="cuda")
+    Wd, Xd = dev(W), dev(X)
+    rd.rd_gemv_f16(Wd.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch)
+    sync()
+    got = y.cpu().numpy().astype(np.float64)
+    for b in range(batch):
+        ref = orc.gemv(W, X[b].astype(np.float64))
+        # fp16 x fp16 products are exact in fp32; only the fp32 summation
+        # rounds: |err| <= K * 2^-24 * sum|w x| (first-order worst case)
+        mag = np.abs(W.astype(np.float64)) @ np.abs(X[b].astype(np.float64))
+        bound = (K + 2) * 2.0 ** -24 * mag + 1e-30
+        err = np.abs(got[b] - ref)
+        assert np.all(err <= bound), (b, np.nanmax(err / bound))
+
+
+# The microbench shapes (fused QKV as listed and as the GQA model has it,
+# gate+up, down, the large square-ish one) plus ragged row counts and K
+# values that leave a partial 512-column chunk.
 @pytest.mark.parametrize("N,K", [(1, 8), (7, 264), (1000, 2056), (4096, 2048), (6144, 2048), (11264, 2048),
                                  (2048, 5632), (16384, 4096), (333, 8192)])
 def test_gemv_vs_oracle(rd, orc, N, K):
-    import torch
-    print(f"gemv N={N} K={K}", flush=True)
-    W, X = synth.gemv_inputs(N, K, 1, seed_w=N + K, seed_x=K)
-    y = torch.empty(N, dtype=torch.float32, device="cuda")
-    Wd, Xd = dev(W), dev(X[0])
-    rd.rd_gemv_f16(Wd.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K)
-    sync()
-    got = y.cpu().numpy().astype(np.float64)
-    ref = orc.gemv(W, X[0].astype(np.float64))
-    # fp16 x fp16 products are exact in fp32; only the fp32 summation rounds:
-    # |err| <= K * 2^-24 * sum|w x| (first-order worst case)
-    mag = np.abs(W.astype(np.float64)) @ np.abs(X[0].astype(np.float64))
-    bound = (K + 2) * 2.0 ** -24 * mag + 1e-30
-    assert np.all(np.abs(got - ref) <= bound), np.max(np.abs(got - ref) / bound)
+    _gemv_check(rd, orc, N, K, 1)
+
+
+# Batch 8 (MFMA thin GEMM): every work split (16-row blocks, K in 1, 2 or 4
+# parts), row counts that are not a multiple of 16, a single block, K = 64.
+@pytest.mark.parametrize("N,K", [(1, 64), (17, 128), (1000, 2048), (4096, 2048), (6144, 2048), (11264, 2048),
+                                 (2048, 5632), (16384, 4096), (333, 8192), (20000, 1024)])
+def test_gemv_batch8_vs_oracle(rd, orc, N, K):
+    _gemv_check(rd, orc, N, K, 8)
 
 
 def _attn_case(H, Hk, hd, L, ld, seed):
