@@ -14,116 +14,158 @@ namespace rd {
 
 namespace {
 
-constexpr int GW = 256;   // threads per workgroup (4 waves)
+constexpr int GW = 256;   // threads per batch-1 workgroup (4 waves)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 // ---- batch 1 ---------------------------------------------------------------------
-// One workgroup per CU walks a contiguous block of rows; each wave takes NR
-// rows at a time (rows r0 + NR*wid + NR*nw*j), and the next group's loads
-// (NR * KCH KiB per wave) are in flight while the current group is reduced.
-// The x vector is in registers in the chunk layout of dot_rows.
-template <int KCH, int NR>
+// dot_rows with x kept as fp16 in registers (8 halves per chunk): every
+// product and every addition is the one dot_rows makes with x widened to
+// fp32 first, in the same order, so the results are the same bits.
+template <int NR, int KCH>
+__device__ __forceinline__ void dot_rows_xh(const u4v (&w)[NR][KCH], const u4v (&xh)[KCH], float (&out)[NR]) {
+    float s0[NR], s1[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s0[r] = s1[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const h8 xv = as_h8(xh[c]);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const h8 hw = as_h8(w[r][c]);
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                s0[r] += (float)hw[i] * (float)xv[i];
+                s1[r] += (float)hw[i + 1] * (float)xv[i + 1];
+            }
+        }
+    }
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = row16_sum(s0[r] + s1[r]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        out[r] = ((readlane_f(v[r], 0) + readlane_f(v[r], 16)) + readlane_f(v[r], 32)) + readlane_f(v[r], 48);
+}
+
+// Each workgroup owns a contiguous block of rows; its waves take NR rows at
+// a time, round robin, and keep NB groups of loads in registers: while one
+// group is reduced the next NB - 1 are in flight.  Launched with several
+// workgroups per CU so that about 128 KiB per CU are in flight, which the
+// HBM needs to stream at full rate.
+template <int KCH, int NR, int NB>
 __global__ __launch_bounds__(GW) void k_gemv_b1(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
                                                  float* __restrict__ y, int N, int K) {
     const int wid = wave_id(), nw = GW / WAVE, lane = lane_id();
     const int per = (N + gridDim.x - 1) / gridDim.x;
     const int r0 = min(N, (int)blockIdx.x * per), r1 = min(N, r0 + per);
-    int r = r0 + wid * NR;
-    u4v wa[NR][KCH], wb[NR][KCH];
-    load_rows<NR, KCH>(W, K, r, max(0, min(NR, r1 - r)), wa);
-    float xr[KCH][8];
-    load_x_f16<KCH>(x, K, xr);
-    auto finish = [&](const u4v (&w)[NR][KCH], int row) {
-        float acc[NR];
-        dot_rows<NR, KCH>(w, xr, acc);
-        if (lane == 0)
+    u4v w[NB][NR][KCH];
 #pragma unroll
-            for (int i = 0; i < NR; ++i)
-                if (row + i < r1) y[row + i] = acc[i];
-    };
-    while (r < r1) {
-        const int rn = r + NR * nw;
-        load_rows<NR, KCH>(W, K, rn, max(0, min(NR, r1 - rn)), wb);
-        finish(wa, r);
-        r = rn;
-        if (r >= r1) break;
-        const int rn2 = r + NR * nw;
-        load_rows<NR, KCH>(W, K, rn2, max(0, min(NR, r1 - rn2)), wa);
-        finish(wb, r);
-        r = rn2;
+    for (int b = 0; b < NB; ++b) {
+        const int r = r0 + (b * nw + wid) * NR;
+        load_rows<NR, KCH>(W, K, r, max(0, min(NR, r1 - r)), w[b]);
+    }
+    u4v xh[KCH];
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const int col = (c * 64 + lane) * 8;
+        xh[c] = col < K ? ld16(x + col) : u4v{0u, 0u, 0u, 0u};
+    }
+    for (int j = 0;; j += NB) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int r = r0 + ((j + b) * nw + wid) * NR;
+            if (r >= r1) return;
+            float acc[NR];
+            dot_rows_xh<NR, KCH>(w[b], xh, acc);
+            if (lane == 0)
+#pragma unroll
+                for (int i = 0; i < NR; ++i)
+                    if (r + i < r1) y[r + i] = acc[i];
+            const int rn = r0 + ((j + b + NB) * nw + wid) * NR;
+            load_rows<NR, KCH>(W, K, rn, max(0, min(NR, r1 - rn)), w[b]);
+        }
     }
 }
 
 // ---- batch 8 (MFMA) ------------------------------------------------------------------
 // v_mfma_f32_16x16x32_f16 with M = batch (rows 8..15 zero), N = 16 weight
-// rows, K = 32.  Lane l (n = l % 16, q = l / 16) loads 32 contiguous bytes
-// of weight row n at columns k0 + 16q .. +15 (four lanes cover a 128-byte
-// line of the row), which feed two MFMAs: its first 8 halves in the first,
-// the last 8 in the second.  A dot product may take its terms in any order
-// as long as both operands use the same order, so the batch operand is
-// loaded with the same permutation of k: lane (m, q) holds x[m][k0 + 16q ..
-// +15].  Output layout of the 16x16 accumulator: lane l holds rows
-// m = 4*(l/16) + j, column n = l % 16.
+// rows, K = 32: lane l of the weight operand holds 8 k-values of row l % 16,
+// lane l of the batch operand 8 k-values of batch row l % 16, and the result
+// lane l holds rows m = 4*(l/16) + j of column n = l % 16.  A dot product
+// may take its terms in any order if both operands use the same order, so
+// which k-values a lane holds is free as long as x and W agree.
 //
-// Work unit = (block of 16 weight rows, one of KS parts of K).  Each
-// workgroup is resident for the whole launch (grid <= CU count), stages x
-// ([8][K] fp16) in LDS once, and walks groups of 4 units (4/KS blocks, all
-// KS parts of each, one unit per wave); with KS > 1 the parts are summed
+// HBM streams best when each load instruction reads whole 128-byte lines,
+// but the operand layout wants 16 rows per instruction.  So W goes through
+// a per-wave LDS ring: LDS-DMA loads (lane l: row l/8, then row 8 + l/8,
+// 16-byte chunk l%8 of the row's 128-byte line of the 64-column step) land
+// each row line contiguously in LDS, with chunk c stored at position
+// c ^ (row % 8) so that the operand reads (row l % 16, chunk 4j + l/16 for
+// MFMA j) hit distinct banks.  The batch operand for a wave's K range is
+// loaded into registers once (chunk 4j + l/16 of each step).
+//
+// Work unit = (16-row block, one of KS parts of K).  Workgroups walk groups
+// of units, one unit per wave; with KS > 1 the parts of a block are summed
 // through LDS in part order, so the result does not depend on timing.
 typedef _Float16 hv8 __attribute__((ext_vector_type(8)));
 typedef float fv4 __attribute__((ext_vector_type(4)));
-constexpr int B8_KMAX = 8192;   // x [8][K+8] fp16 in LDS: 128 KiB + 128 B
-constexpr int B8_U = 8;         // 64-column steps in flight per wave (16 KiB)
+constexpr int B8_SMAX = 16;   // 64-column steps per unit (x operand registers)
 
-template <int KS>
-__global__ __launch_bounds__(GW) void k_gemv_b8(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
-                                                float* __restrict__ y, int N, int K) {
-    // x rows at a stride of K + 8 halves: the 8 rows a ds_read_b128 touches
-    // at one column fall on different banks.  Then [4][64] fv4 partials.
-    extern __shared__ __attribute__((aligned(16))) _Float16 s_x[];
-    const int xs = K + 8;
-    fv4* s_red = reinterpret_cast<fv4*>(s_x + 8 * xs);
+template <int KS, int T, int U>
+__global__ __launch_bounds__(T) void k_gemv_b8(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
+                                               float* __restrict__ y, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) char s_lds[];   // [T/64][U][2 KiB] ring, [T/64][64] fv4
+    constexpr int NWV = T / WAVE, BPG = NWV / KS;
     const int wid = wave_id(), lane = lane_id();
-    for (int i = threadIdx.x * 8; i < 8 * K; i += GW * 8)
-        *reinterpret_cast<u4v*>(s_x + (i / K) * xs + i % K) = ld16(x + i);
-    __syncthreads();
-    constexpr int BPG = 4 / KS;   // blocks per group of 4 units
+    char* ring = s_lds + wid * U * 2048;
+    fv4* s_red = reinterpret_cast<fv4*>(s_lds + NWV * U * 2048);
     const int nblk = (N + 15) / 16, ngrp = (nblk + BPG - 1) / BPG;
     const int n = lane % 16, q = lane / 16;
     const int nsteps = K / 64, part = wid % KS;
-    const int s_beg = part * nsteps / KS, s_end = (part + 1) * nsteps / KS;
+    const int s_beg = part * nsteps / KS, ns = (part + 1) * nsteps / KS - s_beg;   // ns <= B8_SMAX
+    u4v xa[B8_SMAX][2];
+#pragma unroll
+    for (int t = 0; t < B8_SMAX; ++t) {
+        const bool ok = t < ns && n < 8;
+        const _Float16* xp = x + (size_t)(n & 7) * K + (s_beg + t) * 64 + 8 * q;
+        xa[t][0] = ok ? ld16(xp) : u4v{0u, 0u, 0u, 0u};
+        xa[t][1] = ok ? ld16(xp + 32) : u4v{0u, 0u, 0u, 0u};
+    }
+    const int lr = lane / 8, lc = (lane % 8) ^ lr;
+    const int rd0 = (n / 8) * 1024 + (n % 8) * 128 + (q ^ (n % 8)) * 16;
+    const int rd1 = (n / 8) * 1024 + (n % 8) * 128 + ((4 + q) ^ (n % 8)) * 16;
     for (int g = blockIdx.x; g < ngrp; g += gridDim.x) {
         const int blk = g * BPG + wid / KS;
         fv4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (blk < nblk) {
-            const int row = min(blk * 16 + n, N - 1);   // rows past N read row N-1; never stored
-            const _Float16* wp = W + (size_t)row * K + 16 * q;
-            const _Float16* xp = s_x + (n & 7) * xs + 16 * q;
-            u4v wv[B8_U][2];
+        if (blk < nblk && ns > 0) {
+            // rows past N read row N - 1 (never stored)
+            const char* g0 = (const char*)(W + (size_t)min(blk * 16 + lr, N - 1) * K + s_beg * 64) + lc * 16;
+            const char* g1 = (const char*)(W + (size_t)min(blk * 16 + 8 + lr, N - 1) * K + s_beg * 64) + lc * 16;
+            auto issue = [&](int t, int slot) {   // t in [0, ns)
+                __builtin_amdgcn_global_load_lds((glb_void*)(g0 + t * 128), (lds_void*)(ring + slot * 2048), 16, 0, 2);
+                __builtin_amdgcn_global_load_lds((glb_void*)(g1 + t * 128), (lds_void*)(ring + slot * 2048 + 1024), 16,
+                                                 0, 2);
+            };
 #pragma unroll
-            for (int u = 0; u < B8_U; ++u)
-                if (s_beg + u < s_end) {
-                    wv[u][0] = ld_w16(wp + (s_beg + u) * 64);
-                    wv[u][1] = ld_w16(wp + (s_beg + u) * 64 + 8);
-                }
-            for (int s0 = s_beg; s0 < s_end; s0 += B8_U) {
+            for (int u = 0; u < U; ++u) issue(min(u, ns - 1), u);
 #pragma unroll
-                for (int u = 0; u < B8_U; ++u) {
-                    const int s = s0 + u;
-                    if (s >= s_end) break;
-                    const u4v w0 = wv[u][0], w1 = wv[u][1];
-                    if (s + B8_U < s_end) {
-                        wv[u][0] = ld_w16(wp + (s + B8_U) * 64);
-                        wv[u][1] = ld_w16(wp + (s + B8_U) * 64 + 8);
-                    }
-                    u4v a0 = *reinterpret_cast<const u4v*>(xp + s * 64);
-                    u4v a1 = *reinterpret_cast<const u4v*>(xp + s * 64 + 8);
-                    if (n >= 8) a0 = a1 = u4v{0u, 0u, 0u, 0u};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(hv8, a0),
+            for (int t = 0; t < B8_SMAX; ++t) {
+                if (t < ns) {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * (U - 1)) : "memory");
+                    const int slot = t % U;
+                    const u4v w0 = *reinterpret_cast<const u4v*>(ring + slot * 2048 + rd0);
+                    const u4v w1 = *reinterpret_cast<const u4v*>(ring + slot * 2048 + rd1);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    issue(min(t + U, ns - 1), slot);   // past the end: a harmless re-read of the last step
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(hv8, xa[t][0]),
                                                                  __builtin_bit_cast(hv8, w0), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(hv8, a1),
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(hv8, xa[t][1]),
                                                                  __builtin_bit_cast(hv8, w1), acc, 0, 0, 0);
                 }
             }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         if constexpr (KS > 1) {
             s_red[wid * 64 + lane] = acc;
@@ -145,37 +187,43 @@ __global__ __launch_bounds__(GW) void k_gemv_b8(const _Float16* __restrict__ W, 
     }
 }
 
+template <int KS, int T, int U>
+hipError_t launch_b8(const _Float16* W, const _Float16* x, float* y, int N, int K, int gmul, int ncu, hipStream_t s) {
+    const size_t lds = (size_t)(T / WAVE) * U * 2048 + (T / WAVE) * 1024;
+    static bool attr_set = false;   // the attribute is per function, the same value every time
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)&k_gemv_b8<KS, T, U>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int nblk = (N + 15) / 16, ngrp = (nblk * KS + T / WAVE - 1) / (T / WAVE);
+    hipLaunchKernelGGL((k_gemv_b8<KS, T, U>), dim3(std::min(ngrp, gmul * ncu)), dim3(T), lds, s, W, x, y, N, K);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, int batch, int ncu, hipStream_t s) {
+    const auto* Wh = (const _Float16*)W;
+    const auto* xh = (const _Float16*)x;
     if (batch == 8) {
-        if (K % 64 || K > B8_KMAX) return hipErrorInvalidValue;
-        const int nblk = (N + 15) / 16;
-        const int ks = nblk >= 4 * ncu ? 1 : nblk >= 2 * ncu ? 2 : 4;
-        const int ngrp = (nblk * ks + 3) / 4;
-        const int grid = std::min(ngrp, ncu);
-        const size_t lds = (size_t)8 * (K + 8) * 2 + 4 * 64 * 16;
-        const void* fn = ks == 1 ? (const void*)&k_gemv_b8<1> : ks == 2 ? (const void*)&k_gemv_b8<2>
-                                                                        : (const void*)&k_gemv_b8<4>;
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        const auto* Wh = (const _Float16*)W;
-        const auto* xh = (const _Float16*)x;
-        if (ks == 1) hipLaunchKernelGGL(k_gemv_b8<1>, dim3(grid), dim3(GW), lds, s, Wh, xh, y, N, K);
-        else if (ks == 2) hipLaunchKernelGGL(k_gemv_b8<2>, dim3(grid), dim3(GW), lds, s, Wh, xh, y, N, K);
-        else hipLaunchKernelGGL(k_gemv_b8<4>, dim3(grid), dim3(GW), lds, s, Wh, xh, y, N, K);
-        return hipGetLastError();
+        // K <= 4096: 4 parts of <= 16 steps, 4-wave workgroups, 4 per CU;
+        // K <= 8192: 8 parts, 8-wave workgroups, one per CU.
+        if (K % 64 || K > 8192) return hipErrorInvalidValue;
+        if (K <= 4096) return launch_b8<4, 256, 4>(Wh, xh, y, N, K, 4, ncu, s);
+        return launch_b8<8, 512, 6>(Wh, xh, y, N, K, 1, ncu, s);
     }
     if (batch != 1) return hipErrorInvalidValue;
     const int kch = kch_for(K);
-    const int grid = std::min(ncu, (N + 7) / 8);
-#define RD_B1(KC)                                                                                    \
-    case KC:                                                                                         \
-        hipLaunchKernelGGL((k_gemv_b1<KC, (KC >= 11 ? 1 : 2)>), dim3(grid), dim3(GW), 0, s, (const _Float16*)W, \
-                           (const _Float16*)x, y, N, K);                                             \
+    // one row per wave; two groups in flight and 4 workgroups per CU up to
+    // K = 4096, three groups and 2 per CU above
+#define RD_B1(KC, NB, G)                                                                                     \
+    case KC:                                                                                                 \
+        hipLaunchKernelGGL((k_gemv_b1<KC, 1, NB>), dim3(G * ncu), dim3(GW), 0, s, Wh, xh, y, N, K);          \
         break;
     switch (kch) {
-        RD_B1(1) RD_B1(2) RD_B1(4) RD_B1(8) RD_B1(11) RD_B1(16)
+        RD_B1(1, 2, 4) RD_B1(2, 2, 4) RD_B1(4, 2, 4) RD_B1(8, 2, 4) RD_B1(11, 3, 2) RD_B1(16, 3, 2)
         default: return hipErrorInvalidValue;
     }
 #undef RD_B1
