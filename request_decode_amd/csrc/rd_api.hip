@@ -556,15 +556,31 @@ static rd_status trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t ca
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     m->host_pos += 1;
     st = finish_sync(m);
+    // Each region holds the control wave's events in its lower half and the
+    // stream wave's in its upper half (counts packed in word 0); hand them
+    // to the caller merged in clock order as [n, code, clock, ...].
+    std::vector<uint64_t> h(words);
+    HIP_TRY(hipMemcpy(h.data(), dev, words * 8, hipMemcpyDeviceToHost));
+    const size_t rw = 1 + 2 * (size_t)events;
+    auto merge = [&](const uint64_t* r, uint64_t* out) {
+        const size_t nc = std::min<size_t>(r[0] & 0xffffffffu, events / 2);
+        const size_t ns = std::min<size_t>(r[0] >> 32, events - events / 2);
+        std::vector<std::pair<uint64_t, uint64_t>> ev;
+        for (size_t i = 0; i < nc; ++i) ev.push_back({r[2 + 2 * i], r[1 + 2 * i]});
+        for (size_t i = 0; i < ns; ++i) ev.push_back({r[2 + 2 * (events / 2 + i)], r[1 + 2 * (events / 2 + i)]});
+        std::stable_sort(ev.begin(), ev.end(), [](const auto& a, const auto& b) { return a.first < b.first; });
+        out[0] = ev.size();
+        for (size_t i = 0; i < ev.size(); ++i) {
+            out[1 + 2 * i] = ev[i].second;
+            out[2 + 2 * i] = ev[i].first;
+        }
+        for (size_t i = 1 + 2 * ev.size(); i < rw; ++i) out[i] = 0;
+    };
     if (all) {
-        // compact each workgroup's region to the caller's stride of cap words
-        std::vector<uint64_t> h(words);
-        HIP_TRY(hipMemcpy(h.data(), dev, words * 8, hipMemcpyDeviceToHost));
-        for (int w = 0; w < m->nwg; ++w)
-            memcpy(ts + (size_t)w * cap, h.data() + (size_t)w * (1 + 2 * (size_t)events), (1 + 2 * (size_t)events) * 8);
+        for (int w = 0; w < m->nwg; ++w) merge(h.data() + (size_t)w * rw, ts + (size_t)w * cap);
         *n_out = m->nwg;
     } else {
-        HIP_TRY(hipMemcpy(ts, dev, words * 8, hipMemcpyDeviceToHost));
+        merge(h.data(), ts);
         *n_out = (int32_t)ts[0];
     }
     (void)hipFree(dev);

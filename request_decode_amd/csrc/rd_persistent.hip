@@ -74,6 +74,66 @@ __device__ __forceinline__ const uint64_t* word_at(const uint64_t* buf, int i) {
 // keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// LDS accesses of the stream waves are inline asm.  Their LDS-DMA ring loads
+// are outstanding at all times, and the compiler cannot tell that an LDS
+// read or write does not touch a slot still being filled, so before every
+// LDS instruction it emits it would wait for all outstanding loads
+// (vmcnt(0)): the ring would drain at each row group.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)reinterpret_cast<uintptr_t>((lds_void*)p);
+}
+// n (1..8) 16-byte LDS reads and the wait for them, as one asm statement:
+// the results exist only once the statement ends (as separate statements,
+// the compiler could copy a destination before its load landed).  Outputs
+// are early-clobber: no destination may share a register with an address
+// that a later read of the same statement still uses.
+__device__ __forceinline__ void lds_read_wait1(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]) : "v"(a[0]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait2(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]) : "v"(a[0]), "v"(a[1]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait3(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]) : "v"(a[0]), "v"(a[1]), "v"(a[2]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait4(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait5(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %5\n\tds_read_b128 %1, %6\n\tds_read_b128 %2, %7\n\tds_read_b128 %3, %8\n\tds_read_b128 %4, %9\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait6(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\tds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait7(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %7\n\tds_read_b128 %1, %8\n\tds_read_b128 %2, %9\n\tds_read_b128 %3, %10\n\tds_read_b128 %4, %11\n\tds_read_b128 %5, %12\n\tds_read_b128 %6, %13\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]) : "memory");
+}
+__device__ __forceinline__ void lds_read_wait8(u4v* d, const unsigned* a) {
+    asm volatile("ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)" : "=&v"(d[0]), "=&v"(d[1]), "=&v"(d[2]), "=&v"(d[3]), "=&v"(d[4]), "=&v"(d[5]), "=&v"(d[6]), "=&v"(d[7]) : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_read_wait(u4v (&d)[N], const unsigned (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i += 8) {
+        constexpr int dummy = 0;
+        (void)dummy;
+        const int m = N - i < 8 ? N - i : 8;
+        switch (m) {
+            case 1: lds_read_wait1(d + i, a + i); break;
+            case 2: lds_read_wait2(d + i, a + i); break;
+            case 3: lds_read_wait3(d + i, a + i); break;
+            case 4: lds_read_wait4(d + i, a + i); break;
+            case 5: lds_read_wait5(d + i, a + i); break;
+            case 6: lds_read_wait6(d + i, a + i); break;
+            case 7: lds_read_wait7(d + i, a + i); break;
+            default: lds_read_wait8(d + i, a + i); break;
+        }
+    }
+}
+__device__ __forceinline__ void lds_write4(unsigned addr, float v) {
+    asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
 __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
     return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
 }
@@ -164,10 +224,10 @@ __device__ __forceinline__ void regs_to_lds(float* s, int K, const float (&xr)[K
 // Lane 0 of the control wave and of stream wave 0 append (code, wall clock)
 // events to the workgroup's region; the count lives in LDS and is written
 // out by the control wave at the end of the launch.
-__device__ __attribute__((noinline)) void trace_event(unsigned long long* tb, int cap, int* s_nev, int code) {
+__device__ __forceinline__ void trace_event(unsigned long long* tb, int cap, int* s_nev, int code) {
     if (lane_id() == 0) {
         const int i = atomicAdd(s_nev, 1);
-        if (i < cap) {
+        if (i < cap / 2) {
             tb[1 + 2 * i] = (unsigned long long)code;
             tb[2 + 2 * i] = wall_clock64();
         }
@@ -179,6 +239,24 @@ struct Tracer {
     int* s_nev;
     __device__ __forceinline__ void operator()(int code) const {
         if (tb) trace_event(tb, cap, s_nev, code);
+    }
+};
+// The stream waves' tracer: wave 0 of them records into the upper half of
+// the workgroup's region with a register count, inline and without LDS
+// access (an LDS atomic or a call would drain the wave's load ring, see
+// lds_read_wait).
+struct StreamTracer {
+    unsigned long long* tb;
+    int cap, n;
+    __device__ __forceinline__ void operator()(int code) {
+        if (tb) {
+            if (lane_id() == 0 && n < cap - cap / 2) {
+                const int i = cap / 2 + n;
+                tb[1 + 2 * i] = (unsigned long long)code;
+                tb[2 + 2 * i] = wall_clock64();
+            }
+            ++n;
+        }
     }
 };
 __device__ __forceinline__ Tracer make_tracer(const PersistArgs& P, int* s_nev) {
@@ -361,17 +439,22 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
                                              float (&out)[NR]) {
     static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
     const int lane = lane_id();
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
-    u4v w[NR][KCH];
+    const unsigned base = lds_addr(ring) + (unsigned)lane * 16u;
+    unsigned ad[NR * KCH];
     int s = f.slot;
+#pragma unroll
+    for (int i = 0; i < NR * KCH; ++i) {
+        ad[i] = base + (unsigned)s * UNIT;
+        s = s + 1 == RING ? 0 : s + 1;
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
+    u4v wl[NR * KCH];
+    lds_read_wait<NR * KCH>(wl, ad);   // slots read before they are refilled
+    u4v w[NR][KCH];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
-            w[r][c] = *reinterpret_cast<const u4v*>(ring + s * UNIT + lane * 16);
-            s = s + 1 == RING ? 0 : s + 1;
-        }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slots read before they are refilled
+        for (int c = 0; c < KCH; ++c) w[r][c] = wl[r * KCH + c];
     for (int i = 0; i < NR * KCH; ++i) f.issue(A, P);
     if constexpr (!FK) {
 #pragma unroll
@@ -388,7 +471,7 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
 template <int KCH, int KD, int KA, int KF, bool FK, class F>
 __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const PersistArgs& P, int sw,
                                              unsigned char* ring, const float* s_r, float* s_part, int ph,
-                                             const Tracer& tr) {
+                                             StreamTracer& tr) {
     constexpr int NR = KCH <= 4 ? 2 : 1;
     lds_barrier();   // input staged
     const int kind = ph == 4 * A.n_layers ? 4 : (ph & 3);
@@ -397,7 +480,29 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
     const int ra = pick5(f.ra, kind), rb = ra + pick5(f.nr, kind), r0 = pick5(f.r0, kind);
     if (ra < rb) {
         float xr[KCH][8];
-        load_x_f32<KCH>(s_r, K, xr);
+        {   // load_x_f32 from LDS, as asm (see lds_read_wait); columns >= K read
+            // lane 0's (in bounds) and are zeroed after
+            const int lane = lane_id();
+            unsigned ad[2 * KCH];
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const int col = (c * 64 + lane) * 8 < K ? (c * 64 + lane) * 8 : 0;
+                ad[2 * c] = lds_addr(s_r + col);
+                ad[2 * c + 1] = lds_addr(s_r + col + 4);
+            }
+            u4v xv[2 * KCH];
+            lds_read_wait<2 * KCH>(xv, ad);
+#pragma unroll
+            for (int c = 0; c < KCH; ++c) {
+                const bool in = (c * 64 + lane) * 8 < K;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xr[c][i] = in ? __uint_as_float(xv[2 * c][i]) : 0.f;
+                    xr[c][4 + i] = in ? __uint_as_float(xv[2 * c + 1][i]) : 0.f;
+                }
+            }
+        }
+        const unsigned sp = lds_addr(s_part);
         int r = ra;
         for (; r + NR <= rb; r += NR) {
             float v[NR];
@@ -405,12 +510,12 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
             if (sw == 0 && r == ra) tr(101 + 10 * kind);
             if (lane_id() == 0)
 #pragma unroll
-                for (int k = 0; k < NR; ++k) s_part[r + k - r0] = v[k];
+                for (int k = 0; k < NR; ++k) lds_write4(sp + 4u * (unsigned)(r + k - r0), v[k]);
         }
         if (r < rb) {
             float v[1];
             consume_rows<1, KCH, FK>(f, A, P, sw, ring, xr, K, v);
-            if (lane_id() == 0) s_part[r - r0] = v[0];
+            if (lane_id() == 0) lds_write4(sp + 4u * (unsigned)(r - r0), v[0]);
         }
     }
     if (sw == 0) tr(102 + 10 * kind);
@@ -420,7 +525,8 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
 template <int KD, int KA, int KF, bool FK>
 __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* ring,
                                             const float* s_r, float* s_part, int* s_nev) {
-    const Tracer tr = make_tracer(P, s_nev);
+    const Tracer ct = make_tracer(P, s_nev);
+    StreamTracer tr{sw == 0 ? ct.tb : nullptr, ct.cap, 0};
     Feeder<KD, KA, KF, FK> f;
     f.start(A, P, sw, ring);
     const int NL = A.n_layers;
@@ -434,6 +540,7 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
         stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr);
     }
     drain_vmem();   // the trailing ring requests land before the wave ends
+    if (sw == 0 && lane_id() == 0) s_nev[1] = min(tr.n, tr.cap - tr.cap / 2);
     lds_barrier();   // matches the control wave's last barrier (trace count)
 }
 
@@ -756,7 +863,9 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     }
     TR(98);
     lds_barrier();   // every wave's events are recorded
-    if (TR.tb && lane == 0) TR.tb[0] = (unsigned long long)min(*s_nev, TR.cap);
+    // count word: control events (lower half of the region) | stream events << 32
+    if (TR.tb && lane == 0)
+        TR.tb[0] = (unsigned long long)min(s_nev[0], TR.cap / 2) | ((unsigned long long)s_nev[1] << 32);
 }
 
 }  // namespace
@@ -771,14 +880,14 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     __shared__ __attribute__((aligned(16))) float s_r[KIN * 512];   // the phase's GEMV input
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
-    __shared__ int s_nev;                                          // trace events recorded
+    __shared__ int s_nev[2];                                       // trace events: control, stream
     const int wid = wave_id();
-    if (threadIdx.x == 0) s_nev = 0;
+    if (threadIdx.x < 2) s_nev[threadIdx.x] = 0;
     lds_barrier();
     if (wid == 0)
-        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, &s_nev);
+        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, s_nev);
     else
-        stream_role<KD, KA, KF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, &s_nev);
+        stream_role<KD, KA, KF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, s_nev);
 }
 
 // ---- exchange latency probe ------------------------------------------------------------
