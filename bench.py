@@ -30,19 +30,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-PROMPT = 512
+SEG = 128
 
 
-def step_bytes(shape, L: float) -> float:
+def step_bytes(shape, L: int, kv: str = "fp16") -> float:
     """Algorithmic HBM bytes of one decode step attending to L positions:
     every streamed weight once (all layer matrices and gains, the final gain,
-    the LM head, one embedding row) plus the fp16 K and V rows read."""
+    the LM head, one embedding row) plus the K and V rows read in their
+    stored format: fp16 2 B per element, E5M2 1 B; INT8: 1 B per element of
+    sealed 128-position segments plus their (scale, zero point) pair, 2 B per
+    element of the open segment's fp16 staging rows."""
     D, H, Hk, hd, F, V, NL = (shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
                               shape.vocab, shape.n_layers)
     per_layer = ((H + 2 * Hk) * hd * D + D * H * hd + 2 * F * D + D * F + 2 * D) * 2
     weights = NL * per_layer + (D + V * D + D) * 2
-    kv = NL * 2 * Hk * hd * 2 * L
-    return weights + kv
+    if kv == "fp16":
+        kvb = 2 * Hk * hd * 2 * L
+    elif kv == "e5m2":
+        kvb = 2 * Hk * hd * L
+    else:
+        sealed = (L - 1) // SEG * SEG      # the row being written is in the open segment
+        kvb = 2 * Hk * (hd * (sealed + 2 * (L - sealed)) + (sealed // SEG) * 8)
+    return weights + NL * kvb
 
 
 def cpu_baseline(blob, shape, seconds: float):
@@ -122,6 +131,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=None, help="default: --steps (one equal-size warmup launch)")
     ap.add_argument("--kv", default="fp16", choices=["fp16", "e5m2", "int8"])
+    ap.add_argument("--prompt", type=int, default=512,
+                    help="prompt length (512: the 2B decode workload; 32768: long context; 8192: quantized KV)")
     ap.add_argument("--executor", default="auto", choices=["auto", "graph", "eager", "persistent"])
     ap.add_argument("--phase-iters", type=int, default=96)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -134,8 +145,9 @@ def main():
         sys.exit(2)
     if args.warmup is None:
         args.warmup = args.steps
-    if args.steps < 1 or args.steps + PROMPT > 4096 or args.warmup < 0 or args.warmup + PROMPT > 4096:
-        sys.exit("bench.py: --steps/--warmup must keep the context within 4096")
+    PROMPT = args.prompt
+    if args.steps < 1 or args.warmup < 0 or PROMPT < 1 or PROMPT + max(args.steps, args.warmup) > 65536:
+        sys.exit("bench.py: --prompt/--steps/--warmup must keep the context within 65536")
 
     import torch
 
@@ -150,24 +162,28 @@ def main():
     t0 = time.time()
     blob = synth.make_blob(shape, seed=2)
     print(f"[bench] blob {blob.size / 1e9:.3f} GB generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    prompt = synth.prompt(103, PROMPT, shape.vocab)
-    ctx = PROMPT + max(args.steps, args.warmup)
+    # prompt seeds: 103 for the 512-token workload, 104 long context, 105 the 8K quantized-KV comparison
+    prompt = synth.prompt(104 if PROMPT >= 16384 else 105 if PROMPT == 8192 else 103, PROMPT, shape.vocab)
+    # INT8 KV can only be rewound to a segment start: there the timed steps
+    # follow the warmup steps instead of repeating their positions
+    rewind = args.kv != "int8"
+    ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup) + 1   # +1: the phase run
     m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream)
     executor = m.get_info().executor
     persistent = executor == rd.RD_EXEC_PERSISTENT
-    if persistent:
-        m.set_executor("graph")          # the prompt goes through the graph executor
-    for t in prompt[:-1]:
-        m.decode_step(int(t), want_logits=False)
-    if persistent:
-        m.set_executor("persistent")
+    t0 = time.time()
+    m.prefill(prompt[:-1])               # teacher-forced, on the graph path
+    print(f"[bench] prompt of {PROMPT} fed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     first = int(prompt[-1])
     base = PROMPT - 1
     out = torch.empty(max(args.steps, args.warmup, 1), dtype=torch.int32, device="cuda")
     if args.warmup:
-        m.generate(first, args.warmup)
-        m.set_position(base)
-    print(f"[bench] prompt fed, warmup {args.warmup} done", file=sys.stderr, flush=True)
+        warm = m.generate(first, args.warmup)
+        if rewind:
+            m.set_position(base)
+        else:
+            first, base = int(warm[-1]), base + args.warmup
+    print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -182,7 +198,7 @@ def main():
     ms_per_step = ms / args.steps
     tok_s = args.steps / (ms / 1e3)
     Ls = [base + 1 + i for i in range(args.steps)]
-    bytes_run = sum(step_bytes(shape, L) for L in Ls)
+    bytes_run = sum(step_bytes(shape, L, args.kv) for L in Ls)
     bytes_step = bytes_run / args.steps
     gbps = bytes_run / (ms / 1e3) / 1e9
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
@@ -190,7 +206,8 @@ def main():
 
     # the gate/up GEMV phase kernel of the graph executor, timed alone,
     # rotating over the 24 layers so that its weights come from HBM
-    m.set_position(base + args.steps // 2)
+    if rewind:
+        m.set_position(base + args.steps // 2)
     m.run_phase(3, 0, 24)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -216,13 +233,15 @@ def main():
                 "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                 "bytes_per_launch": k_bytes, "us_per_launch": round(k_us, 3)}
+    workload = ("2b-dense-decode" if PROMPT == 512 and args.kv == "fp16" else
+                "2b-long-context-decode" if PROMPT >= 16384 else f"2b-{args.kv}-kv-decode")
     res = {
         "metric": "batch-1 decode tokens/s + achieved HBM GB/s (MBU %) on 2B-class fp16 model",
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic: seeded N(0,0.02) fp16 weights, uniform random prompt ids",
-        "config": {"workload": "2b-dense-decode", "layers": 24, "d_model": 2048, "heads": 16, "kv_heads": 8,
+        "config": {"workload": workload, "layers": 24, "d_model": 2048, "heads": 16, "kv_heads": 8,
                    "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": 1,
                    "kv_cache": args.kv, "executor": ["auto", "eager", "graph", "persistent"][executor],
                    "positions": [base, base + args.steps - 1]},

@@ -132,6 +132,15 @@ rd_status rd_get_position(const rd_model* m, int32_t* pos);
  * logit or an out-of-range token was seen; the step still advanced), DEVICE. */
 rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, float* logits, int32_t* next);
 
+/* Teacher-forced steps: tokens (host [n*batch], step-major) are fed at
+ * positions pos .. pos+n-1 in order, each through the whole decode step
+ * (K/V appended, logits and argmax computed and dropped), the prompt of the
+ * decode-with-cache definition.  Runs on the graph path whatever the
+ * executor (bit-identical results), enqueues all n steps, then
+ * synchronises once.  Errors as rd_decode_step; CONTEXT_FULL (nothing run)
+ * if the tokens do not fit; INVALID_ARG (nothing run) for an id out of range. */
+rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batch, int32_t n);
+
 /* n_steps greedy steps with the token fed back on the device (no host round
  * trip between steps).  first: host [batch], the token at the current
  * position.  out_tokens: host [n_steps*batch], step-major: the argmax of

@@ -75,6 +75,7 @@ SIGNATURES = [
     ("rd_debug_trace_step", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
     ("rd_debug_trace_step_all", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
     ("rd_last_error", C.c_char_p, []),
+    ("rd_prefill", _I32, [_VP, _I32P, _I32, _I32]),
     ("rd_gemv_f16", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
@@ -208,6 +209,11 @@ class Model:
         if not (allow_numeric and st == RD_ERR_NUMERIC):
             check(st)
         return logits, int(nxt[0])
+
+    def prefill(self, tokens):
+        """Teacher-forced steps over `tokens` (no logits), one sync at the end."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        check(lib().rd_prefill(self._h, t.ctypes.data_as(_I32P), 1, int(t.size)))
 
     def generate(self, first: int, n_steps: int) -> np.ndarray:
         f, fp = _i32([first])

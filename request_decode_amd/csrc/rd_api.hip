@@ -641,6 +641,32 @@ extern "C" rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t 
     return st;
 }
 
+extern "C" rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batch, int32_t n) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!tokens && n > 0) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
+    if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
+    if (n < 0) return fail(RD_ERR_INVALID_ARG, "n < 0");
+    if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "tokens do not fit the context");
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    HIP_TRY(hipSetDevice(m->dev));
+    // one step per token on the graph path (the persistent kernel reads its
+    // token from the device state, which a prompt would overwrite per step)
+    const int32_t ex = m->opt.executor;
+    if (ex == RD_EXEC_PERSISTENT) m->opt.executor = RD_EXEC_GRAPH;
+    for (int i = 0; i < n && !st; ++i) {
+        hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tokens[i], 1);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) st = dev_fail(m, "k_set_state", e);
+        else if (!(st = step_enqueue(m))) m->host_pos += 1;
+    }
+    m->opt.executor = ex;
+    if (st) return st;
+    HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
+    return finish_sync(m);
+}
+
 static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t batch, int32_t n) {
     rd_status st = check_model(m);
     if (st) return st;

@@ -221,9 +221,11 @@ __device__ __forceinline__ void regs_to_lds(float* s, int K, const float (&xr)[K
 }
 
 // ---- event trace -----------------------------------------------------------------
-// Lane 0 of the control wave and of stream wave 0 append (code, wall clock)
-// events to the workgroup's region; the count lives in LDS and is written
-// out by the control wave at the end of the launch.
+// Lane 0 of the control wave appends (code, wall clock) events to the lower
+// half of the workgroup's region, counted in LDS; stream wave 0 fills the
+// upper half (StreamTracer).  The control wave writes both counts out at the
+// end of the launch.  Inline: a call would make the wave wait for all its
+// outstanding memory operations at the callee's entry and skew the times.
 __device__ __forceinline__ void trace_event(unsigned long long* tb, int cap, int* s_nev, int code) {
     if (lane_id() == 0) {
         const int i = atomicAdd(s_nev, 1);

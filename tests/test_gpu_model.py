@@ -70,6 +70,30 @@ def test_tiny_teacher_forced(rd, orc, executor):
     assert n == 64 and graded > 0
 
 
+@pytest.mark.parametrize("kv", ["fp16", "int8"])
+def test_prefill_matches_steps(rd, kv):
+    # rd_prefill is the same teacher-forced steps without the per-step sync:
+    # the step after it (logits, cache) equals the one after single steps.
+    # 300 tokens: two INT8 segments sealed inside the prefill.
+    shape = synth.SHAPES["tiny"]
+    blob = synth.make_blob(shape, seed=1)
+    prompt = synth.prompt(102, 300, shape.vocab)
+    a = rd.Model(blob, max_context=320, kv_format=kv, executor="persistent")
+    for t in prompt[:-1]:
+        a.decode_step(int(t), want_logits=False)
+    la, na = a.decode_step(int(prompt[-1]))
+    b = rd.Model(blob, max_context=320, kv_format=kv, executor="persistent")
+    b.prefill(prompt[:-1])
+    assert b.position() == len(prompt) - 1
+    lb, nb = b.decode_step(int(prompt[-1]))
+    assert na == nb and np.array_equal(la, lb)
+    with pytest.raises(rd.RdError):
+        b.prefill([0] * 40)     # does not fit: nothing runs
+    assert b.position() == len(prompt)
+    a.close()
+    b.close()
+
+
 def test_executors_bit_identical(rd):
     shape = synth.SHAPES["tiny"]
     blob = synth.make_blob(shape, seed=1)
