@@ -67,15 +67,20 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
 // The wave reads each K/V row of its key range once for all G query heads of
 // the group.  Tasks past the splits in use at this position exit at once.
 template <int HD, int G, int KVF>
-__global__ __launch_bounds__(WG) void k_attn(AttnArgs T) {
+__global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T) {
     using Geo = AttnGeo<HD>;
+    constexpr int NW = ATT_WAVES;
+    __shared__ float s_att[NW * G * (HD + 2)];
     const int pos = *T.pos_ptr, L = pos + 1;
     int chunk, nact;
     split_plan(L, T.S, chunk, nact);
-    const int t = blockIdx.x * (WG / WAVE) + wave_id();
+    const int t = blockIdx.x;   // one split of one kv-head per workgroup
     if (t >= T.Hk * nact) return;
-    const int g = t / nact, s = t % nact;
+    const int g = t / nact, s = t % nact, w = wave_id();
     const int lane = lane_id(), j = lane % Geo::LPR;
+    const int p0 = s * chunk, p1 = min(L, p0 + chunk), open0 = pos / SEG * SEG;
+    KvBuf<HD> kb, vb;
+    attn_wave_first<HD, KVF, false, NW>(T, g, p0, p1, open0, w, kb, vb);
     const float qs = T.scale * LOG2E;
     float qv[G][8];
 #pragma unroll
@@ -84,16 +89,13 @@ __global__ __launch_bounds__(WG) void k_attn(AttnArgs T) {
         for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
     AttnAcc<HD, G> acc;
     acc.clear();
-    const int p0 = s * chunk, p1 = min(L, p0 + chunk), open0 = pos / SEG * SEG;
-    for (int pb = p0; pb < p1; pb += Geo::BATCH) {
-        KvRaw kr[Geo::U], vr[Geo::U];
-        kv_batch_raw<HD, KVF, false>(T, g, pb, p0, p1, open0, kr, vr);
-        float kf[Geo::U][8], vf[Geo::U][8];
-        bool valid[Geo::U];
-        kv_batch_cvt<HD, KVF>(pb, p1, kr, vr, kf, vf, valid);
-        acc.batch(qv, kf, vf, valid);
-    }
+    attn_wave_run<HD, G, KVF, false, NW>(T, g, p0, p1, open0, w, qv, acc, kb, vb,
+                                         [](int, float (&)[Geo::U][8], float (&)[Geo::U][8]) {});
     acc.finish();
+    attn_part_store<HD, G>(s_att, w, acc);
+    __syncthreads();
+    if (w != 0) return;
+    attn_combine<HD, G, NW>(s_att, acc);
     if (lane < Geo::LPR) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -276,11 +278,11 @@ namespace {
 template <int KVF>
 hipError_t launch_attn_t(const AttnArgs& A, int hd, int G, hipStream_t s) {
     const int wpb = WG / WAVE;
-    dim3 grid((A.Hk * A.S + wpb - 1) / wpb), block(WG);
+    dim3 grid(A.Hk * A.S), ablock(ATT_WAVES * WAVE), block(WG);   // k_attn: one split per workgroup
     dim3 mgrid((A.H * (hd / 64) + wpb - 1) / wpb);
 #define RD_ATT(HDv, Gv)                                                        \
     if (hd == HDv && G == Gv) {                                                \
-        hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, block, 0, s, A);      \
+        hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, ablock, 0, s, A);     \
         hipLaunchKernelGGL((k_merge<HDv, Gv, KVF>), mgrid, block, 0, s, A);    \
         return hipGetLastError();                                              \
     }

@@ -57,7 +57,6 @@ constexpr int UNIT = 1024;              // bytes per ring slot: 16 per lane, one
 constexpr int RING = 40;                // ring slots per stream wave
 constexpr int PART_MAX = 512;           // row sums a workgroup holds per phase
 constexpr int OWN_MAX = 64;             // residual-stream rows a workgroup owns
-constexpr int NPF = 2;                  // attention batches fetched during the QKV phase
 constexpr int LB_MAX = 1024;            // workgroups (argmax candidates)
 
 // buf[i] with a 32-bit byte offset on a scalar base (one VGPR per address).
@@ -470,10 +469,10 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
 
 // A stream wave's share of GEMV phase ph, between the workgroup barriers
 // that bracket it: its rows' sums into s_part.
-template <int KCH, int KD, int KA, int KF, bool FK, class F>
+template <int KCH, int KD, int KA, int KF, bool FK, class F, class Tail>
 __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const PersistArgs& P, int sw,
                                              unsigned char* ring, const float* s_r, float* s_part, int ph,
-                                             StreamTracer& tr) {
+                                             StreamTracer& tr, Tail tail) {
     constexpr int NR = KCH <= 4 ? 2 : 1;
     lds_barrier();   // input staged
     const int kind = ph == 4 * A.n_layers ? 4 : (ph & 3);
@@ -521,25 +520,109 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
         }
     }
     if (sw == 0) tr(102 + 10 * kind);
+    tail();
     lds_barrier();   // row sums complete
 }
 
-template <int KD, int KA, int KF, bool FK>
+// ---- attention split on all waves of the workgroup --------------------------------------
+// Workgroup b < Hk * nact owns split s of kv-head g (t = b); stream wave sw
+// is attention wave sw.  Between the QKV and O phases: the control wave polls
+// q and the new K/V row, writes them to LDS (s_r: [NQ][64] floats, the lane
+// layout of the poll) and meets the stream waves at a barrier; each stream
+// wave reduces its batches and stores its partial (s_r + NQ*64:
+// [NWA][G][HD+2]); after a second barrier the control wave combines them and
+// publishes the split's partial.  The stream waves fetch their first batch
+// at the end of their QKV rows.
+constexpr int NWA = NSW;
+static_assert(NWA == ATT_WAVES, "the graph executor's attention uses the same number of waves");
+struct AttnSplit {
+    int pos, L, t, g, s, p0, p1, open0;
+};
+__device__ __forceinline__ AttnSplit attn_split(const StepArgs& A, const PersistArgs& P, int step) {
+    AttnSplit r;
+    r.pos = P.pos0 + step;
+    r.L = r.pos + 1;
+    int chunk, nact;
+    split_plan(r.L, A.S, chunk, nact);
+    r.t = (int)blockIdx.x < A.Hk * nact ? (int)blockIdx.x : -1;
+    r.g = r.t / nact;
+    r.s = r.t % nact;
+    r.p0 = r.s * chunk;
+    r.p1 = min(r.L, r.p0 + chunk);
+    r.open0 = r.pos / SEG * SEG;
+    return r;
+}
+template <int HD, int G>
+constexpr int attn_nq() { return G * 8 + 16; }
+// Row pos of the batch: this step's K/V row, from the exchange (it may not
+// be visible in the cache yet).
+template <int HD, int G>
+__device__ __forceinline__ void fix_new_row(int pb, int pos, const float (&kn)[8], const float (&vn)[8],
+                                            float (&kf)[AttnGeo<HD>::U][8], float (&vf)[AttnGeo<HD>::U][8]) {
+    const int slot = lane_id() / AttnGeo<HD>::LPR;
+#pragma unroll
+    for (int u = 0; u < AttnGeo<HD>::U; ++u)
+        if (batch_row<HD>(pb, u, slot) == pos)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kf[u][i] = kn[i];
+                vf[u][i] = vn[i];
+            }
+}
+template <int HD, int G, int KVF>
+__device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A, const AttnSplit& sp, int w,
+                                            float* s_r, KvBuf<HD>& kb, KvBuf<HD>& vb) {
+    constexpr int NQ = attn_nq<HD, G>();
+    lds_barrier();   // q and the new row staged
+    if (sp.t >= 0) {
+        const int lane = lane_id();
+        float qv[G][8], kn[8], vn[8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[h][i] = s_r[(h * 8 + i) * 64 + lane] * (A.scale * LOG2E);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            kn[i] = s_r[(G * 8 + i) * 64 + lane];
+            vn[i] = s_r[(G * 8 + 8 + i) * 64 + lane];
+        }
+        AttnAcc<HD, G> acc;
+        acc.clear();
+        attn_wave_run<HD, G, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, w, qv, acc, kb, vb,
+                                             [&](int pb, float (&kf)[AttnGeo<HD>::U][8],
+                                                 float (&vf)[AttnGeo<HD>::U][8]) {
+                                                 fix_new_row<HD, G>(pb, sp.pos, kn, vn, kf, vf);
+                                             });
+        acc.finish();
+        attn_part_store<HD, G>(s_r + NQ * 64, w, acc);
+    }
+    lds_barrier();   // partials stored
+}
+
+template <int KD, int KA, int KF, int HD, int G, int KVF, bool FK>
 __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* ring,
-                                            const float* s_r, float* s_part, int* s_nev) {
+                                            float* s_r, float* s_part, int* s_nev) {
     const Tracer ct = make_tracer(P, s_nev);
     StreamTracer tr{sw == 0 ? ct.tb : nullptr, ct.cap, 0};
     Feeder<KD, KA, KF, FK> f;
     f.start(A, P, sw, ring);
     const int NL = A.n_layers;
+    auto none = [] {};
     for (int step = 0; step < P.n_steps; ++step) {
+        const AttnSplit sp = attn_split(A, P, step);
         for (int l = 0; l < NL; ++l) {
-            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr);
-            stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr);
-            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr);
-            stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr);
+            const AttnArgs T = attn_args(A, l);
+            KvBuf<HD> kb, vb;
+            // after its QKV rows: the raw K/V rows of its first attention batch
+            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr, [&] {
+                if (sp.t >= 0) attn_wave_first<HD, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sw, kb, vb);
+            });
+            attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, vb);
+            stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none);
+            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none);
+            stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none);
         }
-        stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr);
+        stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr, none);
     }
     drain_vmem();   // the trailing ring requests land before the wave ends
     if (sw == 0 && lane_id() == 0) s_nev[1] = min(tr.n, tr.cap - tr.cap / 2);
@@ -577,13 +660,10 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     }
 
     for (int step = 0; step < P.n_steps; ++step) {
-        const int pos = P.pos0 + step, L = pos + 1;
+        const AttnSplit sp = attn_split(A, P, step);
+        const int pos = sp.pos, L = sp.L, t = sp.t, g = sp.g, s = sp.s, p0 = sp.p0, p1 = sp.p1, open0 = sp.open0;
         int chunk, nact;
         split_plan(L, A.S, chunk, nact);
-        const int open0 = pos / SEG * SEG;
-        const int t = b < A.Hk * nact ? b : -1;
-        const int g = t / nact, s = t % nact;
-        const int p0 = s * chunk, p1 = min(L, p0 + chunk);
         const float2* rope = A.rope + (size_t)pos * (HD / 2);
         // (cos, sin) of the RoPE pair each lane rotates in the QKV epilogue
         float2 cs_lane = make_float2(1.f, 0.f);
@@ -611,13 +691,6 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             }
             TR(0 + TR_STAGED);
             lds_barrier();
-            // While the QKV rows stream: this workgroup's first K/V rows of its split.
-            KvRaw kr[NPF][U], vr[NPF][U];
-#pragma unroll
-            for (int bb = 0; bb < NPF; ++bb) {
-                const int pb = p0 + bb * Geo::BATCH;
-                if (t >= 0 && pb < p1) kv_batch_raw<HD, KVF, true>(T, g, pb, p0, p1, open0, kr[bb], vr[bb]);
-            }
             lds_barrier();
             TR(0 + TR_DONE);
             // On the step that seals an INT8 segment the merge reads the open
@@ -642,11 +715,11 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 }
             }
             TR(0 + TR_PUB);
-            // ---------------- attention split ----------------
+            // ---------------- attention split (all waves) ----------------
+            constexpr int NQ = attn_nq<HD, G>();
             if (t >= 0) {
                 const int lane = lane_id(), j = lane % LPR, slot = lane / LPR;
                 const bool has_new = p1 == L;
-                constexpr int NQ = G * 8 + 16;
                 float val[NQ];
 #pragma unroll
                 for (int k = 0; k < NQ; ++k) val[k] = 0.f;
@@ -660,39 +733,15 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
 #pragma unroll
                 for (int k = 0; k < NQ; ++k) val[k] = __shfl(val[k], j, WAVE);
                 TR(10 + TR_RECV);
-                float qv[G][8];
 #pragma unroll
-                for (int h = 0; h < G; ++h)
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) qv[h][i] = val[h * 8 + i] * (A.scale * LOG2E);
+                for (int k = 0; k < NQ; ++k) s_r[k * 64 + lane] = val[k];
+            }
+            lds_barrier();   // q and the new row staged for the stream waves
+            lds_barrier();   // every wave's partial stored
+            if (t >= 0) {
                 AttnAcc<HD, G> acc;
-                acc.clear();
-                // converted rows, with row pos (not yet visible in the cache) from the exchange
-                auto run_batch = [&](int pb, const KvRaw (&kk)[U], const KvRaw (&vv)[U]) {
-                    float kf[U][8], vf[U][8];
-                    bool valid[U];
-                    kv_batch_cvt<HD, KVF>(pb, p1, kk, vv, kf, vf, valid);
-#pragma unroll
-                    for (int u = 0; u < U; ++u)
-                        if (batch_row<HD>(pb, u, slot) == pos)
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) {
-                                kf[u][i] = val[G * 8 + i];
-                                vf[u][i] = val[G * 8 + 8 + i];
-                            }
-                    acc.batch(qv, kf, vf, valid);
-                };
-#pragma unroll
-                for (int bb = 0; bb < NPF; ++bb) {
-                    const int pb = p0 + bb * Geo::BATCH;
-                    if (pb < p1) run_batch(pb, kr[bb], vr[bb]);
-                }
-                for (int pb = p0 + NPF * Geo::BATCH; pb < p1; pb += Geo::BATCH) {
-                    KvRaw kk[U], vv[U];
-                    kv_batch_raw<HD, KVF, true>(T, g, pb, p0, p1, open0, kk, vv);
-                    run_batch(pb, kk, vv);
-                }
-                acc.finish();
+                attn_combine<HD, G, NWA>(s_r + NQ * 64, acc);
+                const int j = lane % LPR;
                 if (lane < LPR) {
 #pragma unroll
                     for (int h = 0; h < G; ++h) {
@@ -878,8 +927,11 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
 template <int KD, int KA, int KF, int HD, int G, int KVF, bool FK, int SMAX>
 __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     constexpr int KIN = KF > KA ? (KF > KD ? KF : KD) : (KA > KD ? KA : KD);
+    constexpr int NATT = attn_nq<HD, G>() * 64 + NWA * G * (HD + 2);
+    constexpr int NSR = KIN * 512 > NATT ? KIN * 512 : NATT;
     __shared__ __attribute__((aligned(16))) unsigned char s_ring[NSW * RING * UNIT];
-    __shared__ __attribute__((aligned(16))) float s_r[KIN * 512];   // the phase's GEMV input
+    // the phase's GEMV input; between the QKV and O phases the attention exchange
+    __shared__ __attribute__((aligned(16))) float s_r[NSR];
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
     __shared__ int s_nev[2];                                       // trace events: control, stream
@@ -889,7 +941,7 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     if (wid == 0)
         control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, s_nev);
     else
-        stream_role<KD, KA, KF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, s_nev);
+        stream_role<KD, KA, KF, HD, G, KVF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, s_nev);
 }
 
 // ---- exchange latency probe ------------------------------------------------------------

@@ -407,6 +407,101 @@ struct AttnAcc {
 };
 
 // ============================================================================
+// One attention split on the NW waves of a workgroup
+// ============================================================================
+// Both executors reduce a split on ATT_WAVES waves (in the persistent kernel
+// its stream waves), so that they produce the same bits.
+constexpr int ATT_WAVES = 3;
+// Wave w takes the batches p0 + (w + NW*i)*BATCH of the split [p0, p1), with
+// the raw rows of the next two of its batches in flight while one is reduced
+// (three buffers).  The caller loads buffer 0 (attn_wave_first) before
+// attn_wave_run; fix(pb, kf, vf) may replace converted rows (the row being
+// written this step, taken from the exchange instead of the cache).
+template <int HD>
+using KvBuf = KvRaw[3][AttnGeo<HD>::U];
+
+template <int HD, int KVF, bool P, int NW>
+__device__ __forceinline__ void attn_wave_first(const AttnArgs& T, int g, int p0, int p1, int open0, int w,
+                                                KvBuf<HD>& kb, KvBuf<HD>& vb) {
+    const int pb = p0 + w * AttnGeo<HD>::BATCH;
+    if (pb < p1) kv_batch_raw<HD, KVF, P>(T, g, pb, p0, p1, open0, kb[0], vb[0]);
+}
+template <int HD, int G, int KVF, bool P, int NW, class Fix>
+__device__ __forceinline__ void attn_wave_run(const AttnArgs& T, int g, int p0, int p1, int open0, int w,
+                                              const float (&qv)[G][8], AttnAcc<HD, G>& acc, KvBuf<HD>& kb,
+                                              KvBuf<HD>& vb, Fix fix) {
+    using Geo = AttnGeo<HD>;
+    constexpr int STEP = NW * Geo::BATCH;
+    const int pf = p0 + w * Geo::BATCH;
+    if (pf >= p1) return;
+    if (pf + STEP < p1) kv_batch_raw<HD, KVF, P>(T, g, pf + STEP, p0, p1, open0, kb[1], vb[1]);
+    for (int i = 0;; i += 3) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int pb = pf + (i + r) * STEP;
+            if (pb >= p1) return;
+            const int pn = pb + 2 * STEP;
+            if (pn < p1) kv_batch_raw<HD, KVF, P>(T, g, pn, p0, p1, open0, kb[(r + 2) % 3], vb[(r + 2) % 3]);
+            float kf[Geo::U][8], vf[Geo::U][8];
+            bool valid[Geo::U];
+            kv_batch_cvt<HD, KVF>(pb, p1, kb[r], vb[r], kf, vf, valid);
+            fix(pb, kf, vf);
+            acc.batch(qv, kf, vf, valid);
+        }
+    }
+}
+// The NW wave partials of a split, combined in wave order with the same
+// log-sum-exp rule as the split merge: M = max_w m_w, f_w = 2^(m_w - M)
+// (0 for a wave that saw no key), l = sum_w f_w l_w, o = sum_w f_w o_w.
+// s_att: LDS [NW][G][HD+2].  Every wave stores (attn_part_store), the
+// workgroup synchronises, then any one wave combines.
+template <int HD, int G>
+__device__ __forceinline__ void attn_part_store(float* s_att, int w, const AttnAcc<HD, G>& acc) {
+    const int lane = lane_id(), j = lane % AttnGeo<HD>::LPR;
+    if (lane < AttnGeo<HD>::LPR) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float* d = s_att + (w * G + h) * (HD + 2);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d[j * 8 + i] = acc.o[h][i];
+            if (lane == 0) {
+                d[HD] = acc.m[h];
+                d[HD + 1] = acc.l[h];
+            }
+        }
+    }
+}
+template <int HD, int G, int NW>
+__device__ __forceinline__ void attn_combine(const float* s_att, AttnAcc<HD, G>& out) {
+    const int j = lane_id() % AttnGeo<HD>::LPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        float mw[NW];
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            mw[w] = s_att[(w * G + h) * (HD + 2) + HD];
+            M = fmaxf(M, mw[w]);
+        }
+        float L = 0.f, o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float* d = s_att + (w * G + h) * (HD + 2);
+            const float f = mw[w] == -INFINITY ? 0.f : exp2_fast(mw[w] - M);
+            L += f * d[HD + 1];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] += f * d[j * 8 + i];
+        }
+        out.m[h] = M;
+        out.l[h] = L;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out.o[h][i] = o[i];
+    }
+}
+
+// ============================================================================
 // Log-sum-exp merge of the split partials of one query head
 // ============================================================================
 // Partial s of query head h lives at part[(h*S + s)*(HD+2)]: o[HD], m, l.
