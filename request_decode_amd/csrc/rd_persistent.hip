@@ -420,6 +420,28 @@ struct Feeder {
             }
         }
     }
+    // n refills; while the current range has more than n chunks left (FK),
+    // unrolled without the per-chunk range test.
+    template <int N>
+    __device__ __forceinline__ void issue_n(const StepArgs& A, const PersistArgs& P) {
+        if constexpr (FK) {
+            if (left > N) {
+                const unsigned off = (unsigned)lane_id() * 16u;
+                int sl = slot;
+#pragma unroll
+                for (int i = 0; i < N; ++i) {
+                    __builtin_amdgcn_global_load_lds((glb_void*)(p + i * UNIT + off), (lds_void*)(ring + sl * UNIT),
+                                                     16, 0, 2);
+                    sl = sl + 1 == RING ? 0 : sl + 1;
+                }
+                p += N * UNIT;
+                left -= N;
+                slot = sl;
+                return;
+            }
+        }
+        for (int i = 0; i < N; ++i) issue(A, P);
+    }
     __device__ __forceinline__ void start(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* r) {
         ring = r;
         init(A, P, sw);
@@ -456,7 +478,7 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
     for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int c = 0; c < KCH; ++c) w[r][c] = wl[r * KCH + c];
-    for (int i = 0; i < NR * KCH; ++i) f.issue(A, P);
+    f.template issue_n<NR * KCH>(A, P);
     if constexpr (!FK) {
 #pragma unroll
         for (int c = 0; c < KCH; ++c)
