@@ -54,6 +54,22 @@ def step_bytes(shape, L: int, kv: str = "fp16") -> float:
     return weights + NL * kvb
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_persist_2b_decode_fp16_traffic.json")
+
+
+def measured_traffic(args):
+    """HBM bytes of the timed persistent launch (read + write), from the
+    calibrated counter runs recorded under profiles/ for this workload
+    (prompt 512, 256 steps, fp16 KV); None if the run differs from that
+    workload or the kernel's sources changed since the counters were taken."""
+    import json as _json
+    from request_decode_amd.traffic import source_hash
+    if not (args.prompt == 512 and args.steps == 256 and args.kv == "fp16") or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = _json.load(open(TRAFFIC_RECORD))
+    return rec["traffic_bytes"] if rec.get("source_sha256") == source_hash() else None
+
+
 def cpu_baseline(blob, shape, seconds: float):
     """Oracle tokens/s on the machine's host cores: a short prompt, then decode
     steps until `seconds` of CPU work have run (at least 3, at most 64)."""
@@ -226,7 +242,7 @@ def main():
     if persistent:
         roof = {"bound": "hbm", "kernel": "k_persist (whole decode steps, one launch for all timed steps)",
                 "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args),
                 "bytes_per_launch": int(bytes_run), "us_per_launch": round(ms * 1e3, 1)}
     else:
         roof = {"bound": "hbm", "kernel": "k_gateup (RMSNorm + gate/up GEMV + SwiGLU)",
