@@ -687,9 +687,6 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
         int chunk, nact;
         split_plan(L, A.S, chunk, nact);
         const float2* rope = A.rope + (size_t)pos * (HD / 2);
-        // (cos, sin) of the RoPE pair each lane rotates in the QKV epilogue
-        float2 cs_lane = make_float2(1.f, 0.f);
-        if (2 * lane < qr1 - qr0) cs_lane = rope[((qr0 + 2 * lane) % HD) >> 1];
         // gains of the first RMSNorm (later ones are loaded while the wait before
         // them is pending, so that their latency hides in the wait)
         u4v gain[KD];
@@ -712,6 +709,11 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 regs_to_lds<KD>(s_r, A.D, xr);
             }
             TR(0 + TR_STAGED);
+            // (cos, sin) of the RoPE pair each lane rotates in the epilogue,
+            // loaded while the rows stream (kept for the whole step it would
+            // be spilled)
+            float2 cs_lane = make_float2(1.f, 0.f);
+            if (2 * lane < qr1 - qr0) cs_lane = rope[((qr0 + 2 * lane) % HD) >> 1];
             lds_barrier();
             lds_barrier();
             TR(0 + TR_DONE);
