@@ -33,17 +33,18 @@ HBM_PEAK_GBPS = 8000.0
 SEG = 128
 
 
-def step_bytes(shape, L: int, kv: str = "fp16") -> float:
+def step_bytes(shape, L: int, kv: str = "fp16", batch: int = 1) -> float:
     """Algorithmic HBM bytes of one decode step attending to L positions:
     every streamed weight once (all layer matrices and gains, the final gain,
-    the LM head, one embedding row) plus the K and V rows read in their
+    the LM head, one embedding row per sequence) plus, for each of the batch
+    sequences, the K and V rows read in their
     stored format: fp16 2 B per element, E5M2 1 B; INT8: 1 B per element of
     sealed 128-position segments plus their (scale, zero point) pair, 2 B per
     element of the open segment's fp16 staging rows."""
     D, H, Hk, hd, F, V, NL = (shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
                               shape.vocab, shape.n_layers)
     per_layer = ((H + 2 * Hk) * hd * D + D * H * hd + 2 * F * D + D * F + 2 * D) * 2
-    weights = NL * per_layer + (D + V * D + D) * 2
+    weights = NL * per_layer + (batch * D + V * D + D) * 2
     if kv == "fp16":
         kvb = 2 * Hk * hd * 2 * L
     elif kv == "e5m2":
@@ -51,7 +52,7 @@ def step_bytes(shape, L: int, kv: str = "fp16") -> float:
     else:
         sealed = (L - 1) // SEG * SEG      # the row being written is in the open segment
         kvb = 2 * Hk * (hd * (sealed + 2 * (L - sealed)) + (sealed // SEG) * 8)
-    return weights + NL * kvb
+    return weights + batch * NL * kvb
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_persist_2b_decode_fp16_traffic.json")
@@ -147,6 +148,7 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=None, help="default: --steps (one equal-size warmup launch)")
     ap.add_argument("--kv", default="fp16", choices=["fp16", "e5m2", "int8"])
+    ap.add_argument("--batch", type=int, default=1, help="sequences in lockstep (1..8; > 1: graph executor)")
     ap.add_argument("--prompt", type=int, default=512,
                     help="prompt length (512: the 2B decode workload; 32768: long context; 8192: quantized KV)")
     ap.add_argument("--executor", default="auto", choices=["auto", "graph", "eager", "persistent"])
@@ -179,26 +181,29 @@ def main():
     blob = synth.make_blob(shape, seed=2)
     print(f"[bench] blob {blob.size / 1e9:.3f} GB generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     # prompt seeds: 103 for the 512-token workload, 104 long context, 105 the 8K quantized-KV comparison
-    prompt = synth.prompt(104 if PROMPT >= 16384 else 105 if PROMPT == 8192 else 103, PROMPT, shape.vocab)
+    pseed = 104 if PROMPT >= 16384 else 105 if PROMPT == 8192 else 103
+    B = args.batch
+    prompt = synth.prompt(pseed, PROMPT, shape.vocab) if B == 1 else synth.prompts(pseed, PROMPT, shape.vocab, B)
     # INT8 KV can only be rewound to a segment start: there the timed steps
     # follow the warmup steps instead of repeating their positions
     rewind = args.kv != "int8"
     ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup) + 1   # +1: the phase run
-    m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream)
+    m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream,
+                 batch=B)
     executor = m.get_info().executor
     persistent = executor == rd.RD_EXEC_PERSISTENT
     t0 = time.time()
-    m.prefill(prompt[:-1])               # teacher-forced, on the graph path
+    m.prefill(prompt[:-1] if B == 1 else prompt[:, :-1].T)   # teacher-forced, on the graph path
     print(f"[bench] prompt of {PROMPT} fed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    first = int(prompt[-1])
+    first = int(prompt[-1]) if B == 1 else prompt[:, -1].copy()
     base = PROMPT - 1
-    out = torch.empty(max(args.steps, args.warmup, 1), dtype=torch.int32, device="cuda")
+    out = torch.empty(max(args.steps, args.warmup, 1) * B, dtype=torch.int32, device="cuda")
     if args.warmup:
         warm = m.generate(first, args.warmup)
         if rewind:
             m.set_position(base)
         else:
-            first, base = int(warm[-1]), base + args.warmup
+            first, base = (int(warm[-1]) if B == 1 else warm[-1].copy()), base + args.warmup
     print(f"[bench] warmup {args.warmup} done", file=sys.stderr, flush=True)
 
     torch.cuda.synchronize()
@@ -212,30 +217,32 @@ def main():
     m.synchronize()
     ms = ev0.elapsed_time(ev1)
     ms_per_step = ms / args.steps
-    tok_s = args.steps / (ms / 1e3)
+    tok_s = args.steps * B / (ms / 1e3)
     Ls = [base + 1 + i for i in range(args.steps)]
-    bytes_run = sum(step_bytes(shape, L, args.kv) for L in Ls)
+    bytes_run = sum(step_bytes(shape, L, args.kv, B) for L in Ls)
     bytes_step = bytes_run / args.steps
     gbps = bytes_run / (ms / 1e3) / 1e9
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
           f"{gbps:.0f} GB/s (wall {wall * 1e3 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
 
-    # the gate/up GEMV phase kernel of the graph executor, timed alone,
-    # rotating over the 24 layers so that its weights come from HBM
-    if rewind:
-        m.set_position(base + args.steps // 2)
-    m.run_phase(3, 0, 24)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    m.run_phase(3, 0, args.phase_iters)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    m.synchronize()
-    k_us = e0.elapsed_time(e1) * 1e3 / args.phase_iters
+    # the gate/up GEMV phase kernel of the (batch-1) graph executor, timed
+    # alone, rotating over the 24 layers so that its weights come from HBM
+    k_us = k_gbps = None
     k_bytes = (2 * shape.d_ff * shape.d_model + shape.d_model) * 2
-    k_gbps = k_bytes / (k_us * 1e-6) / 1e9
-    print(f"[bench] gate/up phase kernel: {k_us:.2f} us/launch, {k_gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    if B == 1:
+        if rewind:
+            m.set_position(base + args.steps // 2)
+        m.run_phase(3, 0, 24)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        m.run_phase(3, 0, args.phase_iters)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        m.synchronize()
+        k_us = e0.elapsed_time(e1) * 1e3 / args.phase_iters
+        k_gbps = k_bytes / (k_us * 1e-6) / 1e9
+        print(f"[bench] gate/up phase kernel: {k_us:.2f} us/launch, {k_gbps:.0f} GB/s", file=sys.stderr, flush=True)
     m.close()
     gemv = None if args.no_gemv else gemv_microbench(rd, torch, stream)
 
@@ -244,28 +251,37 @@ def main():
                 "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args),
                 "bytes_per_launch": int(bytes_run), "us_per_launch": round(ms * 1e3, 1)}
+    elif B > 1:
+        roof = {"bound": "hbm", "kernel": "batch step: graph of per-phase kernels (thin GEMMs k_gemm_b8 on MFMA)",
+                "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                "bytes_per_launch": int(bytes_step), "us_per_launch": round(ms_per_step * 1e3, 1)}
     else:
         roof = {"bound": "hbm", "kernel": "k_gateup (RMSNorm + gate/up GEMV + SwiGLU)",
                 "achieved": round(k_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(k_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                 "bytes_per_launch": k_bytes, "us_per_launch": round(k_us, 3)}
-    workload = ("2b-dense-decode" if PROMPT == 512 and args.kv == "fp16" else
+    workload = ("2b-dense-decode" if PROMPT == 512 and args.kv == "fp16" and B == 1 else
                 "2b-long-context-decode" if PROMPT >= 16384 else f"2b-{args.kv}-kv-decode")
+    if B > 1:
+        workload += f"-batch{B}"
     res = {
-        "metric": "batch-1 decode tokens/s + achieved HBM GB/s (MBU %) on 2B-class fp16 model",
+        "metric": ("batch-1 decode tokens/s + achieved HBM GB/s (MBU %) on 2B-class fp16 model" if B == 1 else
+                   f"batch-{B} decode tokens/s (all sequences) + achieved HBM GB/s on 2B-class fp16 model"),
         "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic: seeded N(0,0.02) fp16 weights, uniform random prompt ids",
         "config": {"workload": workload, "layers": 24, "d_model": 2048, "heads": 16, "kv_heads": 8,
-                   "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": 1,
+                   "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": B,
                    "kv_cache": args.kv, "executor": ["auto", "eager", "graph", "persistent"][executor],
                    "positions": [base, base + args.steps - 1]},
         "hbm_gbps": round(gbps, 1), "mbu": round(gbps / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": int(bytes_step),
         "roofline": roof,
-        "gateup_phase_kernel": {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)},
     }
+    if k_us is not None:
+        res["gateup_phase_kernel"] = {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)}
     if gemv is not None:
         res["gemv_microbench"] = gemv
     if not args.no_cpu_baseline:

@@ -81,7 +81,12 @@ typedef struct {
     int32_t device;       /* HIP device ordinal */
     void* stream;         /* hipStream_t to run on, or NULL for a library-owned stream */
     int32_t max_context;  /* positions per sequence (KV rows allocated), >= 1 */
-    int32_t max_batch;    /* independent sequences advancing in lockstep: 1 */
+    int32_t max_batch;    /* independent sequences advancing in lockstep at one position: 1..8.
+                           * Batch > 1 runs every GEMV as a thin GEMM on the matrix cores
+                           * ("Real-time LLM inference on standard GPUs", section on memory
+                           * bandwidth: a weight byte serves every sequence), on the EAGER or
+                           * GRAPH executor (PERSISTENT: UNSUPPORTED); needs d_model,
+                           * n_heads*head_dim and d_ff multiples of 64, at most 8192. */
     int32_t kv_format;    /* rd_kv_format */
     int32_t executor;     /* rd_executor */
     int32_t attn_splits;  /* maximum key-axis splits per kv-head, 0 = default (64) */
@@ -157,7 +162,7 @@ rd_status rd_generate_async(rd_model* m, const int32_t* first, int32_t batch, in
 /* Wait for the model's stream and report device-side errors. */
 rd_status rd_synchronize(rd_model* m);
 
-/* Copy the raw KV storage of (seq, layer, which: 0 = K, 1 = V) into host
+/* Copy the raw KV storage of (seq < max_batch, layer, which: 0 = K, 1 = V) into host
  * memory dst (capacity cap bytes).  Layout per format:
  *  FP16:  u16 [n_kv_heads][max_context][head_dim]
  *  E5M2:  u8  [n_kv_heads][max_context][head_dim]

@@ -124,14 +124,14 @@ class Model:
     """A decode-step model on one GPU (rd_model_create and friends)."""
 
     def __init__(self, blob: np.ndarray, max_context: int = 4096, kv_format: str = "fp16",
-                 executor: str = "auto", device: int = 0, stream: int = 0, attn_splits: int = 0):
+                 executor: str = "auto", device: int = 0, stream: int = 0, attn_splits: int = 0, batch: int = 1):
         L = lib()
         o = rd_options()
         L.rd_options_init(C.byref(o))
         o.device = device
         o.stream = stream or None
         o.max_context = max_context
-        o.max_batch = 1
+        o.max_batch = batch
         o.kv_format = KV_FORMATS[kv_format]
         o.executor = EXECUTORS[executor]
         o.attn_splits = attn_splits
@@ -143,6 +143,7 @@ class Model:
         self.info = self.get_info()
         self.vocab = self.info.vocab
         self.kv_format = kv_format
+        self.batch = batch
 
     def close(self):
         h = getattr(self, "_h", None)
@@ -200,30 +201,45 @@ class Model:
             out.append((ev[:, 0], ev[:, 1]))
         return out
 
-    def decode_step(self, token: int, want_logits: bool = True, allow_numeric: bool = False):
-        t, tp = _i32([token])
-        nxt, np_ = _i32([0])
-        logits = np.empty(self.vocab, np.float32) if want_logits else None
+    def _tokens(self, tokens):
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if t.size != self.batch:
+            raise ValueError(f"need {self.batch} token(s), one per sequence")
+        return t, t.ctypes.data_as(_I32P)
+
+    def decode_step(self, token, want_logits: bool = True, allow_numeric: bool = False):
+        """One step.  Batch 1: token int -> (logits [V], next int); batch B:
+        tokens [B] -> (logits [B][V], next [B])."""
+        t, tp = self._tokens(token)
+        nxt = np.zeros(self.batch, np.int32)
+        logits = np.empty((self.batch, self.vocab), np.float32) if want_logits else None
         lp = logits.ctypes.data_as(_FP) if want_logits else None
-        st = lib().rd_decode_step(self._h, tp, 1, lp, np_)
+        st = lib().rd_decode_step(self._h, tp, self.batch, lp, nxt.ctypes.data_as(_I32P))
         if not (allow_numeric and st == RD_ERR_NUMERIC):
             check(st)
-        return logits, int(nxt[0])
+        if self.batch == 1:
+            return (logits[0] if want_logits else None), int(nxt[0])
+        return logits, nxt
 
     def prefill(self, tokens):
-        """Teacher-forced steps over `tokens` (no logits), one sync at the end."""
-        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
-        check(lib().rd_prefill(self._h, t.ctypes.data_as(_I32P), 1, int(t.size)))
+        """Teacher-forced steps over `tokens` ([n] at batch 1, [n][B] at batch B,
+        step-major), no logits, one sync at the end."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if t.size % self.batch:
+            raise ValueError("token count must be a multiple of the batch")
+        check(lib().rd_prefill(self._h, t.ctypes.data_as(_I32P), self.batch, int(t.size // self.batch)))
 
-    def generate(self, first: int, n_steps: int) -> np.ndarray:
-        f, fp = _i32([first])
-        out = np.zeros(n_steps, np.int32)
-        check(lib().rd_generate(self._h, fp, 1, n_steps, out.ctypes.data_as(_I32P)))
-        return out
+    def generate(self, first, n_steps: int) -> np.ndarray:
+        """n_steps greedy steps from `first` (int, or [B]): tokens [n_steps]
+        (batch 1) or [n_steps][B]."""
+        f, fp = self._tokens(first)
+        out = np.zeros(n_steps * self.batch, np.int32)
+        check(lib().rd_generate(self._h, fp, self.batch, n_steps, out.ctypes.data_as(_I32P)))
+        return out if self.batch == 1 else out.reshape(n_steps, self.batch)
 
-    def generate_async(self, first: int, n_steps: int, out_dev_ptr: int):
-        f, fp = _i32([first])
-        check(lib().rd_generate_async(self._h, fp, 1, n_steps, out_dev_ptr))
+    def generate_async(self, first, n_steps: int, out_dev_ptr: int):
+        f, fp = self._tokens(first)
+        check(lib().rd_generate_async(self._h, fp, self.batch, n_steps, out_dev_ptr))
 
     def synchronize(self):
         check(lib().rd_synchronize(self._h))
@@ -237,13 +253,13 @@ class Model:
         nseg = (i.max_context + SEG - 1) // SEG
         return main, i.n_kv_heads * SEG * i.head_dim * 2, i.n_kv_heads * nseg * 8
 
-    def export_kv(self, layer: int, which: int):
-        """Raw cache of (layer, K=0|V=1): dict of numpy arrays in the ABI layout."""
+    def export_kv(self, layer: int, which: int, seq: int = 0):
+        """Raw cache of (sequence, layer, K=0|V=1): dict of numpy arrays in the ABI layout."""
         i = self.info
         main, st, meta = self.kv_region_bytes()
         buf = np.empty(main + st + meta, np.uint8)
         w = C.c_size_t()
-        check(lib().rd_debug_export_kv(self._h, 0, layer, which, buf.ctypes.data, buf.size, C.byref(w)))
+        check(lib().rd_debug_export_kv(self._h, seq, layer, which, buf.ctypes.data, buf.size, C.byref(w)))
         Hk, ctx, hd = i.n_kv_heads, i.max_context, i.head_dim
         if i.kv_format == RD_KV_FP16:
             return {"rows": buf.view(np.uint16).reshape(Hk, ctx, hd)}
@@ -254,7 +270,7 @@ class Model:
                 "stage": buf[main:main + st].view(np.uint16).reshape(Hk, SEG, hd),
                 "meta": buf[main + st:].view(np.float32).reshape(Hk, nseg, 2)}
 
-    def import_kv(self, layer: int, which: int, parts: dict, pos: int):
+    def import_kv(self, layer: int, which: int, parts: dict, pos: int, seq: int = 0):
         i = self.info
         if i.kv_format == RD_KV_INT8_SEG128:
             raw = np.concatenate([np.ascontiguousarray(parts["rows"]).view(np.uint8).reshape(-1),
@@ -262,7 +278,7 @@ class Model:
                                   np.ascontiguousarray(parts["meta"]).view(np.uint8).reshape(-1)])
         else:
             raw = np.ascontiguousarray(parts["rows"]).view(np.uint8).reshape(-1)
-        check(lib().rd_debug_import_kv(self._h, 0, layer, which, raw.ctypes.data, raw.size, pos))
+        check(lib().rd_debug_import_kv(self._h, seq, layer, which, raw.ctypes.data, raw.size, pos))
 
 
 # ---- standalone kernels (device pointers as ints) -------------------------------------

@@ -168,9 +168,12 @@ extern "C" void rd_options_init(rd_options* o) {
 
 namespace {
 
-__global__ void k_set_state(StepState* st, int pos, int token, int reset_gen) {
+struct Tokens8 {
+    int t[8];
+};
+__global__ void k_set_state(StepState* st, int pos, Tokens8 tk, int nb, int reset_gen) {
     st->pos = pos;
-    st->token[0] = token;
+    for (int b = 0; b < nb; ++b) st->token[b] = tk.t[b];
     st->err = 0;
     if (reset_gen) st->n_gen = 0;
 }
@@ -241,6 +244,20 @@ rd_status step_enqueue(rd_model* m) {
     return RD_OK;
 }
 
+// Tokens of every sequence (host [max_batch], or NULL for zeros) and the
+// position into the device step state.
+hipError_t set_state(rd_model* m, const int32_t* tokens) {
+    Tokens8 tk{};
+    for (int b = 0; b < m->opt.max_batch; ++b) tk.t[b] = tokens ? tokens[b] : 0;
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tk, m->opt.max_batch, 1);
+    return hipGetLastError();
+}
+bool tokens_ok(const rd_model* m, const int32_t* t, int n) {
+    for (int i = 0; i < n; ++i)
+        if (t[i] < 0 || t[i] >= m->d.V) return false;
+    return true;
+}
+
 rd_status check_model(const rd_model* m) {
     if (!m) return fail(RD_ERR_INVALID_ARG, "model is NULL");
     if (m->poisoned) return fail(RD_ERR_DEVICE, "model is poisoned by an earlier device error");
@@ -260,7 +277,9 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
         opt = *opt_in;
     }
     if (opt.max_context < 1 || opt.max_context > (1 << 22)) return fail(RD_ERR_INVALID_ARG, "max_context out of range");
-    if (opt.max_batch != 1) return fail(RD_ERR_UNSUPPORTED, "max_batch must be 1");
+    if (opt.max_batch < 1 || opt.max_batch > 8) return fail(RD_ERR_UNSUPPORTED, "max_batch must be 1..8");
+    if (opt.max_batch > 1 && opt.executor == RD_EXEC_PERSISTENT)
+        return fail(RD_ERR_UNSUPPORTED, "the persistent executor runs batch 1 only");
     if (opt.kv_format < RD_KV_FP16 || opt.kv_format > RD_KV_INT8_SEG128)
         return fail(RD_ERR_INVALID_ARG, "bad kv_format");
     if (opt.executor < RD_EXEC_AUTO || opt.executor > RD_EXEC_PERSISTENT) return fail(RD_ERR_INVALID_ARG, "bad executor");
@@ -309,6 +328,9 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     CREATE_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking));
 
     const size_t D = d.D, H = d.H, Hk = d.Hk, hd = d.hd, F = d.F, V = d.V, NL = d.L;
+    const size_t NB = opt.max_batch;
+    if (NB > 1 && ((D % 64) || ((H * hd) % 64) || (F % 64) || D > 8192 || H * hd > 8192 || F > 8192))
+        return bail(fail(RD_ERR_UNSUPPORTED, "batch > 1 needs d_model, n_heads*head_dim, d_ff multiples of 64, <= 8192"));
     const size_t Nqkv = (H + 2 * Hk) * hd;
     // ---- device weight image: embed | per layer {wqkv, wo, wgu, wd, g_attn, g_ffn} | g_final | lm_head
     size_t off = 0;
@@ -387,9 +409,10 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     m->lm_head = (const _Float16*)(W + o_lm);
     m->streamed = (NL * (Nqkv * D + D * H * hd + 2 * F * D + D * F + 2 * D) + D + V * D + D) * 2;
 
-    // ---- KV cache
+    // ---- KV cache: NB sequences, each [layer][kv-head][ctx][hd]
     const size_t ctx = opt.max_context;
-    const size_t kv_elems = NL * Hk * ctx * hd;
+    const size_t kv_seq = NL * Hk * ctx * hd;
+    const size_t kv_elems = NB * kv_seq;
     const size_t es = opt.kv_format == RD_KV_FP16 ? 2 : 1;
     m->nseg = (int)((ctx + SEG - 1) / SEG);
     CREATE_TRY(hipMalloc(&m->kc, kv_elems * es));
@@ -398,7 +421,7 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     CREATE_TRY(hipMemset(m->vc, 0, kv_elems * es));
     m->kv_bytes = 2 * kv_elems * es;
     if (opt.kv_format == RD_KV_INT8_SEG128) {
-        const size_t st_elems = NL * 2 * Hk * SEG * hd, meta_elems = NL * 2 * Hk * m->nseg * 2;
+        const size_t st_elems = NB * NL * 2 * Hk * SEG * hd, meta_elems = NB * NL * 2 * Hk * m->nseg * 2;
         CREATE_TRY(hipMalloc(&m->stage, st_elems * 2));
         CREATE_TRY(hipMalloc(&m->meta, meta_elems * 4));
         CREATE_TRY(hipMemset(m->stage, 0, st_elems * 2));
@@ -414,16 +437,18 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
         a = align256(a + bytes);
         return o;
     };
-    const size_t o_x = carve(D * 4), o_q = carve(H * hd * 4), o_a = carve(H * hd * 4), o_m = carve(F * 4);
-    const size_t o_logits = carve(V * 4);
+    const size_t o_x = carve(NB * D * 4), o_q = carve(NB * H * hd * 4), o_a = carve(NB * H * hd * 4);
+    const size_t o_m = carve(NB * F * 4);
+    const size_t o_logits = carve(NB * V * 4);
     const size_t S = m->S;
-    const size_t o_part = carve(H * S * (hd + 2) * 4);
+    const size_t o_part = carve(NB * H * S * (hd + 2) * 4);
+    const size_t o_y = carve(NB > 1 ? NB * std::max(Nqkv, 2 * F) * 4 : 4), o_xh = carve(NB > 1 ? NB * D * 2 : 4);
     const int n_arg = n_lm_wg;   // argmax partials of the LM-head kernel
     const size_t o_av = carve(n_arg * 4), o_ai = carve(n_arg * 4), o_ac = carve(64 * 4);
     // exchange words of the persistent executor
     const size_t o_xb1 = carve(D * 8), o_xb2 = carve(D * 8), o_qb = carve(Nqkv * 8), o_pb = carve(H * S * (hd + 2) * 8);
     const size_t o_ab = carve(H * hd * 8), o_mb = carve(F * 8), o_lb = carve(1024 * 8), o_abort = carve(64);
-    const size_t o_st = carve(sizeof(StepState)), o_gen = carve(ctx * 4);
+    const size_t o_st = carve(sizeof(StepState)), o_gen = carve(NB * ctx * 4);
     const size_t o_rope = carve(ctx * (hd / 2) * sizeof(float2));
     CREATE_TRY(hipMalloc(&m->act, a));
     CREATE_TRY(hipMemset(m->act, 0, a));
@@ -438,8 +463,8 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
             }
         CREATE_TRY(hipMemcpy(X + o_rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice));
     }
-    CREATE_TRY(hipHostMalloc((void**)&m->gen_host, ctx * 4, hipHostMallocDefault));
-    CREATE_TRY(hipHostMalloc((void**)&m->logits_host, V * 4, hipHostMallocDefault));
+    CREATE_TRY(hipHostMalloc((void**)&m->gen_host, NB * ctx * 4, hipHostMallocDefault));
+    CREATE_TRY(hipHostMalloc((void**)&m->logits_host, NB * V * 4, hipHostMallocDefault));
     CREATE_TRY(hipHostMalloc((void**)&m->state_host, sizeof(StepState), hipHostMallocDefault));
 
     StepArgs& A = m->A;
@@ -459,9 +484,18 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     A.st = (StepState*)(X + o_st); A.gen_out = (int*)(X + o_gen);
     A.rope = (const float2*)(X + o_rope);
     A.kc = m->kc; A.vc = m->vc; A.stage = m->stage; A.meta = m->meta; A.nseg = m->nseg;
+    A.B = (int)NB;
+    A.ncu = cus;
+    A.kv_bstride = kv_seq * es;
+    A.st_bstride = NL * 2 * Hk * SEG * hd;
+    A.meta_bstride = NL * 2 * Hk * (size_t)m->nseg * 2;
+    A.y = (float*)(X + o_y);
+    A.xh = (_Float16*)(X + o_xh);
 
     // ---- executor: the persistent kernel where its shape is built, else the graph
-    if (opt.executor == RD_EXEC_AUTO || opt.executor == RD_EXEC_PERSISTENT) {
+    if (NB > 1) {
+        if (m->opt.executor == RD_EXEC_AUTO) m->opt.executor = RD_EXEC_GRAPH;
+    } else if (opt.executor == RD_EXEC_AUTO || opt.executor == RD_EXEC_PERSISTENT) {
         int nwg = 0;
         if (persistent_supported(A) && persistent_max_grid(A, m->dev, &nwg) == hipSuccess && nwg > 0) {
             // the persistent kernel finds layer l's weights layer_stride bytes past layer 0's
@@ -516,7 +550,7 @@ extern "C" rd_status rd_set_executor(rd_model* m, int32_t executor) {
     if (executor != RD_EXEC_EAGER && executor != RD_EXEC_GRAPH && executor != RD_EXEC_PERSISTENT)
         return fail(RD_ERR_INVALID_ARG, "executor must be EAGER, GRAPH or PERSISTENT");
     if (executor == RD_EXEC_PERSISTENT && !m->nwg)
-        return fail(RD_ERR_UNSUPPORTED, "this model has no persistent kernel");
+        return fail(RD_ERR_UNSUPPORTED, "this model has no persistent kernel (batch > 1, or shape not built)");
     m->opt.executor = executor;
     return RD_OK;
 }
@@ -547,8 +581,7 @@ static rd_status trace_step(rd_model* m, int32_t token, uint64_t* ts, int32_t ca
     unsigned long long* dev = nullptr;
     HIP_TRY(hipMalloc(&dev, words * 8));
     HIP_TRY(hipMemset(dev, 0, words * 8));
-    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, token, 1);
-    HIP_TRY(hipGetLastError());
+    HIP_TRY(set_state(m, &token));
     if ((st = persistent_enqueue(m, 1, 0, dev, events, all))) {
         (void)hipFree(dev);
         return st;
@@ -602,8 +635,8 @@ extern "C" rd_status rd_debug_run_phase(rd_model* m, int32_t phase, int32_t laye
         return fail(RD_ERR_INVALID_ARG, "bad phase/layer/iters");
     if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
     HIP_TRY(hipSetDevice(m->dev));
-    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, 0, 1);
-    HIP_TRY(hipGetLastError());
+    if (m->opt.max_batch > 1) return fail(RD_ERR_UNSUPPORTED, "phase kernels are the batch-1 step's");
+    HIP_TRY(set_state(m, nullptr));
     for (int i = 0; i < iters; ++i) HIP_TRY(launch_phase(m->A, phase, (layer + i) % m->d.L, m->stream));
     return RD_OK;
 }
@@ -625,19 +658,19 @@ extern "C" rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t 
     if (!tokens) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
     if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
-    if (tokens[0] < 0 || tokens[0] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (!tokens_ok(m, tokens, batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
     HIP_TRY(hipSetDevice(m->dev));
-    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tokens[0], 1);
-    HIP_TRY(hipGetLastError());
+    HIP_TRY(set_state(m, tokens));
     if ((st = step_enqueue(m))) return st;
-    if (logits)
-        HIP_TRY(hipMemcpyAsync(m->logits_host, m->A.logits, (size_t)m->d.V * 4, hipMemcpyDeviceToHost, m->stream));
+    const size_t nlog = (size_t)batch * m->d.V;
+    if (logits) HIP_TRY(hipMemcpyAsync(m->logits_host, m->A.logits, nlog * 4, hipMemcpyDeviceToHost, m->stream));
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     m->host_pos += 1;
     st = finish_sync(m);
     if (st == RD_ERR_DEVICE) return st;
-    if (logits) memcpy(logits, m->logits_host, (size_t)m->d.V * 4);
-    if (next) next[0] = m->state_host->token[0];
+    if (logits) memcpy(logits, m->logits_host, nlog * 4);
+    if (next)
+        for (int b = 0; b < batch; ++b) next[b] = m->state_host->token[b];
     return st;
 }
 
@@ -648,16 +681,14 @@ extern "C" rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batc
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
     if (n < 0) return fail(RD_ERR_INVALID_ARG, "n < 0");
     if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "tokens do not fit the context");
-    for (int i = 0; i < n; ++i)
-        if (tokens[i] < 0 || tokens[i] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (!tokens_ok(m, tokens, n * batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
     HIP_TRY(hipSetDevice(m->dev));
     // one step per token on the graph path (the persistent kernel reads its
     // token from the device state, which a prompt would overwrite per step)
     const int32_t ex = m->opt.executor;
     if (ex == RD_EXEC_PERSISTENT) m->opt.executor = RD_EXEC_GRAPH;
     for (int i = 0; i < n && !st; ++i) {
-        hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tokens[i], 1);
-        hipError_t e = hipGetLastError();
+        hipError_t e = set_state(m, tokens + (size_t)i * batch);
         if (e != hipSuccess) st = dev_fail(m, "k_set_state", e);
         else if (!(st = step_enqueue(m))) m->host_pos += 1;
     }
@@ -674,10 +705,9 @@ static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t bat
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
     if (n < 0) return fail(RD_ERR_INVALID_ARG, "n_steps < 0");
     if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "steps do not fit the context");
-    if (first[0] < 0 || first[0] >= m->d.V) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (!tokens_ok(m, first, batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
     HIP_TRY(hipSetDevice(m->dev));
-    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, first[0], 1);
-    HIP_TRY(hipGetLastError());
+    HIP_TRY(set_state(m, first));
     if (m->opt.executor == RD_EXEC_PERSISTENT) {
         // whole runs of steps in one launch, in chunks that keep one kernel short
         constexpr int kChunk = 512;
@@ -699,11 +729,12 @@ extern "C" rd_status rd_generate(rd_model* m, const int32_t* first, int32_t batc
     rd_status st = generate_enqueue(m, first, batch, n);
     if (st) return st;
     if (n == 0) return RD_OK;
-    HIP_TRY(hipMemcpyAsync(m->gen_host, m->A.gen_out, (size_t)n * 4, hipMemcpyDeviceToHost, m->stream));
+    const size_t nt = (size_t)n * batch;
+    HIP_TRY(hipMemcpyAsync(m->gen_host, m->A.gen_out, nt * 4, hipMemcpyDeviceToHost, m->stream));
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     st = finish_sync(m);
     if (st == RD_ERR_DEVICE) return st;
-    memcpy(out, m->gen_host, (size_t)n * 4);
+    memcpy(out, m->gen_host, nt * 4);
     return st;
 }
 
@@ -712,7 +743,7 @@ extern "C" rd_status rd_generate_async(rd_model* m, const int32_t* first, int32_
     rd_status st = generate_enqueue(m, first, batch, n);
     if (st) return st;
     if (n > 0)
-        HIP_TRY(hipMemcpyAsync(out_dev, m->A.gen_out, (size_t)n * 4, hipMemcpyDeviceToDevice, m->stream));
+        HIP_TRY(hipMemcpyAsync(out_dev, m->A.gen_out, (size_t)n * batch * 4, hipMemcpyDeviceToDevice, m->stream));
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     return RD_OK;
 }
@@ -731,14 +762,16 @@ struct KvRegion {
     size_t bytes;
 };
 // Regions of (layer, which) in export order.
-int kv_regions(rd_model* m, int layer, int which, KvRegion* r) {
+int kv_regions(rd_model* m, int seq, int layer, int which, KvRegion* r) {
     const size_t Hk = m->d.Hk, ctx = m->opt.max_context, hd = m->d.hd;
     const size_t es = m->opt.kv_format == RD_KV_FP16 ? 2 : 1;
     const size_t lay = (size_t)layer * Hk * ctx * hd * es;
-    r[0] = {(uint8_t*)(which ? m->vc : m->kc) + lay, Hk * ctx * hd * es};
+    r[0] = {(uint8_t*)(which ? m->vc : m->kc) + seq * m->A.kv_bstride + lay, Hk * ctx * hd * es};
     if (m->opt.kv_format != RD_KV_INT8_SEG128) return 1;
-    r[1] = {(uint8_t*)(m->stage + ((size_t)layer * 2 + which) * Hk * SEG * hd), Hk * SEG * hd * 2};
-    r[2] = {(uint8_t*)(m->meta + ((size_t)layer * 2 + which) * Hk * m->nseg * 2), Hk * (size_t)m->nseg * 8};
+    r[1] = {(uint8_t*)(m->stage + seq * m->A.st_bstride + ((size_t)layer * 2 + which) * Hk * SEG * hd),
+            Hk * SEG * hd * 2};
+    r[2] = {(uint8_t*)(m->meta + seq * m->A.meta_bstride + ((size_t)layer * 2 + which) * Hk * m->nseg * 2),
+            Hk * (size_t)m->nseg * 8};
     return 3;
 }
 }  // namespace
@@ -747,10 +780,10 @@ extern "C" rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer,
                                         size_t* written) {
     rd_status st = check_model(m);
     if (st) return st;
-    if (!dst || seq != 0 || layer < 0 || layer >= m->d.L || which < 0 || which > 1)
+    if (!dst || seq < 0 || seq >= m->opt.max_batch || layer < 0 || layer >= m->d.L || which < 0 || which > 1)
         return fail(RD_ERR_INVALID_ARG, "bad export arguments");
     KvRegion r[3];
-    const int nr = kv_regions(m, layer, which, r);
+    const int nr = kv_regions(m, seq, layer, which, r);
     size_t total = 0;
     for (int i = 0; i < nr; ++i) total += r[i].bytes;
     if (cap < total) return fail(RD_ERR_INVALID_ARG, "destination too small: need " + std::to_string(total));
@@ -769,11 +802,11 @@ extern "C" rd_status rd_debug_import_kv(rd_model* m, int32_t seq, int32_t layer,
                                         size_t bytes, int32_t pos) {
     rd_status st = check_model(m);
     if (st) return st;
-    if (!src || seq != 0 || layer < 0 || layer >= m->d.L || which < 0 || which > 1 || pos < 0 ||
-        pos > m->opt.max_context)
+    if (!src || seq < 0 || seq >= m->opt.max_batch || layer < 0 || layer >= m->d.L || which < 0 || which > 1 ||
+        pos < 0 || pos > m->opt.max_context)
         return fail(RD_ERR_INVALID_ARG, "bad import arguments");
     KvRegion r[3];
-    const int nr = kv_regions(m, layer, which, r);
+    const int nr = kv_regions(m, seq, layer, which, r);
     size_t total = 0;
     for (int i = 0; i < nr; ++i) total += r[i].bytes;
     if (bytes != total) return fail(RD_ERR_INVALID_ARG, "source must be exactly " + std::to_string(total) + " bytes");

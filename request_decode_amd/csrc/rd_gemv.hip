@@ -113,9 +113,12 @@ typedef _Float16 hv8 __attribute__((ext_vector_type(8)));
 typedef float fv4 __attribute__((ext_vector_type(4)));
 constexpr int B8_SMAX = 16;   // 64-column steps per unit (x operand registers)
 
-template <int KS, int T, int U>
-__global__ __launch_bounds__(T) void k_gemv_b8(const _Float16* __restrict__ W, const _Float16* __restrict__ x,
-                                               float* __restrict__ y, int N, int K) {
+// x: B rows of K, row stride ldx, fp16 or (XF32) fp32 converted to fp16 as it
+// is loaded; y: B rows of N, row stride ldy, written or (ACC) added to.
+// Rows B..15 of the MFMA tile are zero.
+template <int KS, int T, int U, bool XF32, bool ACC>
+__global__ __launch_bounds__(T) void k_gemm_b8(const _Float16* __restrict__ W, const void* __restrict__ xv, int ldx,
+                                               float* __restrict__ y, int ldy, int N, int K, int B) {
     extern __shared__ __attribute__((aligned(16))) char s_lds[];   // [T/64][U][2 KiB] ring, [T/64][64] fv4
     constexpr int NWV = T / WAVE, BPG = NWV / KS;
     const int wid = wave_id(), lane = lane_id();
@@ -126,12 +129,31 @@ __global__ __launch_bounds__(T) void k_gemv_b8(const _Float16* __restrict__ W, c
     const int nsteps = K / 64, part = wid % KS;
     const int s_beg = part * nsteps / KS, ns = (part + 1) * nsteps / KS - s_beg;   // ns <= B8_SMAX
     u4v xa[B8_SMAX][2];
+    const int xr = n < B ? n : 0;
 #pragma unroll
     for (int t = 0; t < B8_SMAX; ++t) {
-        const bool ok = t < ns && n < 8;
-        const _Float16* xp = x + (size_t)(n & 7) * K + (s_beg + t) * 64 + 8 * q;
-        xa[t][0] = ok ? ld16(xp) : u4v{0u, 0u, 0u, 0u};
-        xa[t][1] = ok ? ld16(xp + 32) : u4v{0u, 0u, 0u, 0u};
+        const bool ok = t < ns && n < B;
+        const size_t c0 = (size_t)xr * ldx + (s_beg + t) * 64 + 8 * q;
+        if constexpr (XF32) {
+            const float* xp = reinterpret_cast<const float*>(xv) + c0;
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+                h8 v;
+                if (ok) {
+                    const float4 a = *reinterpret_cast<const float4*>(xp + 32 * hlf);
+                    const float4 b = *reinterpret_cast<const float4*>(xp + 32 * hlf + 4);
+                    v = h8{(_Float16)a.x, (_Float16)a.y, (_Float16)a.z, (_Float16)a.w,
+                           (_Float16)b.x, (_Float16)b.y, (_Float16)b.z, (_Float16)b.w};
+                } else {
+                    v = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                }
+                xa[t][hlf] = __builtin_bit_cast(u4v, v);
+            }
+        } else {
+            const _Float16* xp = reinterpret_cast<const _Float16*>(xv) + c0;
+            xa[t][0] = ok ? ld16(xp) : u4v{0u, 0u, 0u, 0u};
+            xa[t][1] = ok ? ld16(xp + 32) : u4v{0u, 0u, 0u, 0u};
+        }
     }
     const int lr = lane / 8, lc = (lane % 8) ^ lr;
     const int rd0 = (n / 8) * 1024 + (n % 8) * 128 + (q ^ (n % 8)) * 16;
@@ -181,25 +203,38 @@ __global__ __launch_bounds__(T) void k_gemv_b8(const _Float16* __restrict__ W, c
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int ob = 4 * q + j;
-                if (ob < 8 && on < N) y[(size_t)ob * N + on] = acc[j];
+                if (ob < B && on < N) {
+                    if constexpr (ACC) y[(size_t)ob * ldy + on] += acc[j];
+                    else y[(size_t)ob * ldy + on] = acc[j];
+                }
             }
         }
     }
 }
 
-template <int KS, int T, int U>
-hipError_t launch_b8(const _Float16* W, const _Float16* x, float* y, int N, int K, int gmul, int ncu, hipStream_t s) {
+template <int KS, int T, int U, bool XF32, bool ACC>
+hipError_t launch_b8(const _Float16* W, const void* x, int ldx, float* y, int ldy, int N, int K, int B, int gmul,
+                     int ncu, hipStream_t s) {
     const size_t lds = (size_t)(T / WAVE) * U * 2048 + (T / WAVE) * 1024;
     static bool attr_set = false;   // the attribute is per function, the same value every time
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)&k_gemv_b8<KS, T, U>,
+        hipError_t e = hipFuncSetAttribute((const void*)&k_gemm_b8<KS, T, U, XF32, ACC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int nblk = (N + 15) / 16, ngrp = (nblk * KS + T / WAVE - 1) / (T / WAVE);
-    hipLaunchKernelGGL((k_gemv_b8<KS, T, U>), dim3(std::min(ngrp, gmul * ncu)), dim3(T), lds, s, W, x, y, N, K);
+    hipLaunchKernelGGL((k_gemm_b8<KS, T, U, XF32, ACC>), dim3(std::min(ngrp, gmul * ncu)), dim3(T), lds, s, W, x,
+                       ldx, y, ldy, N, K, B);
     return hipGetLastError();
+}
+template <bool XF32, bool ACC>
+hipError_t launch_b8_k(const _Float16* W, const void* x, int ldx, float* y, int ldy, int N, int K, int B, int ncu,
+                       hipStream_t s) {
+    // K <= 4096: 4 parts of <= 16 steps, 4-wave workgroups, 4 per CU;
+    // K <= 8192: 8 parts, 8-wave workgroups, one per CU.
+    if (K <= 4096) return launch_b8<4, 256, 4, XF32, ACC>(W, x, ldx, y, ldy, N, K, B, 4, ncu, s);
+    return launch_b8<8, 512, 6, XF32, ACC>(W, x, ldx, y, ldy, N, K, B, 1, ncu, s);
 }
 
 }  // namespace
@@ -208,11 +243,8 @@ hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K,
     const auto* Wh = (const _Float16*)W;
     const auto* xh = (const _Float16*)x;
     if (batch == 8) {
-        // K <= 4096: 4 parts of <= 16 steps, 4-wave workgroups, 4 per CU;
-        // K <= 8192: 8 parts, 8-wave workgroups, one per CU.
         if (K % 64 || K > 8192) return hipErrorInvalidValue;
-        if (K <= 4096) return launch_b8<4, 256, 4>(Wh, xh, y, N, K, 4, ncu, s);
-        return launch_b8<8, 512, 6>(Wh, xh, y, N, K, 1, ncu, s);
+        return launch_b8_k<false, false>(Wh, x, K, y, N, N, K, 8, ncu, s);
     }
     if (batch != 1) return hipErrorInvalidValue;
     const int kch = kch_for(K);
@@ -228,6 +260,15 @@ hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K,
     }
 #undef RD_B1
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_b8(const _Float16* W, const void* x, bool x_f32, int ldx, float* y, int ldy, bool acc, int N,
+                          int K, int B, int ncu, hipStream_t s) {
+    if (K % 64 || K > 8192 || B < 1 || B > 8) return hipErrorInvalidValue;
+    if (x_f32) return acc ? launch_b8_k<true, true>(W, x, ldx, y, ldy, N, K, B, ncu, s)
+                          : launch_b8_k<true, false>(W, x, ldx, y, ldy, N, K, B, ncu, s);
+    return acc ? launch_b8_k<false, true>(W, x, ldx, y, ldy, N, K, B, ncu, s)
+               : launch_b8_k<false, false>(W, x, ldx, y, ldy, N, K, B, ncu, s);
 }
 
 }  // namespace rd

@@ -48,11 +48,42 @@ struct AttnArgs {
     const int* pos_ptr;      // L = *pos_ptr + 1
     int ld, nseg, H, Hk, S;
     float scale;
+    // B sequences (grid dimension y): sequence b's q, out, part and cache
+    // regions lie b strides past sequence 0's (strides in elements of each
+    // buffer, the cache ones in bytes)
+    int nseq;
+    size_t q_bstride, part_bstride, kv_bstride, st_bstride, meta_bstride;
 };
+// Sequence b's view of the attention arguments.
+__host__ __device__ inline AttnArgs attn_seq(AttnArgs T, int b) {
+    T.q += (size_t)b * T.q_bstride;
+    T.out += (size_t)b * T.q_bstride;
+    T.part += (size_t)b * T.part_bstride;
+    T.kc = reinterpret_cast<const uint8_t*>(T.kc) + (size_t)b * T.kv_bstride;
+    T.vc = reinterpret_cast<const uint8_t*>(T.vc) + (size_t)b * T.kv_bstride;
+    T.kcw = reinterpret_cast<uint8_t*>(T.kcw) + (size_t)b * T.kv_bstride;
+    T.vcw = reinterpret_cast<uint8_t*>(T.vcw) + (size_t)b * T.kv_bstride;
+    if (T.kst) {
+        T.kst += (size_t)b * T.st_bstride;
+        T.vst += (size_t)b * T.st_bstride;
+        T.kmeta += (size_t)b * T.meta_bstride;
+        T.vmeta += (size_t)b * T.meta_bstride;
+    }
+    return T;
+}
 
 struct StepArgs {
     int D, H, Hk, hd, F, V, max_ctx, S, kvfmt, n_layers;
     float eps, scale;
+    // batch: B sequences in lockstep (B > 1: kernel-per-phase executors only).
+    // Activation buffers hold B rows; sequence b's cache regions lie b
+    // strides past sequence 0's.
+    int B, ncu;
+    size_t kv_bstride;       // bytes of one sequence's K (or V) cache
+    size_t st_bstride;       // INT8: elements of one sequence's staging rows
+    size_t meta_bstride;     // INT8: floats of one sequence's (scale, zp) table
+    float* y;                // B > 1: [B][max(Nqkv, 2F)] GEMM outputs
+    _Float16* xh;            // B > 1: [B][D] normalised inputs of the QKV and gate/up GEMMs
     const _Float16* embed;
     const _Float16* g_final;
     const _Float16* lm_head;
@@ -110,6 +141,12 @@ __host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
     T.Hk = A.Hk;
     T.S = A.S;
     T.scale = A.scale;
+    T.nseq = A.B;
+    T.q_bstride = (size_t)A.H * A.hd;
+    T.part_bstride = (size_t)A.H * A.S * (A.hd + 2);
+    T.kv_bstride = A.kv_bstride;
+    T.st_bstride = A.st_bstride;
+    T.meta_bstride = A.meta_bstride;
     return T;
 }
 
@@ -144,6 +181,12 @@ int kch_for(int K);
 hipError_t launch_step(const StepArgs& A, hipStream_t s);
 hipError_t launch_phase(const StepArgs& A, int phase, int layer, hipStream_t s);
 hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K, int batch, int ncu, hipStream_t s);
+// Y[b][n] (=|+=) sum_k W[n][k] x[b][k] for b < B <= 8 on the matrix cores; x fp16 or fp32 (row stride ldx),
+// y fp32 (row stride ldy); K % 64 == 0, K <= 8192.
+hipError_t launch_step_batch(const StepArgs& A, hipStream_t s);
+hipError_t launch_attn_any(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s);
+hipError_t launch_gemm_b8(const _Float16* W, const void* x, bool x_f32, int ldx, float* y, int ldy, bool acc, int N,
+                          int K, int B, int ncu, hipStream_t s);
 hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s);
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,

@@ -67,8 +67,9 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
 // The wave reads each K/V row of its key range once for all G query heads of
 // the group.  Tasks past the splits in use at this position exit at once.
 template <int HD, int G, int KVF>
-__global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T) {
+__global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
     using Geo = AttnGeo<HD>;
+    const AttnArgs T = attn_seq(T0, blockIdx.y);   // sequence blockIdx.y
     constexpr int NW = ATT_WAVES;
     __shared__ float s_att[NW * G * (HD + 2)];
     const int pos = *T.pos_ptr, L = pos + 1;
@@ -114,8 +115,9 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T) {
 // step that fills an INT8 segment the first merge wave of each kv-head seals
 // it (after every split of this step has read the open segment).
 template <int HD, int G, int KVF>
-__global__ __launch_bounds__(WG) void k_merge(AttnArgs T) {
+__global__ __launch_bounds__(WG) void k_merge(AttnArgs T0) {
     using Geo = AttnGeo<HD>;
+    const AttnArgs T = attn_seq(T0, blockIdx.y);   // sequence blockIdx.y
     const int pos = *T.pos_ptr;
     int chunk, nact;
     split_plan(pos + 1, T.S, chunk, nact);
@@ -278,8 +280,9 @@ namespace {
 template <int KVF>
 hipError_t launch_attn_t(const AttnArgs& A, int hd, int G, hipStream_t s) {
     const int wpb = WG / WAVE;
-    dim3 grid(A.Hk * A.S), ablock(ATT_WAVES * WAVE), block(WG);   // k_attn: one split per workgroup
-    dim3 mgrid((A.H * (hd / 64) + wpb - 1) / wpb);
+    const int nseq = A.nseq > 1 ? A.nseq : 1;
+    dim3 grid(A.Hk * A.S, nseq), ablock(ATT_WAVES * WAVE), block(WG);   // k_attn: one split per workgroup
+    dim3 mgrid((A.H * (hd / 64) + wpb - 1) / wpb, nseq);
 #define RD_ATT(HDv, Gv)                                                        \
     if (hd == HDv && G == Gv) {                                                \
         hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, ablock, 0, s, A);     \
@@ -292,14 +295,6 @@ hipError_t launch_attn_t(const AttnArgs& A, int hd, int G, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_any(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s) {
-    switch (kvfmt) {
-        case KV_FP16: return launch_attn_t<KV_FP16>(A, hd, G, s);
-        case KV_E5M2: return launch_attn_t<KV_E5M2>(A, hd, G, s);
-        case KV_INT8: return launch_attn_t<KV_INT8>(A, hd, G, s);
-    }
-    return hipErrorInvalidValue;
-}
 
 template <bool EMB>
 hipError_t launch_qkv(const StepArgs& A, const LayerW& Lw, int layer, hipStream_t s) {
@@ -329,6 +324,15 @@ hipError_t launch_resid(const float* in, int K, const _Float16* W, float* x, int
 }
 
 }  // namespace
+
+hipError_t launch_attn_any(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s) {
+    switch (kvfmt) {
+        case KV_FP16: return launch_attn_t<KV_FP16>(A, hd, G, s);
+        case KV_E5M2: return launch_attn_t<KV_E5M2>(A, hd, G, s);
+        case KV_INT8: return launch_attn_t<KV_INT8>(A, hd, G, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 int lm_head_workgroups(int V) { return (V + 4 * LM_ROWS - 1) / (4 * LM_ROWS); }
 
@@ -367,6 +371,7 @@ hipError_t launch_phase(const StepArgs& A, int phase, int layer, hipStream_t s) 
 }
 
 hipError_t launch_step(const StepArgs& A, hipStream_t s) {
+    if (A.B > 1) return launch_step_batch(A, s);
     for (int l = 0; l < A.n_layers; ++l)
         for (int ph = 0; ph < 5; ++ph) {
             hipError_t e = launch_layer_phase(A, ph, l, l == 0, s);

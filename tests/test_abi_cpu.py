@@ -76,7 +76,9 @@ def test_blob_validation_on_host(rd):
 def test_option_validation_on_host(rd):
     blob = synth.make_blob(synth.SHAPES["tiny"], seed=1)
     assert _create(rd, blob, max_context=0)[0] == rd.RD_ERR_INVALID_ARG
-    assert _create(rd, blob, max_batch=2)[0] == rd.RD_ERR_UNSUPPORTED
+    assert _create(rd, blob, max_batch=9)[0] == rd.RD_ERR_UNSUPPORTED
+    assert _create(rd, blob, max_batch=0)[0] == rd.RD_ERR_UNSUPPORTED
+    assert _create(rd, blob, max_batch=8, executor=3)[0] == rd.RD_ERR_UNSUPPORTED   # persistent: batch 1
     assert _create(rd, blob, kv_format=7)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, executor=9)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, attn_splits=1000)[0] == rd.RD_ERR_INVALID_ARG

@@ -249,6 +249,13 @@ def test_2b_short_teacher_forced(rd, orc, blob2b, executor):
     print(f"2b short {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
 
 
+def test_2b_batch8_short_teacher_forced(rd, orc, blob2b):
+    # the 2B model's batch-8 step: 8 prompts of 6 tokens, then 3 greedy steps
+    prompts = synth.prompts(115, 6, synth.SHAPES["2b"].vocab, 8)
+    worst, graded, n = teacher_forced_batch(rd, orc, blob2b, prompts, 3)
+    print(f"2b batch 8: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+
+
 @pytest.mark.parametrize("executor", ["graph", "persistent"])
 def test_2b_full_size_sampled(rd, orc, blob2b, executor):
     """The 512-token prompt + 256 greedy steps run at full size; the oracle
@@ -289,3 +296,84 @@ def test_2b_full_size_sampled(rd, orc, blob2b, executor):
     print(f"2b full: last-step max|dlogit|={e:.3e} gradeable={gr}")
     gm.close()
     om.close()
+
+
+# ---- batch B: B sequences in lockstep (thin-GEMM step) ---------------------------------
+
+def teacher_forced_batch(rd, orc, blob, prompts, n_decode, kv="fp16", executor="graph"):
+    """Each of the B sequences fed its own prompt, then the oracle's greedy
+    tokens; every step's B rows of logits compared with the oracle's batch
+    step (same rule as batch 1)."""
+    B, n_prompt = prompts.shape
+    max_ctx = n_prompt + n_decode + 8
+    om = orc.OracleModel(blob, max_ctx, batch=B, kv_format=kv)
+    gm = rd.Model(blob, max_context=max_ctx, kv_format=kv, executor=executor, batch=B)
+    toks = prompts.T.copy()          # [step][B]
+    worst, graded, n = 0.0, 0, 0
+    for i in range(n_prompt + n_decode):
+        t = toks[i] if i < n_prompt else nxt_o
+        ol, on = om.step(t)
+        gl, gn = gm.decode_step(t)
+        for b in range(B):
+            e, gr = compare_step(gl[b], ol[b], int(gn[b]), (kv, executor, B, i, b))
+            worst = max(worst, e)
+            graded += gr
+        nxt_o = on.astype(np.int32)
+        n += 1
+    assert gm.position() == om.pos() == n_prompt + n_decode
+    gm.close()
+    om.close()
+    return worst, graded, n
+
+
+@pytest.mark.parametrize("executor", ["eager", "graph"])
+@pytest.mark.parametrize("B", [8, 3])
+def test_batch_tiny_teacher_forced(rd, orc, executor, B):
+    shape = synth.SHAPES["tiny"]
+    blob = synth.make_blob(shape, seed=1)
+    prompts = synth.prompts(111, 24, shape.vocab, B)
+    worst, graded, n = teacher_forced_batch(rd, orc, blob, prompts, 16, executor=executor)
+    print(f"tiny batch {B} {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+    assert graded > 0
+
+
+@pytest.mark.parametrize("kv", ["e5m2", "int8"])
+def test_batch_quantized_kv_teacher_forced(rd, orc, kv):
+    shape = synth.SHAPES["tiny"]
+    blob = synth.make_blob(shape, seed=1)
+    prompts = synth.prompts(112, 140, shape.vocab, 8)   # crosses an INT8 segment seal
+    worst, graded, n = teacher_forced_batch(rd, orc, blob, prompts, 8, kv=kv)
+    print(f"tiny batch 8 {kv}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+
+
+def test_batch_gqa_teacher_forced(rd, orc):
+    blob = synth.make_blob(GQA2, seed=7)
+    prompts = synth.prompts(113, 40, GQA2.vocab, 8)
+    worst, graded, n = teacher_forced_batch(rd, orc, blob, prompts, 12)
+    print(f"gqa2 batch 8: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+
+
+def test_batch_prefill_generate_match_steps(rd):
+    # rd_prefill and rd_generate at batch 8 are the same steps as single
+    # decode_step calls: same tokens, same logits and caches afterwards.
+    shape = synth.SHAPES["tiny"]
+    blob = synth.make_blob(shape, seed=1)
+    prompts = synth.prompts(114, 30, shape.vocab, 8)
+    a = rd.Model(blob, max_context=64, executor="graph", batch=8)
+    b = rd.Model(blob, max_context=64, executor="graph", batch=8)
+    for i in range(29):
+        a.decode_step(prompts[:, i], want_logits=False)
+    b.prefill(prompts[:, :29].T)
+    first = prompts[:, 29]
+    gen = b.generate(first, 10)
+    t = first
+    for i in range(10):
+        _, t = a.decode_step(t, want_logits=False)
+        assert np.array_equal(t, gen[i]), i
+    assert a.position() == b.position() == 39
+    for seq in (0, 5):
+        assert np.array_equal(a.export_kv(0, 0, seq)["rows"], b.export_kv(0, 0, seq)["rows"])
+    with pytest.raises(rd.RdError):
+        rd.Model(blob, max_context=64, executor="persistent", batch=8)
+    a.close()
+    b.close()
