@@ -137,6 +137,9 @@ __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
     return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
 }
 __device__ __forceinline__ void publish(uint64_t* p, float v, uint32_t tag) { st_agent(p, tagged(v, tag)); }
+__device__ __forceinline__ void publish_bits(uint64_t* p, uint32_t v, uint32_t tag) {
+    st_agent(p, ((uint64_t)tag << 32) | (uint64_t)v);
+}
 __device__ __forceinline__ uint32_t tag_of(const StepArgs& A, const PersistArgs& P, int step, int layer) {
     return P.tag0 + (uint32_t)step * (uint32_t)(A.n_layers + 1) + (uint32_t)layer + 1u;
 }
@@ -204,6 +207,25 @@ __device__ __forceinline__ void poll_vec(Waiter& wt, const uint64_t* buf, int K,
     for (int c = 0; c < KCH; ++c)
 #pragma unroll
         for (int i = 0; i < 8; ++i) xr[c][i] = val[c * 8 + i];
+}
+
+// The same for a vector published as fp16 pairs (word w: elements 2w, 2w+1):
+// the lane's 8 elements of chunk c are 4 consecutive words.
+template <int KCH>
+__device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int K, uint32_t tag,
+                                            float (&xr)[KCH][8]) {
+    const int lane = lane_id();
+    float val[KCH * 4];
+    auto word = [&](int k) { return ((k / 4) * 64 + lane) * 4 + k % 4; };
+    poll_words<KCH * 4>(wt, buf, word, [&](int k) { return 2 * word(k) < K; }, tag, val);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t u = __float_as_uint(val[c * 4 + i]);
+            xr[c][2 * i] = h_bits2f((uint16_t)(u & 0xffffu));
+            xr[c][2 * i + 1] = h_bits2f((uint16_t)(u >> 16));
+        }
 }
 
 template <int KCH>
@@ -306,7 +328,9 @@ __device__ __forceinline__ PhaseGeo phase_geo(const StepArgs& A, const PersistAr
                 wg_rows((A.H + 2 * A.Hk) * A.hd, 2, g.r0, g.r1);
                 break;
             case 1: g.W = layer_w(P, P.layer0.wo, l); g.K = A.H * A.hd; g.kch = KA; wg_rows(A.D, 1, g.r0, g.r1); break;
-            case 2: g.W = layer_w(P, P.layer0.wgu, l); g.K = A.D; g.kch = KD; wg_rows(2 * A.F, 2, g.r0, g.r1); break;
+            // gate/up in tasks of 4 rows: each workgroup's SwiGLU outputs are
+            // whole fp16 pairs of the exchange
+            case 2: g.W = layer_w(P, P.layer0.wgu, l); g.K = A.D; g.kch = KD; wg_rows(2 * A.F, 4, g.r0, g.r1); break;
             default: g.W = layer_w(P, P.layer0.wd, l); g.K = A.F; g.kch = KF; wg_rows(A.D, 1, g.r0, g.r1); break;
         }
     }
@@ -843,13 +867,16 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             lds_barrier();
             lds_barrier();
             TR(40 + TR_DONE);
-            for (int q = lane; 2 * q < gr1 - gr0; q += WAVE)
-                publish(&A.mb[gr0 / 2 + q], silu_mul(s_part[2 * q], s_part[2 * q + 1]), tag);
+            // m[i], m[i+1] as one fp16 pair per word (gr0 % 4 == 0)
+            for (int q = lane; 4 * q < gr1 - gr0; q += WAVE)
+                publish_bits(&A.mb[gr0 / 4 + q],
+                             pack_h2(silu_mul(s_part[4 * q], s_part[4 * q + 1]),
+                                     silu_mul(s_part[4 * q + 2], s_part[4 * q + 3])), tag);
             TR(40 + TR_PUB);
             // ---------------- down projection + residual ----------------
             {
                 float xr[KF][8];
-                poll_vec<KF>(wt, A.mb, A.F, tag, xr);
+                poll_vec_h2<KF>(wt, A.mb, A.F, tag, xr);
                 TR(50 + TR_RECV);
                 regs_to_lds<KF>(s_r, A.F, xr);
             }

@@ -141,7 +141,15 @@ __device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const float (&
         out[r] = ((readlane_f(v[r], 0) + readlane_f(v[r], 16)) + readlane_f(v[r], 32)) + readlane_f(v[r], 48);
 }
 
-__device__ __forceinline__ float silu_mul(float gt, float up) { return gt / (1.0f + expf(-gt)) * up; }
+// SwiGLU output m = silu(gate) * up, rounded to fp16 (nearest even): the
+// precision the down projection takes it in, in every executor (the
+// persistent one exchanges it as fp16 pairs).
+__device__ __forceinline__ float silu_mul(float gt, float up) {
+    return (float)(_Float16)(gt / (1.0f + expf(-gt)) * up);
+}
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)f2h_bits(lo) | ((uint32_t)f2h_bits(hi) << 16);
+}
 
 // ============================================================================
 // QKV epilogue: RoPE on a (j, j+hd/2) pair and the KV-cache append
