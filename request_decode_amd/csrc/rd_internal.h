@@ -105,13 +105,14 @@ struct StepArgs {
     uint16_t* stage;         // INT8: [n_layers][2][Hk][128][hd]
     float* meta;             // INT8: [n_layers][2][Hk][nseg][2]
     int nseg;
-    // exchange words of the persistent executor: (tag << 32) | fp32 bits
-    uint64_t* xb1;           // [D] residual stream after the down projection
-    uint64_t* xb2;           // [D] residual stream after the output projection
+    // exchange words of the persistent executor: (tag << 32) | payload, the
+    // payload fp32 bits or, for "pairs", elements (2w, 2w+1) as two fp16
+    uint64_t* xb1;           // [D/2 pairs] residual stream after the down projection
+    uint64_t* xb2;           // [D/2 pairs] residual stream after the output projection
     uint64_t* qb;            // [(H+2Hk)*hd] rotated q, then the new K and V rows as stored
     uint64_t* pb;            // [H][S][hd+2] attention split partials
-    uint64_t* ab;            // [H*hd] attention output
-    uint64_t* mb;            // [F] SwiGLU output
+    uint64_t* ab;            // [H*hd/2 pairs] attention output
+    uint64_t* mb;            // [F/2 pairs] SwiGLU output
     uint64_t* lb;            // [workgroups] argmax: (value bits << 32) | (index << 12) | tag12
     int* abort_word;         // set when a wait of the persistent kernel gives up
 };

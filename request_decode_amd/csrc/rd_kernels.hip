@@ -44,7 +44,7 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
         if (blockIdx.x == 0)
             for (int i = threadIdx.x; i < D; i += WG) A.x[i] = (float)e[i];
     } else {
-        load_x_f32<KCH>(A.x, D, xr);
+        load_x_f32_h<KCH>(A.x, D, xr);
     }
     rmsnorm_regs<KCH>(xr, Lw.g_attn, D, A.eps);
     if (row0 >= N) return;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(WG) void k_resid(const float* __restrict__ in, int 
     u4v w[R][KCH];
     load_rows<R, KCH>(W, K, row0, max(0, min(R, N - row0)), w);
     float xr[KCH][8];
-    load_x_f32<KCH>(in, K, xr);
+    load_x_f32_h<KCH>(in, K, xr);
     if (row0 >= N) return;
     float acc[R];
     dot_rows<R, KCH>(w, xr, acc);
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(WG) void k_gateup(StepArgs A, LayerW Lw) {
     u4v w[2][KCH];
     load_rows<2, KCH>(Lw.wgu, A.D, row0, row0 < 2 * A.F ? 2 : 0, w);
     float xr[KCH][8];
-    load_x_f32<KCH>(A.x, A.D, xr);
+    load_x_f32_h<KCH>(A.x, A.D, xr);
     rmsnorm_regs<KCH>(xr, Lw.g_ffn, A.D, A.eps);
     if (row0 >= 2 * A.F) return;
     float acc[2];
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
     u4v wa[4][KCH], wb[4][KCH];
     load_rows<4, KCH>(A.lm_head, A.D, rbeg, max(0, min(4, rend - rbeg)), wa);
     float xr[KCH][8];
-    load_x_f32<KCH>(A.x, A.D, xr);
+    load_x_f32_h<KCH>(A.x, A.D, xr);
     rmsnorm_regs<KCH>(xr, A.g_final, A.D, A.eps);
     Best b{-INFINITY, INT_MAX};
     auto consume = [&](const u4v (&w)[4][KCH], int r0) {

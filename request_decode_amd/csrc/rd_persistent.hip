@@ -327,11 +327,12 @@ __device__ __forceinline__ PhaseGeo phase_geo(const StepArgs& A, const PersistAr
                 g.W = layer_w(P, P.layer0.wqkv, l); g.K = A.D; g.kch = KD;
                 wg_rows((A.H + 2 * A.Hk) * A.hd, 2, g.r0, g.r1);
                 break;
-            case 1: g.W = layer_w(P, P.layer0.wo, l); g.K = A.H * A.hd; g.kch = KA; wg_rows(A.D, 1, g.r0, g.r1); break;
+            // O and down: owned residual rows in pairs (published as fp16 pairs)
+            case 1: g.W = layer_w(P, P.layer0.wo, l); g.K = A.H * A.hd; g.kch = KA; wg_rows(A.D, 2, g.r0, g.r1); break;
             // gate/up in tasks of 4 rows: each workgroup's SwiGLU outputs are
             // whole fp16 pairs of the exchange
             case 2: g.W = layer_w(P, P.layer0.wgu, l); g.K = A.D; g.kch = KD; wg_rows(2 * A.F, 4, g.r0, g.r1); break;
-            default: g.W = layer_w(P, P.layer0.wd, l); g.K = A.F; g.kch = KF; wg_rows(A.D, 1, g.r0, g.r1); break;
+            default: g.W = layer_w(P, P.layer0.wd, l); g.K = A.F; g.kch = KF; wg_rows(A.D, 2, g.r0, g.r1); break;
         }
     }
     return g;
@@ -726,7 +727,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                     load_x_f16<KD>(e, A.D, xr);
                     for (int i = lane; i < dr1 - dr0; i += WAVE) s_own[i] = (float)e[dr0 + i];
                 } else {
-                    poll_vec<KD>(wt, A.xb1, A.D, tag_of(A, P, step, l - 1), xr);
+                    poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, l - 1), xr);
                 }
                 TR(0 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
@@ -830,7 +831,9 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 for (int k = 0; k < 64; ++k) ov[k] = k < SMAX ? val[k] : 0.f;
                 float num = 0.f;
                 merge_acc<SMAX>(num, 0, mw, ov);
-                publish(&A.ab[hm * HD + mpart * 64 + lane], num / mw.den, tag);
+                // dims (d, d+1) as one fp16 pair per word
+                const float av = num / mw.den, av1 = __shfl_down(av, 1, WAVE);
+                if ((lane & 1) == 0) publish_bits(&A.ab[(hm * HD + mpart * 64 + lane) / 2], pack_h2(av, av1), tag);
                 if constexpr (KVF == KV_INT8) {
                     if ((pos + 1) % SEG == 0 && mpart == 0 && hm % G == 0) {
                         seal_head<HD, true>(T, hm / G, pos);
@@ -842,24 +845,25 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // ---------------- output projection + residual ----------------
             {
                 float xr[KA][8];
-                poll_vec<KA>(wt, A.ab, A.H * HD, tag, xr);
+                poll_vec_h2<KA>(wt, A.ab, A.H * HD, tag, xr);
                 TR(30 + TR_RECV);
                 regs_to_lds<KA>(s_r, A.H * HD, xr);
             }
             lds_barrier();
             lds_barrier();
             TR(30 + TR_DONE);
-            for (int i = lane; i < dr1 - dr0; i += WAVE) {
-                const float xn = s_own[i] + s_part[i];
-                s_own[i] = xn;
-                publish(&A.xb2[dr0 + i], xn, tag);
+            for (int q = lane; 2 * q < dr1 - dr0; q += WAVE) {   // (dr1 - dr0) even
+                const float x0 = s_own[2 * q] + s_part[2 * q], x1 = s_own[2 * q + 1] + s_part[2 * q + 1];
+                s_own[2 * q] = x0;
+                s_own[2 * q + 1] = x1;
+                publish_bits(&A.xb2[dr0 / 2 + q], pack_h2(x0, x1), tag);
             }
             TR(30 + TR_PUB);
             load_gain<KD>(layer_w(P, P.layer0.g_ffn, l), A.D, gain);
             // ---------------- RMSNorm + gate/up + SwiGLU ----------------
             {
                 float xr[KD][8];
-                poll_vec<KD>(wt, A.xb2, A.D, tag, xr);
+                poll_vec_h2<KD>(wt, A.xb2, A.D, tag, xr);
                 TR(40 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
                 regs_to_lds<KD>(s_r, A.D, xr);
@@ -886,10 +890,11 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // This layer's cache rows are stored (acknowledged) before the
             // residual stream that every later reader depends on is published.
             drain_vmem();
-            for (int i = lane; i < dr1 - dr0; i += WAVE) {
-                const float xn = s_own[i] + s_part[i];
-                s_own[i] = xn;
-                publish(&A.xb1[dr0 + i], xn, tag);
+            for (int q = lane; 2 * q < dr1 - dr0; q += WAVE) {
+                const float x0 = s_own[2 * q] + s_part[2 * q], x1 = s_own[2 * q + 1] + s_part[2 * q + 1];
+                s_own[2 * q] = x0;
+                s_own[2 * q + 1] = x1;
+                publish_bits(&A.xb1[dr0 / 2 + q], pack_h2(x0, x1), tag);
             }
             TR(50 + TR_PUB);
             load_gain<KD>(l + 1 < NL ? layer_w(P, P.layer0.g_attn, l + 1) : A.g_final, A.D, gain);
@@ -897,7 +902,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
         // ---------------- final RMSNorm + LM head + argmax ----------------
         {
             float xr[KD][8];
-            poll_vec<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), xr);
+            poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), xr);
             TR(60 + TR_RECV);
             rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
             regs_to_lds<KD>(s_r, A.D, xr);

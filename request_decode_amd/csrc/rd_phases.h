@@ -43,6 +43,18 @@ __device__ __forceinline__ void load_x_f32(const float* __restrict__ x, int K, f
     }
 }
 
+// The same, each element rounded to fp16 (nearest even): the precision in
+// which the GEMV inputs of the step travel between workgroups (the residual
+// stream itself stays fp32 where it is accumulated).
+template <int KCH>
+__device__ __forceinline__ void load_x_f32_h(const float* __restrict__ x, int K, float (&xr)[KCH][8]) {
+    load_x_f32<KCH>(x, K, xr);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xr[c][i] = (float)(_Float16)xr[c][i];
+}
+
 template <int KCH>
 __device__ __forceinline__ void load_x_f16(const _Float16* __restrict__ x, int K, float (&xr)[KCH][8]) {
     const int lane = lane_id();
