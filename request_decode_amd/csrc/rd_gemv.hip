@@ -20,35 +20,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 // ---- batch 1 ---------------------------------------------------------------------
-// dot_rows with x kept as fp16 in registers (8 halves per chunk): every
-// product and every addition is the one dot_rows makes with x widened to
-// fp32 first, in the same order, so the results are the same bits.
-template <int NR, int KCH>
-__device__ __forceinline__ void dot_rows_xh(const u4v (&w)[NR][KCH], const u4v (&xh)[KCH], float (&out)[NR]) {
-    float s0[NR], s1[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) s0[r] = s1[r] = 0.f;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-        const h8 xv = as_h8(xh[c]);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            const h8 hw = as_h8(w[r][c]);
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                s0[r] += (float)hw[i] * (float)xv[i];
-                s1[r] += (float)hw[i + 1] * (float)xv[i + 1];
-            }
-        }
-    }
-    float v[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = row16_sum(s0[r] + s1[r]);
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        out[r] = ((readlane_f(v[r], 0) + readlane_f(v[r], 16)) + readlane_f(v[r], 32)) + readlane_f(v[r], 48);
-}
-
 // Each workgroup owns a contiguous block of rows; its waves take NR rows at
 // a time, round robin, and keep NB groups of loads in registers: while one
 // group is reduced the next NB - 1 are in flight.  Launched with several
@@ -78,7 +49,7 @@ __global__ __launch_bounds__(GW) void k_gemv_b1(const _Float16* __restrict__ W, 
             const int r = r0 + ((j + b) * nw + wid) * NR;
             if (r >= r1) return;
             float acc[NR];
-            dot_rows_xh<NR, KCH>(w[b], xh, acc);
+            dot_rows<NR, KCH>(w[b], xh, acc);
             if (lane == 0)
 #pragma unroll
                 for (int i = 0; i < NR; ++i)

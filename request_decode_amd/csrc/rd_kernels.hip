@@ -48,8 +48,10 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
     }
     rmsnorm_regs<KCH>(xr, Lw.g_attn, D, A.eps);
     if (row0 >= N) return;
+    u4v xh[KCH];
+    pack_x<KCH>(xr, xh);
     float acc[2];
-    dot_rows<2, KCH>(w, xr, acc);
+    dot_rows<2, KCH>(w, xh, acc);
     if (lane == 0) {
         const QkvPair o = qkv_pair(A.hd, A.H, A.Hk, row0, acc[0], acc[1], A.rope + (size_t)pos * (A.hd / 2));
         if (o.kind == 0) {
@@ -158,10 +160,12 @@ __global__ __launch_bounds__(WG) void k_resid(const float* __restrict__ in, int 
     u4v w[R][KCH];
     load_rows<R, KCH>(W, K, row0, max(0, min(R, N - row0)), w);
     float xr[KCH][8];
-    load_x_f32_h<KCH>(in, K, xr);
+    load_x_f32<KCH>(in, K, xr);
     if (row0 >= N) return;
+    u4v xh[KCH];
+    pack_x<KCH>(xr, xh);
     float acc[R];
-    dot_rows<R, KCH>(w, xr, acc);
+    dot_rows<R, KCH>(w, xh, acc);
     if (lane == 0)
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -179,8 +183,10 @@ __global__ __launch_bounds__(WG) void k_gateup(StepArgs A, LayerW Lw) {
     load_x_f32_h<KCH>(A.x, A.D, xr);
     rmsnorm_regs<KCH>(xr, Lw.g_ffn, A.D, A.eps);
     if (row0 >= 2 * A.F) return;
+    u4v xh[KCH];
+    pack_x<KCH>(xr, xh);
     float acc[2];
-    dot_rows<2, KCH>(w, xr, acc);
+    dot_rows<2, KCH>(w, xh, acc);
     if (lane == 0) A.m[row0 >> 1] = silu_mul(acc[0], acc[1]);
 }
 
@@ -198,10 +204,12 @@ __global__ __launch_bounds__(WG) void k_lmhead(StepArgs A) {
     float xr[KCH][8];
     load_x_f32_h<KCH>(A.x, A.D, xr);
     rmsnorm_regs<KCH>(xr, A.g_final, A.D, A.eps);
+    u4v xh[KCH];
+    pack_x<KCH>(xr, xh);
     Best b{-INFINITY, INT_MAX};
     auto consume = [&](const u4v (&w)[4][KCH], int r0) {
         float acc[4];
-        dot_rows<4, KCH>(w, xr, acc);
+        dot_rows<4, KCH>(w, xh, acc);
         if (lane == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

@@ -54,7 +54,7 @@ typedef __attribute__((address_space(1))) void glb_void;
 constexpr int NSW = 3;                  // stream waves per workgroup (waves 1..3)
 constexpr int PWG = (NSW + 1) * WAVE;   // threads per workgroup
 constexpr int UNIT = 1024;              // bytes per ring slot: 16 per lane, one chunk of one row
-constexpr int RING = 40;                // ring slots per stream wave
+constexpr int RING = 47;                // ring slots per stream wave
 constexpr int PART_MAX = 512;           // row sums a workgroup holds per phase
 constexpr int OWN_MAX = 64;             // residual-stream rows a workgroup owns
 constexpr int LB_MAX = 1024;            // workgroups (argmax candidates)
@@ -228,17 +228,16 @@ __device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int
         }
 }
 
+// The GEMV operand of a phase into LDS for the stream waves: the fp16
+// rounding of the vector (pack_x), 16 bytes per lane and chunk at byte
+// (c*64 + lane)*16, zero past K.
 template <int KCH>
-__device__ __forceinline__ void regs_to_lds(float* s, int K, const float (&xr)[KCH][8]) {
+__device__ __forceinline__ void regs_to_lds(float* s, const float (&xr)[KCH][8]) {
     const int lane = lane_id();
+    u4v xh[KCH];
+    pack_x<KCH>(xr, xh);
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-        const int col = (c * 64 + lane) * 8;
-        if (col < K) {
-            *reinterpret_cast<float4*>(s + col) = make_float4(xr[c][0], xr[c][1], xr[c][2], xr[c][3]);
-            *reinterpret_cast<float4*>(s + col + 4) = make_float4(xr[c][4], xr[c][5], xr[c][6], xr[c][7]);
-        }
-    }
+    for (int c = 0; c < KCH; ++c) reinterpret_cast<u4v*>(s)[c * 64 + lane] = xh[c];
 }
 
 // ---- event trace -----------------------------------------------------------------
@@ -483,7 +482,7 @@ struct Feeder {
 // then the dot products of dot_rows.
 template <int NR, int KCH, bool FK, class F>
 __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const PersistArgs& P, int sw,
-                                             unsigned char* ring, const float (&xr)[KCH][8], int K,
+                                             unsigned char* ring, const u4v (&xh)[KCH], int K,
                                              float (&out)[NR]) {
     static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
     const int lane = lane_id();
@@ -511,7 +510,7 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
 #pragma unroll
                 for (int r = 0; r < NR; ++r) w[r][c] = u4v{0u, 0u, 0u, 0u};
     }
-    dot_rows<NR, KCH>(w, xr, out);
+    dot_rows<NR, KCH>(w, xh, out);
 }
 
 // A stream wave's share of GEMV phase ph, between the workgroup barriers
@@ -527,34 +526,19 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
     const int K = kind == 1 ? A.H * A.hd : kind == 3 ? A.F : A.D;
     const int ra = pick5(f.ra, kind), rb = ra + pick5(f.nr, kind), r0 = pick5(f.r0, kind);
     if (ra < rb) {
-        float xr[KCH][8];
-        {   // load_x_f32 from LDS, as asm (see lds_read_wait); columns >= K read
-            // lane 0's (in bounds) and are zeroed after
-            const int lane = lane_id();
-            unsigned ad[2 * KCH];
+        u4v xh[KCH];
+        {   // the fp16 operand from LDS (regs_to_lds), as asm (see lds_read_wait)
+            const unsigned base = lds_addr(s_r) + (unsigned)lane_id() * 16u;
+            unsigned ad[KCH];
 #pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const int col = (c * 64 + lane) * 8 < K ? (c * 64 + lane) * 8 : 0;
-                ad[2 * c] = lds_addr(s_r + col);
-                ad[2 * c + 1] = lds_addr(s_r + col + 4);
-            }
-            u4v xv[2 * KCH];
-            lds_read_wait<2 * KCH>(xv, ad);
-#pragma unroll
-            for (int c = 0; c < KCH; ++c) {
-                const bool in = (c * 64 + lane) * 8 < K;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xr[c][i] = in ? __uint_as_float(xv[2 * c][i]) : 0.f;
-                    xr[c][4 + i] = in ? __uint_as_float(xv[2 * c + 1][i]) : 0.f;
-                }
-            }
+            for (int c = 0; c < KCH; ++c) ad[c] = base + (unsigned)c * 1024u;
+            lds_read_wait<KCH>(xh, ad);
         }
         const unsigned sp = lds_addr(s_part);
         int r = ra;
         for (; r + NR <= rb; r += NR) {
             float v[NR];
-            consume_rows<NR, KCH, FK>(f, A, P, sw, ring, xr, K, v);
+            consume_rows<NR, KCH, FK>(f, A, P, sw, ring, xh, K, v);
             if (sw == 0 && r == ra) tr(101 + 10 * kind);
             if (lane_id() == 0)
 #pragma unroll
@@ -562,7 +546,7 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
         }
         if (r < rb) {
             float v[1];
-            consume_rows<1, KCH, FK>(f, A, P, sw, ring, xr, K, v);
+            consume_rows<1, KCH, FK>(f, A, P, sw, ring, xh, K, v);
             if (lane_id() == 0) lds_write4(sp + 4u * (unsigned)(r - r0), v[0]);
         }
     }
@@ -731,7 +715,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 }
                 TR(0 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
-                regs_to_lds<KD>(s_r, A.D, xr);
+                regs_to_lds<KD>(s_r, xr);
             }
             TR(0 + TR_STAGED);
             // (cos, sin) of the RoPE pair each lane rotates in the epilogue,
@@ -847,7 +831,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 float xr[KA][8];
                 poll_vec_h2<KA>(wt, A.ab, A.H * HD, tag, xr);
                 TR(30 + TR_RECV);
-                regs_to_lds<KA>(s_r, A.H * HD, xr);
+                regs_to_lds<KA>(s_r, xr);
             }
             lds_barrier();
             lds_barrier();
@@ -866,7 +850,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 poll_vec_h2<KD>(wt, A.xb2, A.D, tag, xr);
                 TR(40 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
-                regs_to_lds<KD>(s_r, A.D, xr);
+                regs_to_lds<KD>(s_r, xr);
             }
             lds_barrier();
             lds_barrier();
@@ -882,7 +866,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 float xr[KF][8];
                 poll_vec_h2<KF>(wt, A.mb, A.F, tag, xr);
                 TR(50 + TR_RECV);
-                regs_to_lds<KF>(s_r, A.F, xr);
+                regs_to_lds<KF>(s_r, xr);
             }
             lds_barrier();
             lds_barrier();
@@ -905,7 +889,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), xr);
             TR(60 + TR_RECV);
             rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
-            regs_to_lds<KD>(s_r, A.D, xr);
+            regs_to_lds<KD>(s_r, xr);
         }
         lds_barrier();
         lds_barrier();
@@ -984,7 +968,7 @@ template <int KD, int KA, int KF, int HD, int G, int KVF, bool FK, int SMAX>
 __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     constexpr int KIN = KF > KA ? (KF > KD ? KF : KD) : (KA > KD ? KA : KD);
     constexpr int NATT = attn_nq<HD, G>() * 64 + NWA * G * (HD + 2);
-    constexpr int NSR = KIN * 512 > NATT ? KIN * 512 : NATT;
+    constexpr int NSR = KIN * 256 > NATT ? KIN * 256 : NATT;   // fp16 GEMV operand: KIN KiB
     __shared__ __attribute__((aligned(16))) unsigned char s_ring[NSW * RING * UNIT];
     // the phase's GEMV input; between the QKV and O phases the attention exchange
     __shared__ __attribute__((aligned(16))) float s_r[NSR];
@@ -1115,8 +1099,11 @@ hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg) {
                               std::max(rows_per_wg(A.D, 1, n), rows_per_wg(A.V, 1, n)));
     // every attention task and merge task needs a workgroup of its own
     const int ntask = A.Hk * A.S, nmerge = A.H * (A.hd / 64);
+    // past its last row each stream wave keeps requesting the LM head from
+    // its first byte (up to RING chunks, plus a partial row): it must be that long
+    const bool lm_short = (size_t)A.V * A.D * 2 < (size_t)RING * UNIT + (size_t)A.D * 2;
     if (most > PART_MAX || rows_per_wg(A.D, 1, n) > OWN_MAX || n > LB_MAX || ntask > n || nmerge > n ||
-        A.V >= (1 << 20))
+        A.V >= (1 << 20) || lm_short)
         return hipErrorInvalidConfiguration;
     *nwg = n;
     return hipSuccess;

@@ -124,12 +124,27 @@ __device__ __forceinline__ void load_rows(const _Float16* __restrict__ W, int K,
         }
 }
 
-// out[r] = row r . x for NR loaded rows (columns past K already zero), the
-// same value in every lane.  Per lane: even and odd columns in two running
-// sums over the chunks in order; then the 16-lane DPP row sums and the four
-// rows in a fixed order.
+// The GEMV operand: the fp16 rounding (nearest even) of the register-resident
+// vector, 8 halves per chunk in one u4v (column order kept).
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)f2h_bits(lo) | ((uint32_t)f2h_bits(hi) << 16);
+}
+template <int KCH>
+__device__ __forceinline__ void pack_x(const float (&xr)[KCH][8], u4v (&xh)[KCH]) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xh[c][i] = pack_h2(xr[c][2 * i], xr[c][2 * i + 1]);
+}
+
+// out[r] = row r . x for NR loaded rows (columns past K already zero) and
+// the fp16 operand x, the same value in every lane.  Per lane: two running
+// fp32 sums over the chunks in order, each step a two-term fp16 dot product
+// (v_dot2_f32_f16: words 0, 2 of a chunk into the first sum, words 1, 3 into
+// the second); then the 16-lane DPP row sums and the four rows in a fixed
+// order.
 template <int NR, int KCH>
-__device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const float (&xr)[KCH][8], float (&out)[NR]) {
+__device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const u4v (&xh)[KCH], float (&out)[NR]) {
     float s0[NR], s1[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) s0[r] = s1[r] = 0.f;
@@ -137,12 +152,14 @@ __device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const float (&
     for (int c = 0; c < KCH; ++c) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const h8 hw = as_h8(w[r][c]);
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                s0[r] += (float)hw[i] * xr[c][i];
-                s1[r] += (float)hw[i + 1] * xr[c][i + 1];
-            }
+            // (vector elements go through plain locals before the bit casts)
+            const u4v wv = w[r][c], xv = xh[c];
+            const unsigned w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
+            const unsigned x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+            s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), __builtin_bit_cast(h2, x0), s0[r], false);
+            s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), __builtin_bit_cast(h2, x1), s1[r], false);
+            s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), __builtin_bit_cast(h2, x2), s0[r], false);
+            s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), __builtin_bit_cast(h2, x3), s1[r], false);
         }
     }
     float v[NR];
@@ -158,9 +175,6 @@ __device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const float (&
 // persistent one exchanges it as fp16 pairs).
 __device__ __forceinline__ float silu_mul(float gt, float up) {
     return (float)(_Float16)(gt / (1.0f + expf(-gt)) * up);
-}
-__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
-    return (uint32_t)f2h_bits(lo) | ((uint32_t)f2h_bits(hi) << 16);
 }
 
 // ============================================================================

@@ -283,7 +283,13 @@ def test_2b_full_size_sampled(rd, orc, blob2b, executor):
         k, v = om.layer0_kv(seq[p] if p < len(seq) else last_tok, p)
         for got, ref in ((k0[:, p], k), (v0[:, p], v)):
             g = got.view(np.float16).astype(np.float64)
-            assert np.allclose(g, ref, rtol=2e-3, atol=2e-4), (p, np.abs(g - ref).max())
+            # The GEMV operand (the normalised embedding) is rounded to fp16:
+            # each of the 2048 terms of a row element carries a relative error
+            # of at most 2^-11, uniform with random sign, so the element's
+            # error has standard deviation 2^-11/sqrt(3)*||w (.) xn||_2, about
+            # 3e-4 at this model's scale (row elements of order 1); atol 2e-3
+            # is over 6 of those; the fp16 cache row adds half an ulp (rtol).
+            assert np.allclose(g, ref, rtol=2e-3, atol=2e-3), (p, np.abs(g - ref).max())
     # (b) last step from the GPU cache
     for layer in range(shape.n_layers):
         for which in (0, 1):
