@@ -108,6 +108,8 @@ def test_executors_bit_identical(rd):
 
 
 GQA2 = synth.ModelShape(n_layers=2, d_model=512, n_heads=8, n_kv_heads=2, head_dim=64, d_ff=1408, vocab=1000)
+# eight kv heads: one kv-head group per XCD in the persistent kernel's attention placement
+HK8 = synth.ModelShape(n_layers=2, d_model=512, n_heads=8, n_kv_heads=8, head_dim=64, d_ff=1024, vocab=2048)
 
 
 @pytest.mark.parametrize("executor", ["graph", "persistent"])
@@ -116,6 +118,14 @@ def test_gqa_two_layers_teacher_forced(rd, orc, executor):
     prompt = synth.prompt(9, 70, GQA2.vocab)
     worst, graded, n, _ = teacher_forced(rd, orc, blob, GQA2, prompt, 20, executor=executor)
     print(f"gqa2 {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
+
+
+@pytest.mark.parametrize("executor", ["graph", "persistent"])
+def test_hk8_two_layers_teacher_forced(rd, orc, executor):
+    blob = synth.make_blob(HK8, seed=8)
+    prompt = synth.prompt(10, 70, HK8.vocab)
+    worst, graded, n, _ = teacher_forced(rd, orc, blob, HK8, prompt, 20, executor=executor)
+    print(f"hk8 {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
 
 
 @pytest.mark.parametrize("executor", ["graph", "persistent"])
@@ -129,13 +139,13 @@ def test_tiny_quantized_kv_teacher_forced(rd, orc, kv, executor):
 
 
 @pytest.mark.parametrize("shape_name,kv", [("tiny", "fp16"), ("tiny", "e5m2"), ("tiny", "int8"),
-                                           ("gqa2", "int8"), ("gqa2", "e5m2")])
+                                           ("gqa2", "int8"), ("gqa2", "e5m2"), ("hk8", "fp16"), ("hk8", "int8")])
 def test_persistent_multistep_matches_graph(rd, shape_name, kv):
     """One persistent launch decoding 300 greedy steps (crossing INT8 seals,
     E5M2 rows that share cache lines) gives the same tokens, final logits and
     cache bytes as the graph executor, which synchronises at every kernel
     boundary.  Detects stale-cache and ordering races in the persistent path."""
-    shape = synth.SHAPES["tiny"] if shape_name == "tiny" else GQA2
+    shape = {"tiny": synth.SHAPES["tiny"], "gqa2": GQA2, "hk8": HK8}[shape_name]
     blob = synth.make_blob(shape, seed=5)
     prompt = synth.prompt(106, 20, shape.vocab)
     res = {}
