@@ -152,6 +152,7 @@ def main():
     ap.add_argument("--prompt", type=int, default=512,
                     help="prompt length (512: the 2B decode workload; 32768: long context; 8192: quantized KV)")
     ap.add_argument("--executor", default="auto", choices=["auto", "graph", "eager", "persistent"])
+    ap.add_argument("--attn-splits", type=int, default=0, help="key splits per kv head (0: the library's default)")
     ap.add_argument("--phase-iters", type=int, default=96)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,7 +190,7 @@ def main():
     rewind = args.kv != "int8"
     ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup) + 1   # +1: the phase run
     m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream,
-                 batch=B)
+                 batch=B, attn_splits=args.attn_splits)
     executor = m.get_info().executor
     persistent = executor == rd.RD_EXEC_PERSISTENT
     t0 = time.time()

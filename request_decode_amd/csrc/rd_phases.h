@@ -255,10 +255,14 @@ struct AttnGeo {
     static constexpr int NPART = HD / 64;       // merge tasks per query head (64 dims each)
 };
 
-// Splits of at least 4 keys, at most S of them, for L attended positions.
+// Splits of L attended positions: at most S of them, each a multiple of 4
+// keys and at least 48 (one 16-row batch for each of the three waves that
+// reduce a split): below that, a split's latency no longer shrinks, and every
+// extra split is one more partial for the merge to wait for.
 __device__ __forceinline__ void split_plan(int L, int S, int& chunk, int& nact) {
     chunk = (L + S - 1) / S;
     chunk = (chunk + 3) & ~3;
+    chunk = chunk < 48 ? 48 : chunk;
     nact = (L + chunk - 1) / chunk;
 }
 
