@@ -76,10 +76,35 @@ __device__ __forceinline__ float group_sum(float v) {
         return v + dpp_f<0x141>(v);
     }
 }
+// gfx950 lane swaps between rows: swap16 pairs row 2k with row 2k+1 (lanes
+// l and l ^ 16), swap32 the two halves (lanes l and l ^ 32); each returns
+// the pair (first: the even row's / lower half's value, second: the other)
+// in every lane of the pair, a VALU operation with no LDS round trip.
+__device__ __forceinline__ float swap16_sum(float v) {
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float swap32_sum(float v) {
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+// Row 0's value (lanes 0..15) in the same lane of every row.
+__device__ __forceinline__ float row0_bcast(float v) {
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const auto r = __builtin_amdgcn_permlane32_swap(q[0], q[0], false, false);
+    return __uint_as_float(r[0]);
+}
+// Maximum over the 64 lanes, in every lane: row maxima by DPP, then the
+// row pairs and halves by lane swaps.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
-    return v;
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll

@@ -763,8 +763,13 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 };
                 // the lanes of slot 0 poll; the other slots take their copy (same dims)
                 poll_words<NQ>(wt, A.qb, qidx, [&](int k) { return slot == 0 && (k < G * 8 || has_new); }, tag, val);
+                if constexpr (LPR == 16) {   // slot 0 is row 0
 #pragma unroll
-                for (int k = 0; k < NQ; ++k) val[k] = __shfl(val[k], j, WAVE);
+                    for (int k = 0; k < NQ; ++k) val[k] = row0_bcast(val[k]);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < NQ; ++k) val[k] = __shfl(val[k], j, WAVE);
+                }
                 TR(10 + TR_RECV);
 #pragma unroll
                 for (int k = 0; k < NQ; ++k) s_r[k * 64 + lane] = val[k];

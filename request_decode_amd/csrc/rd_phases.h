@@ -431,12 +431,14 @@ struct AttnAcc {
             float L = 0.f;
 #pragma unroll
             for (int r = 0; r < RPW; ++r) L += readlane_f(wl, r * LPR);
+            // v + v[l ^ s] for s = LPR, ..., 32 (row rotation by 8 is l ^ 8 in a
+            // row of 16; the swaps add the same two values in either order)
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 float v = w * o[h][i];
-#pragma unroll
-                for (int s = LPR; s < WAVE; s <<= 1) v += __shfl_xor(v, s, WAVE);
-                o[h][i] = v;
+                if constexpr (LPR == 8) v += dpp_f<0x128>(v);
+                v = swap16_sum(v);
+                o[h][i] = swap32_sum(v);
             }
             m[h] = M;
             l[h] = L;

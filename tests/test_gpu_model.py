@@ -138,9 +138,10 @@ def test_tiny_quantized_kv_teacher_forced(rd, orc, kv, executor):
     print(f"tiny {kv} {executor}: steps={n} graded={graded} max|dlogit|={worst:.3e}")
 
 
-@pytest.mark.parametrize("shape_name,kv", [("tiny", "fp16"), ("tiny", "e5m2"), ("tiny", "int8"),
-                                           ("gqa2", "int8"), ("gqa2", "e5m2"), ("hk8", "fp16"), ("hk8", "int8")])
-def test_persistent_multistep_matches_graph(rd, shape_name, kv):
+@pytest.mark.parametrize("shape_name,kv,splits", [("tiny", "fp16", 0), ("tiny", "e5m2", 0), ("tiny", "int8", 0),
+                                                  ("gqa2", "int8", 0), ("gqa2", "e5m2", 0), ("hk8", "fp16", 0),
+                                                  ("hk8", "int8", 0), ("tiny", "fp16", 2), ("gqa2", "fp16", 3)])
+def test_persistent_multistep_matches_graph(rd, shape_name, kv, splits):
     """One persistent launch decoding 300 greedy steps (crossing INT8 seals,
     E5M2 rows that share cache lines) gives the same tokens, final logits and
     cache bytes as the graph executor, which synchronises at every kernel
@@ -150,7 +151,9 @@ def test_persistent_multistep_matches_graph(rd, shape_name, kv):
     prompt = synth.prompt(106, 20, shape.vocab)
     res = {}
     for ex in ("graph", "persistent"):
-        m = rd.Model(blob, max_context=400, kv_format=kv, executor=ex)
+        # splits = 2 or 3: several attention batches per wave (the fp16 cache's
+        # register-load path); default: one batch per wave at these contexts
+        m = rd.Model(blob, max_context=400, kv_format=kv, executor=ex, attn_splits=splits)
         assert m.get_info().executor == rd.EXECUTORS[ex]
         for t in prompt[:-1]:
             m.decode_step(int(t), want_logits=False)
