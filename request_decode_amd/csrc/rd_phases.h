@@ -339,12 +339,44 @@ __device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, i
                                              KvRaw (&kr)[AttnGeo<HD>::U], KvRaw (&vr)[AttnGeo<HD>::U]) {
     using Geo = AttnGeo<HD>;
     const int lane = lane_id(), slot = lane / Geo::LPR, j = lane % Geo::LPR;
+    if constexpr (KVF == KV_INT8) {
+        // the (scale, zp) pairs of the at most two segments the batch's rows
+        // fall in, one 8-byte load each for K and V (the same address in
+        // every lane), instead of two loads per row
+        const int last = min(pb + Geo::BATCH, p1) - 1;
+        const int s0 = pb / SEG, s1 = last / SEG;
+        const bool sealed0 = s0 * SEG < open0, sealed1 = s1 != s0 && s1 * SEG < open0;
+        auto meta = [&](const float* m, int sg) {
+            const uint64_t* q = reinterpret_cast<const uint64_t*>(m + ((size_t)g * A.nseg + sg) * 2);
+            return P ? ld_agent(q) : *q;
+        };
+        const uint64_t mk0 = sealed0 ? meta(A.kmeta, s0) : 0ull, mv0 = sealed0 ? meta(A.vmeta, s0) : 0ull;
+        const uint64_t mk1 = sealed1 ? meta(A.kmeta, s1) : mk0, mv1 = sealed1 ? meta(A.vmeta, s1) : mv0;
 #pragma unroll
-    for (int u = 0; u < Geo::U; ++u) {
-        const int p = batch_row<HD>(pb, u, slot);
-        const int pc = p < p1 ? p : p0;
-        kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
-        vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
+        for (int u = 0; u < Geo::U; ++u) {
+            const int p = batch_row<HD>(pb, u, slot);
+            const int pc = p < p1 ? p : p0;
+            const size_t row = (size_t)g * A.ld + pc;
+            if (pc < open0) {
+                const u2v ck = ld8(reinterpret_cast<const uint8_t*>(A.kc) + row * HD + j * 8);
+                const u2v cv = ld8(reinterpret_cast<const uint8_t*>(A.vc) + row * HD + j * 8);
+                const bool hi = pc / SEG != s0;
+                const uint64_t mk = hi ? mk1 : mk0, mv = hi ? mv1 : mv0;
+                kr[u] = KvRaw{u4v{ck.x, ck.y, 0u, 0u}, __uint_as_float((uint32_t)mk), __uint_as_float((uint32_t)(mk >> 32))};
+                vr[u] = KvRaw{u4v{cv.x, cv.y, 0u, 0u}, __uint_as_float((uint32_t)mv), __uint_as_float((uint32_t)(mv >> 32))};
+            } else {
+                kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
+                vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < Geo::U; ++u) {
+            const int p = batch_row<HD>(pb, u, slot);
+            const int pc = p < p1 ? p : p0;
+            kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
+            vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
+        }
     }
 }
 template <int HD, int KVF>
