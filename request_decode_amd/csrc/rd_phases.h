@@ -352,6 +352,24 @@ __device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, i
         };
         const uint64_t mk0 = sealed0 ? meta(A.kmeta, s0) : 0ull, mv0 = sealed0 ? meta(A.vmeta, s0) : 0ull;
         const uint64_t mk1 = sealed1 ? meta(A.kmeta, s1) : mk0, mv1 = sealed1 ? meta(A.vmeta, s1) : mv0;
+        // every row of the batch sealed (the common case, decided for the
+        // whole wave): no branch between a row's load and its registers, so
+        // that all of the batch's loads stay in flight together
+        if (last < open0 && p0 < open0) {
+#pragma unroll
+            for (int u = 0; u < Geo::U; ++u) {
+                const int p = batch_row<HD>(pb, u, slot);
+                const int pc = p < p1 ? p : p0;
+                const size_t row = (size_t)g * A.ld + pc;
+                const u2v ck = ld8(reinterpret_cast<const uint8_t*>(A.kc) + row * HD + j * 8);
+                const u2v cv = ld8(reinterpret_cast<const uint8_t*>(A.vc) + row * HD + j * 8);
+                const bool hi = pc / SEG != s0;
+                const uint64_t mk = hi ? mk1 : mk0, mv = hi ? mv1 : mv0;
+                kr[u] = KvRaw{u4v{ck.x, ck.y, 0u, 0u}, __uint_as_float((uint32_t)mk), __uint_as_float((uint32_t)(mk >> 32))};
+                vr[u] = KvRaw{u4v{cv.x, cv.y, 0u, 0u}, __uint_as_float((uint32_t)mv), __uint_as_float((uint32_t)(mv >> 32))};
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < Geo::U; ++u) {
             const int p = batch_row<HD>(pb, u, slot);
