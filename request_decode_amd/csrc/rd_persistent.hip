@@ -11,8 +11,9 @@
 // Dataflow instead of barriers.  Every vector one phase hands to the next
 // (the residual stream after each projection, the rotated q with the new
 // K/V row, the attention partials and output, the SwiGLU output, the argmax
-// candidates) is published as 64-bit words that carry the value in the low
-// half and a tag naming the (step, layer) in the high half, written with one
+// candidates) is published as 64-bit words that carry the payload in the low
+// half (an fp32 value, or two fp16 elements of a GEMV operand) and a tag
+// naming the (step, layer) in the high half, written with one
 // agent-coherent store each.  A consumer polls exactly the words it needs
 // until every tag matches; a word is never torn, so seeing the tag means
 // seeing the value, and the data arrives in the same round trip that
@@ -35,8 +36,10 @@
 //   - wave 0 (control) polls each phase's input, stages it into LDS (with
 //     the RMSNorm where the phase has one), runs every epilogue from the row
 //     sums (RoPE and the KV append, residual adds, SwiGLU, logits, argmax),
-//     the workgroup's attention split (its K/V rows fetched while the QKV
-//     rows stream) and, in some workgroups, the merge of one query head.
+//     polls the query and the new K/V row of the workgroup's attention split
+//     and combines the stream waves' partials of it, and in some workgroups
+//     merges one query head.  The stream waves reduce the split's key rows
+//     (the first batch fetched at the end of their QKV rows).
 //
 // Every arithmetic step is the one the kernel-per-phase executor performs
 // (rd_phases.h), in the same order, so both executors give identical bits.
