@@ -15,16 +15,25 @@ import csv
 import hashlib
 import json
 import os
+import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["csrc/rd_persistent.hip", "csrc/rd_phases.h", "csrc/rd_device.h", "csrc/rd_internal.h"]
 
 
+def _code_only(text: str) -> str:
+    """The source with its comments and layout removed, so that the hash
+    follows the code the counters were taken from, not its commentary."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(HERE, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(HERE, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
