@@ -89,7 +89,8 @@ typedef struct {
                            * n_heads*head_dim and d_ff multiples of 64, at most 8192. */
     int32_t kv_format;    /* rd_kv_format */
     int32_t executor;     /* rd_executor */
-    int32_t attn_splits;  /* maximum key-axis splits per kv-head, 0 = default (64) */
+    int32_t attn_splits;  /* maximum key-axis splits per kv-head (1..64); 0 = default: CUs / kv-heads
+                             at batch 1, 2 * CUs / (kv-heads * max_batch) above, within 1..64 */
 } rd_options;
 
 typedef struct {

@@ -299,12 +299,16 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     m->dev = opt.device;
     m->d = d;
     m->opt = opt;
-    // Default key splits per kv-head: one attention task per CU over all
-    // kv-heads, at most 64 (the persistent kernel gives each task a workgroup).
+    // Default key splits per kv-head, at most 64: batch 1, one attention task
+    // per CU over all kv-heads (the persistent kernel gives each task a
+    // workgroup); B sequences, two tasks per CU over all kv-heads and
+    // sequences (fewer, longer tasks: at 8192 keys and B = 8, 8 splits
+    // measured 3% faster per step than 32).
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, opt.device) != hipSuccess || cus < 1)
         cus = 1;
-    m->S = opt.attn_splits ? opt.attn_splits : std::max(1, std::min(64, cus / (int)d.Hk));
+    const int s_def = opt.max_batch > 1 ? 2 * cus / ((int)d.Hk * opt.max_batch) : cus / (int)d.Hk;
+    m->S = opt.attn_splits ? opt.attn_splits : std::max(1, std::min(64, s_def));
     auto bail = [&](rd_status st) {
         std::string keep = g_err;
         free_model(m);

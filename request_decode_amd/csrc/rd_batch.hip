@@ -8,9 +8,11 @@
 // shares each weight byte among the sequences).
 //
 // The GEMM inputs are fp16: the RMSNorm output of the QKV and gate/up GEMMs
-// (written by k_b_norm), and the attention output and SwiGLU output, which
-// the GEMM converts from fp32 as it loads them.  The residual adds are the
-// O and down GEMMs accumulating into x.
+// (written by k_b_norm), the SwiGLU output (written in fp16 by the gate/up
+// GEMM's epilogue), and the attention output, which the O GEMM converts
+// from fp32 as it loads it.  The QKV GEMM's epilogue applies RoPE and
+// appends each sequence's new K/V row; the residual adds are the O and down
+// GEMMs accumulating into x.
 #include "rd_phases.h"
 
 namespace rd {
@@ -31,15 +33,29 @@ __global__ __launch_bounds__(BW) void k_b_embed(StepArgs A) {
     for (int i = threadIdx.x; i < A.D; i += BW) A.x[(size_t)b * A.D + i] = (float)e[i];
 }
 
-// xh[b] = fp16(x[b] * (mean(x[b]^2) + eps)^-1/2 * g): thread-strided partial
+// xh[b] = fp16(x[b] * (mean(x[b]^2) + eps)^-1/2 * g).  D % 64 == 0 and
+// D <= 4 * NV * BW: each thread holds NV float4 of the row (and the gains
+// for them), all requested before the first is used; per-thread partial
 // sums of squares, wave sums, then the four waves in order.
+template <int NV>
 __global__ __launch_bounds__(BW) void k_b_norm(const float* __restrict__ x, int D, const _Float16* __restrict__ g,
                                                float eps, _Float16* __restrict__ xh) {
     __shared__ float s_w[BW / WAVE];
-    const int b = blockIdx.x;
-    const float* xb = x + (size_t)b * D;
+    const int b = blockIdx.x, n4 = D / 4;
+    const float4* xb = reinterpret_cast<const float4*>(x + (size_t)b * D);
+    const uint2* gb = reinterpret_cast<const uint2*>(g);
+    float4 v[NV];
+    uint2 gv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {   // past the row: re-read its last float4 (not used)
+        const int i = min((int)threadIdx.x + j * BW, n4 - 1);
+        v[j] = xb[i];
+        gv[j] = gb[i];
+    }
     float ss = 0.f;
-    for (int i = threadIdx.x; i < D; i += BW) ss += xb[i] * xb[i];
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        if ((int)threadIdx.x + j * BW < n4) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     ss = wave_sum(ss);
     if (lane_id() == 0) s_w[wave_id()] = ss;
     __syncthreads();
@@ -47,60 +63,63 @@ __global__ __launch_bounds__(BW) void k_b_norm(const float* __restrict__ x, int 
 #pragma unroll
     for (int w = 0; w < BW / WAVE; ++w) tot += s_w[w];
     const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-    for (int i = threadIdx.x; i < D; i += BW) xh[(size_t)b * D + i] = (_Float16)(xb[i] * inv * (float)g[i]);
-}
-
-// RoPE pairs of the QKV GEMM output y[b] (re-ordered rows) and the cache
-// append of sequence b (blockIdx.y): one thread per row pair.
-template <int KVF>
-__global__ __launch_bounds__(BW) void k_b_qkv_epi(StepArgs A, int layer) {
-    const int b = blockIdx.y, p = blockIdx.x * BW + threadIdx.x;
-    const int N = (A.H + 2 * A.Hk) * A.hd;
-    if (2 * p >= N) return;
-    const int pos = A.st->pos;
-    const float* y = A.y + (size_t)b * N;
-    const QkvPair o = qkv_pair(A.hd, A.H, A.Hk, 2 * p, y[2 * p], y[2 * p + 1], A.rope + (size_t)pos * (A.hd / 2));
-    if (o.kind == 0) {
-        float* q = A.q + (size_t)b * A.H * A.hd;
-        q[o.head * A.hd + o.d0] = o.y0;
-        q[o.head * A.hd + o.d1] = o.y1;
-    } else {
-        StepArgs Ab = A;   // sequence b's cache
-        Ab.kc = reinterpret_cast<uint8_t*>(A.kc) + (size_t)b * A.kv_bstride;
-        Ab.vc = reinterpret_cast<uint8_t*>(A.vc) + (size_t)b * A.kv_bstride;
-        if (A.stage) {
-            Ab.stage = A.stage + (size_t)b * A.st_bstride;
-            Ab.meta = A.meta + (size_t)b * A.meta_bstride;
+    uint2* ob = reinterpret_cast<uint2*>(xh + (size_t)b * D);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int i = (int)threadIdx.x + j * BW;
+        if (i < n4) {
+            const h4 gh = __builtin_bit_cast(h4, gv[j]);
+            const h4 o = h4{(_Float16)(v[j].x * inv * (float)gh[0]), (_Float16)(v[j].y * inv * (float)gh[1]),
+                            (_Float16)(v[j].z * inv * (float)gh[2]), (_Float16)(v[j].w * inv * (float)gh[3])};
+            ob[i] = __builtin_bit_cast(uint2, o);
         }
-        const int which = o.kind == 2;
-        kv_put<KVF, false>(Ab, layer, which, o.head, pos, o.d0, o.y0);
-        kv_put<KVF, false>(Ab, layer, which, o.head, pos, o.d1, o.y1);
     }
 }
 
-// m[b][i] = silu(y[b][2i]) * y[b][2i+1] (gate/up rows interleaved).
-__global__ __launch_bounds__(BW) void k_b_swiglu(const float* __restrict__ y, float* __restrict__ m, int F) {
-    const int b = blockIdx.y, i = blockIdx.x * BW + threadIdx.x;
-    if (i >= F) return;
-    const float* yb = y + (size_t)b * 2 * F;
-    m[(size_t)b * F + i] = silu_mul(yb[2 * i], yb[2 * i + 1]);
+hipError_t norm_rows(const float* x, int D, const _Float16* g, float eps, _Float16* xh, int B, hipStream_t s) {
+    const int n4 = D / 4;
+    if (n4 <= BW) hipLaunchKernelGGL(k_b_norm<1>, dim3(B), dim3(BW), 0, s, x, D, g, eps, xh);
+    else if (n4 <= 2 * BW) hipLaunchKernelGGL(k_b_norm<2>, dim3(B), dim3(BW), 0, s, x, D, g, eps, xh);
+    else if (n4 <= 4 * BW) hipLaunchKernelGGL(k_b_norm<4>, dim3(B), dim3(BW), 0, s, x, D, g, eps, xh);
+    else hipLaunchKernelGGL(k_b_norm<8>, dim3(B), dim3(BW), 0, s, x, D, g, eps, xh);
+    return hipGetLastError();
 }
 
 // Greedy argmax of sequence b's logits (lowest index on ties; a non-finite
-// logit flags ERR_NONFINITE): token[b], and gen_out[n_gen*B + b].
-__global__ __launch_bounds__(BW) void k_b_argmax(StepArgs A) {
-    const int b = blockIdx.x;
-    const float* lg = A.logits + (size_t)b * A.V;
+// logit flags ERR_NONFINITE): token[b], and gen_out[n_gen*B + b].  1024
+// threads, each with AU logits requested at a time (the ranking is a total
+// order, so the split of the row does not change the winner).
+constexpr int BWA = 1024, AU = 16;
+__global__ __launch_bounds__(BWA) void k_b_argmax(StepArgs A) {
+    __shared__ float s_v[BWA / WAVE];
+    __shared__ int s_i[BWA / WAVE];
+    const int b = blockIdx.x, V = A.V;
+    const float* lg = A.logits + (size_t)b * V;
     Best best{-INFINITY, INT_MAX};
     bool bad = false;
-    for (int i = threadIdx.x; i < A.V; i += BW) {
-        const float v = lg[i];
-        bad |= !isfinite(v);
-        best = better(best, Best{v, i});
+    for (int base = 0; base < V; base += BWA * AU) {
+        float v[AU];
+#pragma unroll
+        for (int k = 0; k < AU; ++k) v[k] = lg[min(base + k * BWA + (int)threadIdx.x, V - 1)];
+#pragma unroll
+        for (int k = 0; k < AU; ++k) {
+            const int i = base + k * BWA + (int)threadIdx.x;
+            if (i < V) {
+                bad |= !isfinite(v[k]);
+                best = better(best, Best{v[k], i});
+            }
+        }
     }
     if (bad) atomicOr(&A.st->err, ERR_NONFINITE);
-    const Best fin = block_best(best);
+    best = wave_best(best);
+    if (lane_id() == 0) {
+        s_v[wave_id()] = best.v;
+        s_i[wave_id()] = best.i;
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
+        Best fin{s_v[0], s_i[0]};
+        for (int w = 1; w < BWA / WAVE; ++w) fin = better(fin, Best{s_v[w], s_i[w]});
         A.st->token[b] = fin.i;
         const int n = A.st->n_gen;
         if (n < A.max_ctx) A.gen_out[(size_t)n * A.B + b] = fin.i;
@@ -112,13 +131,6 @@ __global__ void k_b_advance(StepState* st) {
     st->pos += 1;
 }
 
-template <int KVF>
-hipError_t qkv_epi(const StepArgs& A, int layer, hipStream_t s) {
-    const int pairs = (A.H + 2 * A.Hk) * A.hd / 2;
-    hipLaunchKernelGGL(k_b_qkv_epi<KVF>, dim3((pairs + BW - 1) / BW, A.B), dim3(BW), 0, s, A, layer);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 #define B_TRY(expr)                          \
@@ -128,32 +140,23 @@ hipError_t qkv_epi(const StepArgs& A, int layer, hipStream_t s) {
     } while (0)
 
 hipError_t launch_step_batch(const StepArgs& A, hipStream_t s) {
-    const int B = A.B, D = A.D, HD = A.H * A.hd, F = A.F, Nqkv = (A.H + 2 * A.Hk) * A.hd;
+    const int B = A.B, D = A.D, HD = A.H * A.hd, F = A.F;
     hipLaunchKernelGGL(k_b_embed, dim3(B), dim3(BW), 0, s, A);
     B_TRY(hipGetLastError());
     for (int l = 0; l < A.n_layers; ++l) {
         const LayerW& Lw = A.layers[l];
-        hipLaunchKernelGGL(k_b_norm, dim3(B), dim3(BW), 0, s, A.x, D, Lw.g_attn, A.eps, A.xh);
-        B_TRY(hipGetLastError());
-        B_TRY(launch_gemm_b8(Lw.wqkv, A.xh, false, D, A.y, Nqkv, false, Nqkv, D, B, A.ncu, s));
-        switch (A.kvfmt) {
-            case KV_FP16: B_TRY(qkv_epi<KV_FP16>(A, l, s)); break;
-            case KV_E5M2: B_TRY(qkv_epi<KV_E5M2>(A, l, s)); break;
-            default: B_TRY(qkv_epi<KV_INT8>(A, l, s)); break;
-        }
+        B_TRY(norm_rows(A.x, D, Lw.g_attn, A.eps, A.xh, B, s));
+        B_TRY(launch_gemm_b8_qkv(A, l, Lw.wqkv, s));
         B_TRY(launch_attn_any(attn_args(A, l), A.kvfmt, A.hd, A.H / A.Hk, s));
         B_TRY(launch_gemm_b8(Lw.wo, A.a, true, HD, A.x, D, true, D, HD, B, A.ncu, s));
-        hipLaunchKernelGGL(k_b_norm, dim3(B), dim3(BW), 0, s, A.x, D, Lw.g_ffn, A.eps, A.xh);
-        B_TRY(hipGetLastError());
-        B_TRY(launch_gemm_b8(Lw.wgu, A.xh, false, D, A.y, 2 * F, false, 2 * F, D, B, A.ncu, s));
-        hipLaunchKernelGGL(k_b_swiglu, dim3((F + BW - 1) / BW, B), dim3(BW), 0, s, A.y, A.m, F);
-        B_TRY(hipGetLastError());
-        B_TRY(launch_gemm_b8(Lw.wd, A.m, true, F, A.x, D, true, D, F, B, A.ncu, s));
+        B_TRY(norm_rows(A.x, D, Lw.g_ffn, A.eps, A.xh, B, s));
+        _Float16* mh = reinterpret_cast<_Float16*>(A.m);   // [B][F] fp16 in the fp32 buffer's space
+        B_TRY(launch_gemm_b8_swiglu(Lw.wgu, A.xh, D, mh, F, F, D, B, A.ncu, s));
+        B_TRY(launch_gemm_b8(Lw.wd, mh, false, F, A.x, D, true, D, F, B, A.ncu, s));
     }
-    hipLaunchKernelGGL(k_b_norm, dim3(B), dim3(BW), 0, s, A.x, D, A.g_final, A.eps, A.xh);
-    B_TRY(hipGetLastError());
+    B_TRY(norm_rows(A.x, D, A.g_final, A.eps, A.xh, B, s));
     B_TRY(launch_gemm_b8(A.lm_head, A.xh, false, D, A.logits, A.V, false, A.V, D, B, A.ncu, s));
-    hipLaunchKernelGGL(k_b_argmax, dim3(B), dim3(BW), 0, s, A);
+    hipLaunchKernelGGL(k_b_argmax, dim3(B), dim3(BWA), 0, s, A);
     B_TRY(hipGetLastError());
     hipLaunchKernelGGL(k_b_advance, dim3(1), dim3(1), 0, s, A.st);
     return hipGetLastError();

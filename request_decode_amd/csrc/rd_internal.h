@@ -188,6 +188,13 @@ hipError_t launch_step_batch(const StepArgs& A, hipStream_t s);
 hipError_t launch_attn_any(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s);
 hipError_t launch_gemm_b8(const _Float16* W, const void* x, bool x_f32, int ldx, float* y, int ldy, bool acc, int N,
                           int K, int B, int ncu, hipStream_t s);
+// m[b][i] = fp16(silu(gate_i . x[b]) * (up_i . x[b])) for B <= 8 rows of fp16 x,
+// Wgu [2F][K] with gate and up rows interleaved; m row stride ldm.
+hipError_t launch_gemm_b8_swiglu(const _Float16* Wgu, const _Float16* x, int ldx, _Float16* m, int ldm, int F, int K,
+                                 int B, int ncu, hipStream_t s);
+// The batch step's QKV GEMM of layer `layer` over A.xh (B rows), with RoPE
+// and the K/V append of each sequence at A.st->pos as its epilogue.
+hipError_t launch_gemm_b8_qkv(const StepArgs& A, int layer, const _Float16* Wqkv, hipStream_t s);
 hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s);
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,

@@ -63,10 +63,12 @@ def test_gemv_vs_oracle(rd, orc, N, K):
     _gemv_check(rd, orc, N, K, 1)
 
 
-# Batch 8 (MFMA thin GEMM): every work split (16-row blocks, K in 1, 2 or 4
-# parts), row counts that are not a multiple of 16, a single block, K = 64.
+# Batch 8 (MFMA thin GEMM): both block heights (8 rows below 16 * CUs rows,
+# else 16) with K in 4 and in 8 parts, parts of 1 to 16 steps and empty
+# parts (K = 64), row counts that are not a multiple of the block, a single
+# block, and more blocks than workgroups.
 @pytest.mark.parametrize("N,K", [(1, 64), (17, 128), (1000, 2048), (4096, 2048), (6144, 2048), (11264, 2048),
-                                 (2048, 5632), (16384, 4096), (333, 8192), (20000, 1024)])
+                                 (2048, 5632), (16384, 4096), (333, 8192), (20000, 1024), (4100, 4160)])
 def test_gemv_batch8_vs_oracle(rd, orc, N, K):
     _gemv_check(rd, orc, N, K, 8)
 
