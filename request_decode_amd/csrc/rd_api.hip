@@ -446,7 +446,7 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     const size_t o_logits = carve(NB * V * 4);
     const size_t S = m->S;
     const size_t o_part = carve(NB * H * S * (hd + 2) * 4);
-    const size_t o_y = carve(NB > 1 ? NB * std::max(Nqkv, 2 * F) * 4 : 4), o_xh = carve(NB > 1 ? NB * D * 2 : 4);
+    const size_t o_xh = carve(NB > 1 ? NB * D * 2 : 4);
     const int n_arg = n_lm_wg;   // argmax partials of the LM-head kernel
     const size_t o_av = carve(n_arg * 4), o_ai = carve(n_arg * 4), o_ac = carve(64 * 4);
     // exchange words of the persistent executor
@@ -493,7 +493,6 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     A.kv_bstride = kv_seq * es;
     A.st_bstride = NL * 2 * Hk * SEG * hd;
     A.meta_bstride = NL * 2 * Hk * (size_t)m->nseg * 2;
-    A.y = (float*)(X + o_y);
     A.xh = (_Float16*)(X + o_xh);
 
     // ---- executor: the persistent kernel where its shape is built, else the graph

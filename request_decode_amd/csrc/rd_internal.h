@@ -82,7 +82,6 @@ struct StepArgs {
     size_t kv_bstride;       // bytes of one sequence's K (or V) cache
     size_t st_bstride;       // INT8: elements of one sequence's staging rows
     size_t meta_bstride;     // INT8: floats of one sequence's (scale, zp) table
-    float* y;                // B > 1: [B][max(Nqkv, 2F)] GEMM outputs
     _Float16* xh;            // B > 1: [B][D] normalised inputs of the QKV and gate/up GEMMs
     const _Float16* embed;
     const _Float16* g_final;
@@ -91,7 +90,7 @@ struct StepArgs {
     float* x;                // [D] residual stream
     float* q;                // [H*hd]
     float* a;                // [H*hd]
-    float* m;                // [F]
+    float* m;                // [B][F] SwiGLU output (B > 1: fp16 rows, F halves apart)
     float* logits;           // [V]
     float* part;             // [H][S][hd+2]
     float* arg_val;          // [n LM-head workgroups]
