@@ -159,7 +159,7 @@ def main():
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV microbench")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {args.gpus}); "
+        print(f"bench.py: the decode path runs on one GPU only (asked for {args.gpus}); "
               "multi-GPU sharding is designed but not built", file=sys.stderr)
         sys.exit(2)
     if args.warmup is None:

@@ -57,7 +57,7 @@ typedef enum {
     RD_ERR_BAD_BLOB = -2,      /* malformed or mis-sized weight blob */
     RD_ERR_OUT_OF_MEMORY = -3, /* device allocation failed */
     RD_ERR_CONTEXT_FULL = -4,  /* position would reach max_context; state unchanged */
-    RD_ERR_UNSUPPORTED = -5,   /* valid request this build does not implement */
+    RD_ERR_UNSUPPORTED = -5,   /* valid request the library does not implement */
     RD_ERR_DEVICE = -6,        /* HIP error; the model is poisoned */
     RD_ERR_NUMERIC = -7        /* non-finite logit or out-of-range token seen on the device */
 } rd_status;
