@@ -54,6 +54,7 @@ def lib():
         L.orc_seg_quant.argtypes = [u16p, C.c_int, u8p, fp, fp]
         L.orc_seg_dequant.restype = C.c_float
         L.orc_seg_dequant.argtypes = [C.c_uint8, C.c_float, C.c_float]
+        L.orc_seg_dequant_n.argtypes = [u8p, C.c_size_t, C.c_float, C.c_float, fp]
         L.orc_rmsnorm.argtypes = [dp, u16p, C.c_int, C.c_double, dp]
         L.orc_rope.argtypes = [dp, C.c_int, C.c_int, C.c_double]
         L.orc_gemv.argtypes = [u16p, dp, C.c_int, C.c_int, dp]
@@ -80,6 +81,7 @@ def lib():
         L.orc_seg_meta.argtypes = [C.c_void_p] + [C.c_int] * 5 + [fp, fp, C.c_int]
         L.orc_read_row.restype = C.c_int
         L.orc_read_row.argtypes = [C.c_void_p] + [C.c_int] * 5 + [dp]
+        L.orc_set_store.argtypes = [C.c_void_p, C.c_int]
         L.orc_set_pos.restype = C.c_int
         L.orc_set_pos.argtypes = [C.c_void_p, C.c_int, C.c_int]
         _lib = L
@@ -130,9 +132,11 @@ def seg_quant(h: np.ndarray):
 
 
 def seg_dequant(codes: np.ndarray, scale, zp) -> np.ndarray:
-    f = lib().orc_seg_dequant
-    return np.array([f(int(c), float(scale), float(zp)) for c in np.asarray(codes).reshape(-1)],
-                    dtype=np.float32).reshape(np.shape(codes))
+    """(code - zp) * scale in binary32, element-wise (orc_seg_dequant)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float32)
+    lib().orc_seg_dequant_n(_p(c, C.c_uint8), c.size, float(scale), float(zp), _p(out, C.c_float))
+    return out
 
 
 # ---- building blocks ---------------------------------------------------------
@@ -214,6 +218,10 @@ class OracleModel:
     def set_pos(self, pos: int, b: int = 0):
         if lib().orc_set_pos(self._h, b, pos) != 0:
             raise ValueError("bad position")
+
+    def set_store(self, store: bool):
+        """False: steps keep the rows already at their position (orc_set_store)."""
+        lib().orc_set_store(self._h, 1 if store else 0)
 
     def step(self, tokens):
         t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(self.batch))

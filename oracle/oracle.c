@@ -134,7 +134,11 @@ void orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale_out, f
         if (v > mx) mx = v;
     }
     float scale = (mx - mn) / 255.0f;
-    if (!(scale > 0.0f)) scale = 1.0f;             /* all values equal: any scale is exact enough */
+    /* The page's formula gives scale 0 for a segment whose values are all
+     * equal.  Then the value itself (its magnitude) is the unit: zp becomes
+     * -1, 0 or +1, every code is 0 and (0 - zp) * scale returns the value
+     * exactly.  An all-zero segment takes scale 1. */
+    if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;
     float zp = rintf(-mn / scale);
     for (int i = 0; i < n; ++i) {
         float v = (float)orc_h2d(x[i]);
@@ -148,6 +152,10 @@ void orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale_out, f
 }
 
 float orc_seg_dequant(uint8_t code, float scale, float zp) { return ((float)code - zp) * scale; }
+
+void orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, float* out) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_seg_dequant(codes[i], scale, zp);
+}
 
 /* ------------------------------------------------------------------------ */
 /* Building blocks                                                           */
@@ -236,6 +244,7 @@ struct orc_model {
     const uint16_t *embed, *final_norm, *lm_head;
     orc_layer* layer;
     int max_ctx, batch, fmt;
+    int store;         /* 0: a step keeps the row already at its position (see orc_set_store) */
     int* pos;
     void* kv;          /* [b][layer][which][head][max_ctx][hd] of the format's element */
     uint16_t* stage;   /* INT8: [b][layer][which][head][128][hd] open segment */
@@ -323,6 +332,7 @@ orc_model* orc_create(const void* blob_v, size_t bytes, int max_ctx, int batch, 
     m->max_ctx = max_ctx;
     m->batch = batch;
     m->fmt = kv_format;
+    m->store = 1;
     m->pos = (int*)calloc((size_t)batch, sizeof(int));
     size_t lanes = (size_t)batch * L * 2 * Hk;
     m->kv = calloc(lanes * (size_t)max_ctx * hd, kv_elem_size(kv_format));
@@ -350,6 +360,8 @@ int orc_pos(const orc_model* m, int b) { return m->pos[b]; }
 void orc_dims(const orc_model* m, int* o) {
     o[0] = m->L; o[1] = m->D; o[2] = m->H; o[3] = m->Hk; o[4] = m->hd; o[5] = m->F; o[6] = m->V;
 }
+
+void orc_set_store(orc_model* m, int store) { m->store = store != 0; }
 
 int orc_set_pos(orc_model* m, int b, int pos) {
     if (b < 0 || b >= m->batch || pos < 0 || pos > m->max_ctx) return -1;
@@ -501,10 +513,11 @@ int orc_step(orc_model* m, const int32_t* tokens, double* logits, int32_t* next)
             orc_gemv(y->wv, r, Hk * hd, D, v);
             for (int h = 0; h < H; ++h) orc_rope(q + (size_t)h * hd, hd, pos, m->base);
             for (int g = 0; g < Hk; ++g) orc_rope(k + (size_t)g * hd, hd, pos, m->base);
-            for (int g = 0; g < Hk; ++g) {
-                store_row(m, b, l, 0, g, pos, k + (size_t)g * hd);
-                store_row(m, b, l, 1, g, pos, v + (size_t)g * hd);
-            }
+            if (m->store)
+                for (int g = 0; g < Hk; ++g) {
+                    store_row(m, b, l, 0, g, pos, k + (size_t)g * hd);
+                    store_row(m, b, l, 1, g, pos, v + (size_t)g * hd);
+                }
             /* attention: query head h reads kv head h / G */
 #pragma omp parallel for schedule(dynamic, 1)
             for (int g = 0; g < Hk; ++g) {

@@ -43,9 +43,11 @@ void orc_h_from_e5m2_n(const uint8_t* e, size_t n, uint16_t* out);
 /* Adaptive-range segment quantization ("Grok-3 v3.2.4 hot update", §3.2):
  * over n binary16 values, min/max -> scale=(max-min)/255,
  * zp=round(-min/scale) (round half to even), code=clamp(round(x/scale)+zp,0,255).
- * All in binary32.  Degenerate max==min uses scale 1. */
+ * All in binary32.  Degenerate max==min uses scale |min| (1 when the
+ * segment is all zeros), which reproduces the constant exactly. */
 void  orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale, float* zp);
 float orc_seg_dequant(uint8_t code, float scale, float zp);
+void  orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, float* out);
 
 /* ---- building blocks (binary64) ----------------------------------------- */
 void   orc_rmsnorm(const double* x, const uint16_t* gain, int d, double eps, double* out);
@@ -97,6 +99,12 @@ int orc_seg_meta(orc_model* m, int b, int layer, int which, int head, int seg, f
 /* Dequantized (as-attended) value of one cache row, binary64 [hd]. */
 int orc_read_row(const orc_model* m, int b, int layer, int which, int head, int pos, double* dst);
 int orc_set_pos(orc_model* m, int b, int pos);
+/* store = 0: orc_step computes the K/V rows of its position but does not
+ * store them; attention reads whatever row that position already holds
+ * (set with orc_set_rows), and the INT8 seal quantizes the staging rows as
+ * they are.  A test of the 8-bit formats uses it to run a step over the
+ * exact stored bytes of another implementation's cache.  Default 1. */
+void orc_set_store(orc_model* m, int store);
 
 #ifdef __cplusplus
 }

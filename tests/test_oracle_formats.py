@@ -117,8 +117,15 @@ def test_segquant_invariants(orc, lo, hi, seed):
     assert np.array_equal(deq, (codes.astype(np.float32) - zp) * scale)
 
 
-def test_segquant_degenerate(orc):
-    x = np.full(128 * 4, 0.5, np.float16)
+@pytest.mark.parametrize("c", [0.3, -0.3, 0.5, -1e-3, 60000.0, 2.0 ** -24, 0.0])
+def test_segquant_degenerate(orc, c):
+    """A segment of one repeated value (max == min, where the page's formula
+    gives scale 0) dequantizes to that value exactly: scale |min|, zero point
+    -sign(min), every code 0; an all-zero segment takes scale 1."""
+    x = np.full(128 * 4, c, np.float16)
     codes, scale, zp = orc.seg_quant(x.view(np.uint16))
-    assert scale == 1.0 and zp == np.float32(np.rint(-0.5))
-    assert np.all(codes == codes[0])
+    v = np.float32(x[0])
+    assert scale == (abs(v) if v != 0 else np.float32(1.0))
+    assert zp == np.float32(-np.sign(v))
+    assert np.all(codes == 0)
+    assert np.all(orc.seg_dequant(codes[:4], scale, zp) == v)

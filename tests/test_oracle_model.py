@@ -127,3 +127,173 @@ def test_quantized_caches(orc):
     for t in toks[128:]:
         ref.step([t]); e5.step([t]); i8.step([t])
     assert ref.pos() == e5.pos() == i8.pos() == 300
+
+
+# ---- in-model KV formats: every row of the cache against an independent path ----------
+
+# head_dim 64 and 128, two kv heads, two layers (the seal runs for every layer)
+SEAL64 = synth.ModelShape(n_layers=2, d_model=128, n_heads=4, n_kv_heads=2, head_dim=64, d_ff=256, vocab=512)
+SEAL128 = synth.ModelShape(n_layers=2, d_model=256, n_heads=4, n_kv_heads=2, head_dim=128, d_ff=256, vocab=512)
+
+
+@pytest.mark.parametrize("shape", [SEAL64, SEAL128], ids=["hd64", "hd128"])
+def test_int8_seal_codes_in_model(orc, shape):
+    """The INT8 cache after 256 steps holds two sealed segments per (layer,
+    K/V, kv head).  Each one's codes and fp32 (scale, zero point) must be the
+    segment quantizer of exactly the 128 x head_dim binary16 rows that segment
+    held ("Grok-3 v3.2.4 hot update deep dive", section 3.2):
+      * layer 0, both segments: the rows from orc_layer0_kv, which depend on
+        (token, position) alone (an independent path to the same rows);
+      * every layer, segment 0: the rows of an fp16-cache run on the same
+        tokens (until the first seal both runs attend to the same binary16
+        rows, so their caches agree bit for bit);
+      * every layer, segment 1: the staging rows the run itself held, read
+        back by rewinding into that segment.
+    A wrong lane, head or segment offset in the seal, or a per-row seal,
+    fails one of the three."""
+    blob = synth.make_blob(shape, seed=11)
+    toks = synth.prompt(12, 256, shape.vocab)
+    i8 = orc.OracleModel(blob, 300, kv_format="int8")
+    f16 = orc.OracleModel(blob, 300, kv_format="fp16")
+    for t in toks[:128]:
+        i8.step([t])
+        f16.step([t])
+    for t in toks[128:]:
+        i8.step([t])
+    assert i8.pos() == 256
+    Hk = shape.n_kv_heads
+    sealed = {}
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(Hk):
+                for seg in (0, 1):
+                    codes = i8.get_rows(l, w, g, seg * 128, 128)
+                    assert codes.dtype == np.uint8
+                    sealed[l, w, g, seg] = (codes, i8.seg_meta(l, w, g, seg))
+    # layer 0 against orc_layer0_kv
+    k0 = np.empty((256, Hk, shape.head_dim))
+    v0 = np.empty((256, Hk, shape.head_dim))
+    for p in range(256):
+        k0[p], v0[p] = i8.layer0_kv(int(toks[p]), p)
+    for w, rows in ((0, k0), (1, v0)):
+        for g in range(Hk):
+            for seg in (0, 1):
+                h = orc.d2h(rows[seg * 128:(seg + 1) * 128, g])
+                codes, scale, zp = orc.seg_quant(h)
+                got, (gs, gz) = sealed[0, w, g, seg]
+                assert np.array_equal(got, codes) and gs == scale and gz == zp, (w, g, seg)
+    # every layer, segment 0, against the fp16-cache run
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(Hk):
+                codes, scale, zp = orc.seg_quant(f16.get_rows(l, w, g, 0, 128))
+                got, (gs, gz) = sealed[l, w, g, 0]
+                assert np.array_equal(got, codes) and gs == scale and gz == zp, (l, w, g)
+    # every layer, segment 1, against its own staging rows (rewound into segment 1)
+    i8.set_pos(255)
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(Hk):
+                st = i8.get_rows(l, w, g, 128, 128)
+                assert st.dtype == np.uint16
+                codes, scale, zp = orc.seg_quant(st)
+                got, (gs, gz) = sealed[l, w, g, 1]
+                assert np.array_equal(got, codes) and gs == scale and gz == zp, (l, w, g)
+    # the attention reads a sealed row as (code - zp) * scale
+    i8.set_pos(256)
+    codes, (scale, zp) = sealed[1, 1, 1, 0]
+    assert np.array_equal(i8.read_row(1, 1, 1, 77),
+                          ((codes[77].astype(np.float32) - zp) * scale).astype(np.float64))
+
+
+def test_quantized_rows_layer0_every_position(orc):
+    """Every layer-0 row of the E5M2 cache is the E5M2 encoding of the
+    binary16 rounding of orc_layer0_kv; every row of the INT8 cache's open
+    segment is that binary16 value (staging), for all positions and heads."""
+    shape = SEAL64
+    blob = synth.make_blob(shape, seed=13)
+    toks = synth.prompt(14, 200, shape.vocab)
+    e5 = orc.OracleModel(blob, 256, kv_format="e5m2")
+    i8 = orc.OracleModel(blob, 256, kv_format="int8")
+    for t in toks:
+        e5.step([t])
+        i8.step([t])
+    for p in range(200):
+        k, v = e5.layer0_kv(int(toks[p]), p)
+        for w, rows in ((0, k), (1, v)):
+            for g in range(shape.n_kv_heads):
+                h = orc.d2h(rows[g])
+                assert np.array_equal(e5.get_rows(0, w, g, p, 1)[0], orc.e5m2_from_h(h)), (p, w, g)
+                if p >= 128:
+                    assert np.array_equal(i8.get_rows(0, w, g, p, 1)[0], h), (p, w, g)
+                    assert np.array_equal(i8.read_row(0, w, g, p), orc.h2d(h))
+                else:
+                    assert np.array_equal(e5.read_row(0, w, g, p), orc.h2d(orc.h_from_e5m2(orc.e5m2_from_h(h))))
+
+
+@pytest.mark.parametrize("kv,n", [("fp16", 40), ("e5m2", 40), ("int8", 140)])
+def test_batch_step_equals_independent_sequences(orc, kv, n):
+    """The batch-B step is B independent sequences: its logits and argmax are
+    bit-identical to B batch-1 models fed the same token streams (int8: the
+    streams cross a segment seal)."""
+    shape = SEAL64
+    blob = synth.make_blob(shape, seed=15)
+    B = 3
+    streams = synth.prompts(16, n, shape.vocab, B)
+    mb = orc.OracleModel(blob, n + 4, batch=B, kv_format=kv)
+    singles = [orc.OracleModel(blob, n + 4, kv_format=kv) for _ in range(B)]
+    for i in range(n):
+        lb, nb = mb.step(streams[:, i])
+        for b in range(B):
+            ls, ns = singles[b].step([streams[b, i]])
+            assert np.array_equal(lb[b], ls[0]) and nb[b] == ns[0], (kv, i, b)
+    for b in range(B):
+        assert mb.pos(b) == n
+        for w in (0, 1):
+            got = mb.get_rows(1, w, 1, 0, n // 128 * 128 or n, b=b)
+            ref = singles[b].get_rows(1, w, 1, 0, n // 128 * 128 or n)
+            assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("kv", ["fp16", "e5m2", "int8"])
+def test_store_off_step_is_the_same_step(orc, kv):
+    """With its row store switched off, a step whose position already holds
+    the rows the step would store gives bit-identical logits, argmax and
+    cache (int8: the seal quantizes the staging rows as they are).  Model B
+    gets A's rows of each position before its step, A stores its own."""
+    shape = SEAL64
+    blob = synth.make_blob(shape, seed=17)
+    toks = synth.prompt(18, 140, shape.vocab)
+    a = orc.OracleModel(blob, 160, kv_format=kv)
+    b = orc.OracleModel(blob, 160, kv_format=kv)
+    b.set_store(False)
+    for i, t in enumerate(toks):
+        la, na = a.step([t])
+        b.set_pos(i)
+        for l in range(shape.n_layers):
+            for w in (0, 1):
+                for g in range(shape.n_kv_heads):
+                    if kv == "int8" and i % 128 == 127:
+                        # A's segment is sealed by now: give B the staging row A held
+                        a.set_pos(i)
+                        row = a.get_rows(l, w, g, i, 1)
+                        a.set_pos(i + 1)
+                    else:
+                        row = a.get_rows(l, w, g, i, 1)
+                    b.set_rows(l, w, g, i, row)
+        lb, nb = b.step([t])
+        assert np.array_equal(la, lb) and na[0] == nb[0], (kv, i)
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(shape.n_kv_heads):
+                assert np.array_equal(a.get_rows(l, w, g, 0, 128 if kv == "int8" else 140),
+                                      b.get_rows(l, w, g, 0, 128 if kv == "int8" else 140))
+                if kv == "int8":
+                    assert a.seg_meta(l, w, g, 0) == b.seg_meta(l, w, g, 0)
+    # and switched off it really stores nothing: a fresh position keeps what it held
+    c = orc.OracleModel(blob, 8, kv_format=kv)
+    c.set_store(False)
+    before = c.get_rows(0, 0, 0, 0, 1).copy()
+    c.step([int(toks[0])])
+    c.set_pos(0)
+    assert np.array_equal(c.get_rows(0, 0, 0, 0, 1), before)
