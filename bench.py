@@ -58,31 +58,52 @@ def step_bytes(shape, L: int, kv: str = "fp16", batch: int = 1) -> float:
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_persist_2b_decode_fp16_traffic.json")
 
 
-def measured_traffic(args):
-    """HBM bytes of the timed persistent launch (read + write), from the
+def measured_traffic(args, bytes_run):
+    """HBM bytes (read + write) of the timed persistent launch: the
     calibrated counter runs recorded under profiles/ for this workload
-    (prompt 512, 256 steps, fp16 KV); None if the run differs from that
-    workload or the kernel's sources changed since the counters were taken."""
+    (512-token prompt, fp16 KV, batch 1) give counter bytes per algorithmic
+    byte over a 256-step launch at positions 511..766; the timed launch's
+    algorithmic bytes times that ratio.  None if the run is another workload
+    or the kernel's sources changed since the counters were taken."""
     import json as _json
     from request_decode_amd.traffic import source_hash
-    if not (args.prompt == 512 and args.steps == 256 and args.kv == "fp16") or not os.path.exists(TRAFFIC_RECORD):
+    if not (args.prompt == 512 and args.kv == "fp16" and args.batch == 1) or not os.path.exists(TRAFFIC_RECORD):
         return None
     rec = _json.load(open(TRAFFIC_RECORD))
-    return rec["traffic_bytes"] if rec.get("source_sha256") == source_hash() else None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return int(round(bytes_run * rec["traffic_bytes"] / rec["algorithmic_bytes"]))
 
 
-def cpu_baseline(blob, shape, seconds: float):
-    """Oracle tokens/s on the machine's host cores: a short prompt, then decode
-    steps until `seconds` of CPU work have run (at least 3, at most 64)."""
+def cpu_model_name() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(blob, shape, seconds: float, base: int, first: int):
+    """Oracle tokens/s on the machine's host cores at the timed positions: the
+    oracle's fp16 cache holds seeded synthetic rows at positions 0..base-1
+    (the step's cost does not depend on their values), then greedy decode
+    steps from position `base` until `seconds` of CPU work have run (at
+    least 3, at most 64)."""
     cores = len(os.sched_getaffinity(0))
     os.environ["OMP_NUM_THREADS"] = str(cores)
+    import numpy as np
     import oracle
     import synth
-    om = oracle.OracleModel(blob, 128, kv_format="fp16")
-    toks = synth.prompt(103, 4, shape.vocab)
-    for t in toks[:-1]:
-        om.step([t])
-    t = int(toks[-1])
+    om = oracle.OracleModel(blob, base + 72, kv_format="fp16")
+    fill = synth.normal_f16(7, (base, shape.head_dim)).view(np.uint16)
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(shape.n_kv_heads):
+                om.set_rows(l, w, g, 0, fill)
+    om.set_pos(base)
+    t = first
     n, t0 = 0, time.perf_counter()
     while True:
         _, nxt = om.step([t])
@@ -92,10 +113,80 @@ def cpu_baseline(blob, shape, seconds: float):
         if (el >= seconds and n >= 3) or n >= 64:
             break
     om.close()
-    return {"value": n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"2B model, 3-token prompt then {n} greedy decode steps (positions 3..{3 + n - 1}); "
-                      f"the oracle's per-step cost is dominated by the 2.4 GB of weights, as on the GPU "
-                      f"(KV at L<=768 adds <3%)"}
+    return {"value": n / el, "unit": "tokens/s", "cores": cores, "cpu": cpu_model_name(), "kind": "oracle",
+            "sample": f"2B model, fp16 cache filled with synthetic rows at positions 0..{base - 1}, then {n} "
+                      f"greedy decode steps at positions {base}..{base + n - 1} (the timed positions' start)"}
+
+
+def layer_trace(m, token: int, reps: int):
+    """Where a layer of one persistent step spends its time, from the kernel's
+    in-kernel event trace of every workgroup (rd_debug_trace_step_all; the
+    wall clock is shared by all CUs).  Per workgroup and layer (the middle
+    layers 2..21 of the step), the control wave's events give its own work
+    per phase (input received -> output published) and its waits (own
+    output published -> next input received).  The six exchanges of a layer
+    are the waits of the workgroups that consume them: QKV <- down, the
+    attention split <- QKV (attention workgroups), the merge <- attention
+    (merge workgroups), O <- merge (merge workgroups), gate/up <- O and
+    down <- gate/up.  Reported: medians over workgroups and layers, in us,
+    of the last of `reps` traced steps (the first is not used)."""
+    import numpy as np
+    for _ in range(max(2, reps)):
+        tr = m.trace_step_all(token)
+        m.set_position(m.position() - 1)
+    per = []
+    for codes, clk in tr:
+        d, occ = {}, {}
+        for c, t in zip(codes.tolist(), clk.tolist()):
+            k = occ.get(c, 0)
+            occ[c] = k + 1
+            d[(c, k)] = t * 0.01        # 100 MHz clock -> us
+        per.append(d)
+    seg = {k: [] for k in ("layer", "qkv", "att", "merge", "o", "gu", "down", "x_qkv", "x_att", "x_merge", "x_o",
+                           "x_gu", "x_down")}
+    # inside each GEMV phase (stream wave 0's events 100 + 10 * kind + point:
+    # released, first rows reduced, all rows reduced; kinds 0 QKV, 1 O,
+    # 2 gate/up, 3 down): staging of the input, release of the stream waves,
+    # first rows, the rest of the rows, the control wave's epilogue
+    ctrl = {"qkv": 0, "o": 30, "gu": 40, "down": 50}
+    kind = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
+    for ph in ctrl:
+        for part in ("stage", "release", "first", "rows", "epilogue"):
+            seg[f"{ph}.{part}"] = []
+    for d in per:
+        for l in range(2, 22):
+            g = lambda c, ll=l: d.get((c, ll))
+            if None in (g(0), g(3), g(30), g(33), g(40), g(43), g(50), g(53)) or (0, l + 1) not in d:
+                continue
+            seg["layer"].append(d[(0, l + 1)] - g(0))
+            seg["qkv"].append(g(3) - g(0))
+            seg["o"].append(g(33) - g(30))
+            seg["gu"].append(g(43) - g(40))
+            seg["down"].append(g(53) - g(50))
+            seg["x_gu"].append(g(40) - g(33))
+            seg["x_down"].append(g(50) - g(43))
+            seg["x_qkv"].append(d[(0, l + 1)] - g(53))
+            for ph, c in ctrl.items():
+                k = 100 + 10 * kind[ph]
+                staged = g(c + 1) if g(c + 1) is not None else g(c)   # only QKV records its staging
+                ev = (g(c), staged, g(k), g(k + 1), g(k + 2), g(c + 2), g(c + 3))
+                if None not in ev:
+                    seg[f"{ph}.stage"].append(ev[1] - ev[0])
+                    seg[f"{ph}.release"].append(ev[2] - ev[1])
+                    seg[f"{ph}.first"].append(ev[3] - ev[2])
+                    seg[f"{ph}.rows"].append(ev[4] - ev[3])
+                    seg[f"{ph}.epilogue"].append(ev[6] - ev[4])
+            if g(10) is not None and g(13) is not None:
+                seg["x_att"].append(g(10) - g(3))
+                seg["att"].append(g(13) - g(10))
+            if g(20) is not None and g(23) is not None:
+                seg["x_merge"].append(g(20) - (g(13) if g(13) is not None else g(3)))
+                seg["merge"].append(g(23) - g(20))
+                seg["x_o"].append(g(30) - g(23))
+    med = {k: round(float(np.median(v)), 3) for k, v in seg.items() if v}
+    med["exchanges"] = round(sum(med.get(k, 0.0) for k in ("x_qkv", "x_att", "x_merge", "x_o", "x_gu", "x_down")), 3)
+    med["workgroups"] = len(per)
+    return med
 
 
 GEMV_SHAPES = [(16384, 4096), (6144, 2048), (4096, 2048), (11264, 2048), (2048, 5632)]
@@ -106,8 +197,10 @@ def gemv_microbench(rd, torch, stream, iters: int = 3):
     """The weight-streaming GEMV alone: y = W x (fp16 in, fp32 out) at batch
     1 and 8 on the listed shapes.  Cold cache: launches rotate over distinct
     copies of W totalling >= 768 MiB, so every launch streams W from HBM.
-    Each launch is bracketed by its own pair of events on the launch stream;
-    reported: mean duration and algorithmic GB/s (W + x + y bytes)."""
+    Kernel time: the launches are captured into one graph and replayed
+    back to back between one pair of events, so no per-launch host or event
+    overhead is counted; reported: mean time per launch and algorithmic
+    GB/s (W + x + y bytes)."""
     import synth
     out = []
     for N, K in GEMV_SHAPES:
@@ -124,14 +217,20 @@ def gemv_microbench(rd, torch, stream, iters: int = 3):
                 rd.rd_gemv_f16(c.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch, stream.cuda_stream)
             torch.cuda.synchronize()
             n = ncopy * iters
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            for i in range(n):
-                evs[i][0].record(stream)
-                rd.rd_gemv_f16(copies[i % ncopy].data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch,
-                               stream.cuda_stream)
-                evs[i][1].record(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    rd.rd_gemv_f16(copies[i % ncopy].data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, batch,
+                                   stream.cuda_stream)
+            g.replay()
             torch.cuda.synchronize()
-            us = sum(a.elapsed_time(b) for a, b in evs) * 1e3 / n
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / n
+            del g
             nbytes = wbytes + batch * K * 2 + batch * N * 4
             gbps = nbytes / (us * 1e-6) / 1e9
             row[f"b{batch}"] = {"us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
@@ -157,6 +256,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV microbench")
+    ap.add_argument("--trace", type=int, default=0,
+                    help="persistent executor: trace this many steps in the middle of the timed range and "
+                         "report where a layer's time goes (exchange waits and per-phase work)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the decode path runs on one GPU only (asked for {args.gpus}); "
@@ -224,7 +326,15 @@ def main():
     bytes_step = bytes_run / args.steps
     gbps = bytes_run / (ms / 1e3) / 1e9
     print(f"[bench] timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
-          f"{gbps:.0f} GB/s (wall {wall * 1e3 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+          f"{gbps:.0f} GB/s (host wall clock {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+
+    trace = None
+    if args.trace and persistent and rewind:
+        m.set_position(base + args.steps // 2)
+        tok = int(out[args.steps // 2 - 1].item()) if args.steps >= 2 else first
+        trace = layer_trace(m, tok, args.trace)
+        print(f"[bench] layer trace (us, medians over workgroups and layers 2..21): {trace}", file=sys.stderr,
+              flush=True)
 
     # the gate/up GEMV phase kernel of the (batch-1) graph executor, timed
     # alone, rotating over the 24 layers so that its weights come from HBM
@@ -245,12 +355,13 @@ def main():
         k_gbps = k_bytes / (k_us * 1e-6) / 1e9
         print(f"[bench] gate/up phase kernel: {k_us:.2f} us/launch, {k_gbps:.0f} GB/s", file=sys.stderr, flush=True)
     m.close()
+    del out
     gemv = None if args.no_gemv else gemv_microbench(rd, torch, stream)
 
     if persistent:
         roof = {"bound": "hbm", "kernel": "k_persist (whole decode steps, one launch for all timed steps)",
                 "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(args, bytes_run),
                 "bytes_per_launch": int(bytes_run), "us_per_launch": round(ms * 1e3, 1)}
     elif B > 1:
         roof = {"bound": "hbm", "kernel": "batch step: graph of per-phase kernels (thin GEMMs k_gemm_b8 on MFMA)",
@@ -283,10 +394,20 @@ def main():
     }
     if k_us is not None:
         res["gateup_phase_kernel"] = {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)}
+    if trace is not None:
+        res["layer_trace_us"] = trace
     if gemv is not None:
         res["gemv_microbench"] = gemv
+        big = [r for r in gemv if (r["N"], r["K"]) == (16384, 4096)]
+        if big:
+            res["gemv_16384x4096_b1_frac"] = big[0]["b1"]["frac"]
+    # device resources released before the interpreter's own teardown
+    torch.cuda.synchronize()
+    rd.release_scratch()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(blob, shape, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(blob, shape, args.cpu_seconds, base,
+                                           first if B == 1 else int(first[0]))
     print(json.dumps(res), flush=True)
 
 

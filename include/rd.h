@@ -70,10 +70,14 @@ typedef enum {
 } rd_kv_format;
 
 typedef enum {
-    RD_EXEC_AUTO = 0,      /* the fastest measured executor */
+    RD_EXEC_AUTO = 0,      /* PERSISTENT where a persistent kernel is built for the model's shape
+                              (batch 1; the 2B-class, tiny and small-GQA test shapes with their
+                              split counts), otherwise GRAPH */
     RD_EXEC_EAGER = 1,     /* one kernel launch per phase */
     RD_EXEC_GRAPH = 2,     /* the step's launches captured once into a hipGraph, replayed per step */
-    RD_EXEC_PERSISTENT = 3 /* one cooperative launch per step, grid barriers between phases */
+    RD_EXEC_PERSISTENT = 3 /* one cooperative launch runs a whole run of steps (rd_generate: up to
+                              512 per launch); workgroups hand vectors to each other through
+                              tagged exchange words instead of grid barriers */
 } rd_executor;
 
 typedef struct {
@@ -89,8 +93,11 @@ typedef struct {
                            * n_heads*head_dim and d_ff multiples of 64, at most 8192. */
     int32_t kv_format;    /* rd_kv_format */
     int32_t executor;     /* rd_executor */
-    int32_t attn_splits;  /* maximum key-axis splits per kv-head (1..64); 0 = default: CUs / kv-heads
-                             at batch 1, 2 * CUs / (kv-heads * max_batch) above, within 1..64 */
+    int32_t attn_splits;  /* maximum key-axis splits per kv-head, 1..256; 0 = default: CUs / kv-heads
+                             at batch 1, 2 * CUs / (kv-heads * max_batch) above, within 1..64.
+                             Each split covers at least 48 keys.  The persistent kernels merge at
+                             most 32 (2B-class shape) or 64 (test shapes) splits: with more, AUTO
+                             takes GRAPH and PERSISTENT is UNSUPPORTED. */
 } rd_options;
 
 typedef struct {
@@ -107,7 +114,9 @@ typedef struct {
  * max_context 4096, max_batch 1, fp16 KV, AUTO executor, 0 splits). */
 void rd_options_init(rd_options* opt);
 
-/* Create a model from a weight blob ("RDW1"): a 256-byte header (magic,
+/* Create a model from a weight blob ("RDW1"), the engine options of "How
+ * the xAI engineering team cut Grok Bot latency to milliseconds", §3.3
+ * (model, device, KV cache dtype, maximum KV length): a 256-byte header (magic,
  * version 1, header bytes 256, dtype 1 = fp16, n_layers, d_model, n_heads,
  * n_kv_heads, head_dim, d_ff, vocab as i32, rope_base and norm_eps as f32,
  * flags 0), then fp16 row-major [out,in] tensors on 256-byte boundaries:
@@ -115,9 +124,13 @@ void rd_options_init(rd_options* opt);
  * wo[D,H*hd], ffn_norm[D], w_gate[F,D], w_up[F,D], w_down[D,F]; then
  * final_norm[D], lm_head[V,D]; the blob ends there.
  * blob: host, borrowed for the call only (copied and re-tiled).
+ * The QKV rows are re-ordered (RoPE pairs adjacent) and the gate/up rows
+ * interleaved once, here, into the layout the kernels stream.
  * Errors: INVALID_ARG (NULL, bad options), BAD_BLOB, UNSUPPORTED (a shape the
- * kernels do not cover: head_dim must be 64 or 128, d_model and d_ff
- * multiples of 8, n_heads a multiple of n_kv_heads), OUT_OF_MEMORY, DEVICE. */
+ * kernels do not cover: head_dim must be 64 or 128, n_heads / n_kv_heads 1,
+ * 2, 4 or 8, d_model and d_ff multiples of 8, d_model <= 4096,
+ * n_heads * head_dim <= 4096, d_ff <= 8192; max_batch > 1 with the
+ * persistent executor), OUT_OF_MEMORY, DEVICE. */
 rd_status rd_model_create(const void* blob, size_t blob_bytes, const rd_options* opt, rd_model** out);
 
 /* Release everything; NULL-safe. */
@@ -131,7 +144,11 @@ rd_status rd_reset(rd_model* m);
 /* Position of the next token to be decoded (the same for every sequence). */
 rd_status rd_get_position(const rd_model* m, int32_t* pos);
 
-/* One decode step.  tokens: host [batch] ids at the current position.
+/* One decode step: the per-token forward of "How the xAI engineering team
+ * cut Grok Bot latency to milliseconds", §2.1 (embedding, per layer RMSNorm,
+ * QKV, RoPE, attention over the cache, output projection, SwiGLU FFN; final
+ * norm, logits), with greedy sampling on the GPU ("Real-time LLM inference
+ * on standard GPUs", loss table).  tokens: host [batch] ids at the current position.
  * logits: host [batch*vocab] fp32 or NULL.  next: host [batch] greedy argmax
  * (lowest index on ties) or NULL.  batch must equal max_batch.
  * Errors: INVALID_ARG, CONTEXT_FULL (nothing changed), NUMERIC (a non-finite
@@ -148,7 +165,8 @@ rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, floa
 rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batch, int32_t n);
 
 /* n_steps greedy steps with the token fed back on the device (no host round
- * trip between steps).  first: host [batch], the token at the current
+ * trip between steps: the whole sequence is decoded without the CPU in the
+ * loop, "Real-time LLM inference on standard GPUs", last section).  first: host [batch], the token at the current
  * position.  out_tokens: host [n_steps*batch], step-major: the argmax of
  * every step.  Errors as rd_decode_step; CONTEXT_FULL if the steps do not fit. */
 rd_status rd_generate(rd_model* m, const int32_t* first, int32_t batch, int32_t n_steps, int32_t* out_tokens);
@@ -164,7 +182,9 @@ rd_status rd_generate_async(rd_model* m, const int32_t* first, int32_t batch, in
 rd_status rd_synchronize(rd_model* m);
 
 /* Copy the raw KV storage of (seq < max_batch, layer, which: 0 = K, 1 = V) into host
- * memory dst (capacity cap bytes).  Layout per format:
+ * memory dst (capacity cap bytes), in the formats of "How the xAI engineering
+ * team cut Grok Bot latency to milliseconds", §2.3 (E5M2) and "Grok-3 v3.2.4
+ * hot update deep dive", §3.2 (INT8 per 128-token segment).  Layout per format:
  *  FP16:  u16 [n_kv_heads][max_context][head_dim]
  *  E5M2:  u8  [n_kv_heads][max_context][head_dim]
  *  INT8:  u8 codes [n_kv_heads][max_context][head_dim], then
@@ -245,42 +265,69 @@ rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t
 
 /* Single-query attention of n_heads query heads over one sequence's cache
  * with grouped kv heads (query head h reads kv head h / (n_heads/n_kv_heads)):
- * out[h] = softmax(q[h] . K[g][0..L) * scale) V[g][0..L), computed as
- * partial softmaxes over at most `splits` key ranges merged by log-sum-exp.
- * q: device f32 [n_heads][hd]; K, V: device fp16 [n_kv_heads][ld][hd];
- * out: device f32 [n_heads][hd]; scale: the softmax scale (1/sqrt(hd) in the
- * model); hd 64 or 128; 1 <= L <= ld; 1 <= splits <= 256.  Uses a library
- * scratch buffer allocated on first use. */
+ * out[h] = softmax(q[h] . K^[g][0..L) * scale) V^[g][0..L), computed as
+ * partial softmaxes over at most `splits` key ranges merged by log-sum-exp,
+ * where K^, V^ are the rows as stored, dequantized ("How the xAI engineering
+ * team cut Grok Bot latency to milliseconds", §3.1: attention with a
+ * 1/sqrt(d) scale; "LLM inference architecture rebuild", §3.3: the softmax
+ * scale passed explicitly).  The step's own kernels, the cache read-only.
+ * q: device f32 [n_heads][hd]; out: device f32 [n_heads][hd].
+ * kv_format (rd_kv_format) and K, V (device, [n_kv_heads][ld][hd]):
+ *   FP16: fp16 rows;
+ *   FP8_E5M2: E5M2 bytes, read as the fp16 with that high byte (§2.3 of the
+ *     xAI page);
+ *   INT8_SEG128 ("Grok-3 v3.2.4 hot update deep dive", §3.2): u8 codes; the
+ *     rows of segment k < (L-1)/128 read as (code - zp) * scale with
+ *     (scale, zp) = k_meta/v_meta [n_kv_heads][ceil(ld/128)][2] (f32), the
+ *     rows of the open segment (positions (L-1)/128*128 .. L-1) come from
+ *     k_stage/v_stage, device u16 [n_kv_heads][128][hd] (fp16, row p % 128).
+ *     Other formats: the four pointers are ignored (may be NULL).
+ * scale: the softmax scale (1/sqrt(hd) in the model); hd 64 or 128;
+ * 1 <= L <= ld; 1 <= splits <= 256; n_heads <= 128.  q, K, V and the
+ * staging rows 16-byte aligned, the tables 8-byte aligned.  Uses a library
+ * scratch buffer (split partials), allocated on the device's first call and
+ * kept until the process ends: calls that overlap on one device (several
+ * streams or threads) race on it. */
+rd_status rd_attention(const float* q, const void* K, const void* V, const uint16_t* k_stage,
+                       const uint16_t* v_stage, const float* k_meta, const float* v_meta, float* out,
+                       int32_t n_heads, int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, int32_t kv_format,
+                       float scale, int32_t splits, void* stream);
+
+/* rd_attention with kv_format FP16 (same kernels, same scratch, same rules). */
 rd_status rd_attention_f16(const float* q, const void* K, const void* V, float* out, int32_t n_heads,
                            int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
                            void* stream);
 
 /* out[i] = E5M2 encoding of the fp16 value in[i] (round to nearest even on
- * the dropped mantissa bits, overflow to inf, NaN to quiet NaN).
+ * the dropped mantissa bits, overflow to inf, NaN to quiet NaN): the KV
+ * format of "How the xAI engineering team cut Grok Bot latency to
+ * milliseconds", §2.3, whose range §4.3 gives as +-57344.
  * in: device u16 [n]; out: device u8 [n]. */
 rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* stream);
 
-/* Segment quantization of n_seg independent segments of seg_elems fp16
- * values each: per segment min/max in fp32, scale=(max-min)/255 (1 when
- * max==min), zp=rint(-min/scale), code=clamp(rint(x/scale)+zp, 0, 255).
+/* Segment quantization ("Grok-3 v3.2.4 hot update deep dive", §3.2) of
+ * n_seg independent segments of seg_elems fp16 values each: per segment
+ * min/max in fp32, scale=(max-min)/255 (when max==min: |min|, or 1 for an
+ * all-zero segment, so that the value is kept exactly), zp=rint(-min/scale),
+ * code=clamp(rint(x/scale)+zp, 0, 255).
  * in: device u16 [n_seg][seg_elems]; codes: device u8 [n_seg][seg_elems];
  * meta: device f32 [n_seg][2] (scale, zp).  seg_elems <= 65536. */
 rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uint8_t* codes, float* meta,
                        void* stream);
 
-/* Average latency in microseconds of one grid barrier (one workgroup per
- * CU), measured over n back-to-back barriers with HIP events on the null
- * stream of `device` ("Real-time LLM inference on standard GPUs", loss
- * table: grid synchronisation between phases).  mode selects the scheme:
- * 0 two-level counter tree with resets and a generation word, 1 one
- * monotonic counter, 2 monotonic two-level counter tree, 3 packed
- * per-workgroup epoch flags polled by every workgroup, 4 the same with one
- * flag per cache line.  Errors: INVALID_ARG, DEVICE. */
-rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t mode, float* us_per_barrier);
-
-/* *out = index of the largest of v[0..n) (lowest index on ties).
- * v: device f32 [n]; out: device i32 [1]. */
+/* *out = index of the largest of v[0..n) (lowest index on ties): the greedy
+ * sampling the step keeps on the GPU ("Real-time LLM inference on standard
+ * GPUs", loss table).  v: device f32 [n]; out: device i32 [1].  Uses the
+ * library scratch of rd_attention (its own part of it): calls that overlap
+ * on one device race. */
 rd_status rd_argmax_f32(const float* v, int32_t n, int32_t* out, void* stream);
+
+/* Free the scratch buffers of rd_attention, rd_attention_f16 and
+ * rd_argmax_f32 on every device that has one (they are allocated again by
+ * the next call), after waiting for each such device to go idle; for a
+ * process that wants its device memory back before it exits.  No call that
+ * uses the scratch may be in flight or start meanwhile.  Errors: DEVICE. */
+rd_status rd_release_scratch(void);
 
 #ifdef __cplusplus
 }

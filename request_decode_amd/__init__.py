@@ -78,10 +78,12 @@ SIGNATURES = [
     ("rd_prefill", _I32, [_VP, _I32P, _I32, _I32]),
     ("rd_gemv_f16", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
+    ("rd_attention", _I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, C.c_float,
+                            _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
     ("rd_seg_quant", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
     ("rd_argmax_f32", _I32, [_VP, _I32, _VP, _VP]),
-    ("rd_debug_barrier_probe", _I32, [_I32, _I32, _I32, _FP]),
+    ("rd_release_scratch", _I32, []),
 ]
 
 _lib = None
@@ -292,6 +294,13 @@ def rd_attention_f16(q: int, K: int, V: int, out: int, n_heads: int, n_kv_heads:
     check(lib().rd_attention_f16(q, K, V, out, n_heads, n_kv_heads, hd, L, ld, scale, splits, stream or None))
 
 
+def rd_attention(q: int, K: int, V: int, out: int, n_heads: int, n_kv_heads: int, hd: int, L: int, ld: int,
+                 kv_format: str, scale: float, splits: int, k_stage: int = 0, v_stage: int = 0, k_meta: int = 0,
+                 v_meta: int = 0, stream: int = 0):
+    check(lib().rd_attention(q, K, V, k_stage or None, v_stage or None, k_meta or None, v_meta or None, out, n_heads,
+                             n_kv_heads, hd, L, ld, KV_FORMATS[kv_format], scale, splits, stream or None))
+
+
 def rd_e5m2_encode(inp: int, out: int, n: int, stream: int = 0):
     check(lib().rd_e5m2_encode(inp, out, n, stream or None))
 
@@ -304,7 +313,5 @@ def rd_argmax_f32(v: int, n: int, out: int, stream: int = 0):
     check(lib().rd_argmax_f32(v, n, out, stream or None))
 
 
-def rd_debug_barrier_probe(device: int = 0, n: int = 10000, mode: int = 1) -> float:
-    us = C.c_float()
-    check(lib().rd_debug_barrier_probe(device, n, mode, C.byref(us)))
-    return us.value
+def release_scratch():
+    check(lib().rd_release_scratch())

@@ -171,10 +171,12 @@ namespace {
 struct Tokens8 {
     int t[8];
 };
-__global__ void k_set_state(StepState* st, int pos, Tokens8 tk, int nb, int reset_gen) {
+// clear_err = 0 keeps the error bits of earlier steps, so that a run of
+// teacher-forced steps synchronised once reports an error of any of them.
+__global__ void k_set_state(StepState* st, int pos, Tokens8 tk, int nb, int reset_gen, int clear_err) {
     st->pos = pos;
     for (int b = 0; b < nb; ++b) st->token[b] = tk.t[b];
-    st->err = 0;
+    if (clear_err) st->err = 0;
     if (reset_gen) st->n_gen = 0;
 }
 
@@ -185,9 +187,10 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 void free_model(rd_model* m) {
     if (!m) return;
     (void)hipSetDevice(m->dev);
+    // work still queued (rd_generate_async) may be running the graph
+    if (m->stream) (void)hipStreamSynchronize(m->stream);
     if (m->gexec) (void)hipGraphExecDestroy(m->gexec);
     if (m->graph) (void)hipGraphDestroy(m->graph);
-    if (m->stream) (void)hipStreamSynchronize(m->stream);
     (void)hipFree(m->wbuf);
     (void)hipFree(m->kc);
     (void)hipFree(m->vc);
@@ -246,10 +249,11 @@ rd_status step_enqueue(rd_model* m) {
 
 // Tokens of every sequence (host [max_batch], or NULL for zeros) and the
 // position into the device step state.
-hipError_t set_state(rd_model* m, const int32_t* tokens) {
+hipError_t set_state(rd_model* m, const int32_t* tokens, bool clear_err = true) {
     Tokens8 tk{};
     for (int b = 0; b < m->opt.max_batch; ++b) tk.t[b] = tokens ? tokens[b] : 0;
-    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tk, m->opt.max_batch, 1);
+    hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tk, m->opt.max_batch, 1,
+                       clear_err ? 1 : 0);
     return hipGetLastError();
 }
 bool tokens_ok(const rd_model* m, const int32_t* t, int n) {
@@ -691,7 +695,7 @@ extern "C" rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batc
     const int32_t ex = m->opt.executor;
     if (ex == RD_EXEC_PERSISTENT) m->opt.executor = RD_EXEC_GRAPH;
     for (int i = 0; i < n && !st; ++i) {
-        hipError_t e = set_state(m, tokens + (size_t)i * batch);
+        hipError_t e = set_state(m, tokens + (size_t)i * batch, i == 0);
         if (e != hipSuccess) st = dev_fail(m, "k_set_state", e);
         else if (!(st = step_enqueue(m))) m->host_pos += 1;
     }
@@ -867,6 +871,20 @@ hipError_t get_scratch(Scratch** out) {
 }
 }  // namespace
 
+extern "C" rd_status rd_release_scratch(void) {
+    std::lock_guard<std::mutex> lk(g_scr_mu);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(RD_ERR_DEVICE, "hipGetDevice failed");
+    for (int d = 0; d < 64; ++d) {
+        if (!g_scr[d].part) continue;
+        if (hipSetDevice(d) != hipSuccess || hipDeviceSynchronize() != hipSuccess || hipFree(g_scr[d].part) != hipSuccess)
+            return fail(RD_ERR_DEVICE, "releasing the scratch of device " + std::to_string(d) + " failed");
+        g_scr[d] = Scratch{};
+    }
+    if (hipSetDevice(cur) != hipSuccess) return fail(RD_ERR_DEVICE, "hipSetDevice failed");
+    return RD_OK;
+}
+
 #define K_TRY(expr)                                                                                  \
     do {                                                                                             \
         hipError_t e_ = (expr);                                                                      \
@@ -889,37 +907,78 @@ extern "C" rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t
     return RD_OK;
 }
 
-extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void* Vc, float* out, int32_t H,
-                                      int32_t Hk, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
-                                      void* stream) {
-    if (!q || !Kc || !Vc || !out) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
-    if (hd != 64 && hd != 128) return fail(RD_ERR_INVALID_ARG, "hd must be 64 or 128");
-    if (H < 1 || Hk < 1 || H % Hk || H > SCR_HEADS) return fail(RD_ERR_INVALID_ARG, "bad head counts");
+namespace {
+// Checks and launches the step's attention (split partials, then the
+// log-sum-exp merge) over a caller's cache, with the partials in `part`
+// (H * splits * (hd + 2) floats) and the position word in `posw`.
+rd_status attention_call(const float* q, const void* Kc, const void* Vc, const uint16_t* kst, const uint16_t* vst,
+                         const float* kmeta, const float* vmeta, float* out, int32_t H, int32_t Hk, int32_t hd,
+                         int32_t L, int32_t ld, int32_t kvf, float scale, int32_t splits, hipStream_t st,
+                         float* part, int* posw) {
     const int G = H / Hk;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RD_ERR_INVALID_ARG, "n_heads/n_kv_heads must be 1, 2, 4 or 8");
-    if (L < 1 || L > ld) return fail(RD_ERR_INVALID_ARG, "need 1 <= L <= ld");
-    if (splits < 1 || splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "splits out of range");
-    if (((uintptr_t)q | (uintptr_t)Kc | (uintptr_t)Vc) & 15) return fail(RD_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
-    Scratch* s = nullptr;
-    K_TRY(get_scratch(&s));
-    hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, st, s->pos, L - 1);
+    hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, st, posw, L - 1);
     K_TRY(hipGetLastError());
     AttnArgs A{};
     A.q = q;
     A.out = out;
     A.kc = Kc;
     A.vc = Vc;
-    A.part = s->part;
-    A.pos_ptr = s->pos;
+    if (kvf == KV_INT8) {
+        A.kst = const_cast<uint16_t*>(kst);
+        A.vst = const_cast<uint16_t*>(vst);
+        A.kmeta = const_cast<float*>(kmeta);
+        A.vmeta = const_cast<float*>(vmeta);
+    }
+    A.part = part;
+    A.pos_ptr = posw;
     A.ld = ld;
-    A.nseg = 0;
+    A.nseg = (ld + SEG - 1) / SEG;
     A.H = H;
     A.Hk = Hk;
     A.S = splits;
     A.scale = scale;
-    K_TRY(launch_attention_f16(A, hd, G, st));
+    A.seal = 0;   // read-only: the caller's cache is never written
+    K_TRY(launch_attention(A, kvf, hd, G, st));
     return RD_OK;
+}
+
+rd_status attention_args_ok(const float* q, const void* Kc, const void* Vc, const uint16_t* kst, const uint16_t* vst,
+                            const float* kmeta, const float* vmeta, const float* out, int32_t H, int32_t Hk,
+                            int32_t hd, int32_t L, int32_t ld, int32_t kvf, int32_t splits) {
+    if (!q || !Kc || !Vc || !out) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (kvf < RD_KV_FP16 || kvf > RD_KV_INT8_SEG128) return fail(RD_ERR_INVALID_ARG, "bad kv_format");
+    if (kvf == RD_KV_INT8_SEG128 && (!kst || !vst || !kmeta || !vmeta))
+        return fail(RD_ERR_INVALID_ARG, "the INT8 cache needs staging rows and (scale, zero point) tables");
+    if (hd != 64 && hd != 128) return fail(RD_ERR_INVALID_ARG, "hd must be 64 or 128");
+    if (H < 1 || Hk < 1 || H % Hk || H > SCR_HEADS) return fail(RD_ERR_INVALID_ARG, "bad head counts");
+    const int G = H / Hk;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RD_ERR_INVALID_ARG, "n_heads/n_kv_heads must be 1, 2, 4 or 8");
+    if (L < 1 || L > ld) return fail(RD_ERR_INVALID_ARG, "need 1 <= L <= ld");
+    if (splits < 1 || splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "splits out of range");
+    if (((uintptr_t)q | (uintptr_t)Kc | (uintptr_t)Vc | (uintptr_t)kst | (uintptr_t)vst) & 15)
+        return fail(RD_ERR_INVALID_ARG, "q, K, V and the staging rows must be 16-byte aligned");
+    if (((uintptr_t)kmeta | (uintptr_t)vmeta) & 7) return fail(RD_ERR_INVALID_ARG, "meta tables must be 8-byte aligned");
+    return RD_OK;
+}
+}  // namespace
+
+extern "C" rd_status rd_attention(const float* q, const void* Kc, const void* Vc, const uint16_t* kst,
+                                  const uint16_t* vst, const float* kmeta, const float* vmeta, float* out, int32_t H,
+                                  int32_t Hk, int32_t hd, int32_t L, int32_t ld, int32_t kv_format, float scale,
+                                  int32_t splits, void* stream) {
+    rd_status r = attention_args_ok(q, Kc, Vc, kst, vst, kmeta, vmeta, out, H, Hk, hd, L, ld, kv_format, splits);
+    if (r) return r;
+    Scratch* s = nullptr;
+    K_TRY(get_scratch(&s));
+    return attention_call(q, Kc, Vc, kst, vst, kmeta, vmeta, out, H, Hk, hd, L, ld, kv_format, scale, splits,
+                          (hipStream_t)stream, s->part, s->pos);
+}
+
+extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void* Vc, float* out, int32_t H,
+                                      int32_t Hk, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
+                                      void* stream) {
+    return rd_attention(q, Kc, Vc, nullptr, nullptr, nullptr, nullptr, out, H, Hk, hd, L, ld, RD_KV_FP16, scale,
+                        splits, stream);
 }
 
 extern "C" rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* stream) {
@@ -935,21 +994,6 @@ extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg
         return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, seg_elems a multiple of 8 in [8, 65536]");
     if (((uintptr_t)in | (uintptr_t)codes) & 15) return fail(RD_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
     K_TRY(launch_seg_quant(in, n_seg, seg_elems, codes, meta, (hipStream_t)stream));
-    return RD_OK;
-}
-
-extern "C" rd_status rd_debug_barrier_probe(int32_t device, int32_t n, int32_t mode, float* us) {
-    if (!us || n < 1 || n > (1 << 20)) return fail(RD_ERR_INVALID_ARG, "need us != NULL and 1 <= n <= 2^20");
-    if (mode < 0 || mode > 1) return fail(RD_ERR_INVALID_ARG, "mode must be 0 or 1");
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev)
-        return fail(RD_ERR_INVALID_ARG, "bad device");
-    K_TRY(hipSetDevice(device));
-    hipDeviceProp_t prop;
-    K_TRY(hipGetDeviceProperties(&prop, device));
-    int errbits = 0;
-    K_TRY(barrier_probe(prop.multiProcessorCount, n, mode, us, &errbits));
-    if (errbits & ERR_STALL) return fail(RD_ERR_DEVICE, "a probe wait timed out");
     return RD_OK;
 }
 

@@ -48,6 +48,7 @@ struct AttnArgs {
     const int* pos_ptr;      // L = *pos_ptr + 1
     int ld, nseg, H, Hk, S;
     float scale;
+    int seal;                // INT8: the merge seals a segment the step fills (0: the cache is read-only)
     // B sequences (grid dimension y): sequence b's q, out, part and cache
     // regions lie b strides past sequence 0's (strides in elements of each
     // buffer, the cache ones in bytes)
@@ -142,6 +143,7 @@ __host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
     T.S = A.S;
     T.scale = A.scale;
     T.nseq = A.B;
+    T.seal = 1;
     T.q_bstride = (size_t)A.H * A.hd;
     T.part_bstride = (size_t)A.H * A.S * (A.hd + 2);
     T.kv_bstride = A.kv_bstride;
@@ -174,7 +176,6 @@ enum { TR_RECV = 0, TR_STAGED = 1, TR_DONE = 2, TR_PUB = 3 };
 bool persistent_supported(const StepArgs& A);
 hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, hipStream_t s);
 hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg);
-hipError_t barrier_probe(int nwg, int n, int mode, float* us, int* errbits);
 
 // Host launchers (rd_kernels.hip).
 int kch_for(int K);
@@ -194,7 +195,7 @@ hipError_t launch_gemm_b8_swiglu(const _Float16* Wgu, const _Float16* x, int ldx
 // The batch step's QKV GEMM of layer `layer` over A.xh (B rows), with RoPE
 // and the K/V append of each sequence at A.st->pos as its epilogue.
 hipError_t launch_gemm_b8_qkv(const StepArgs& A, int layer, const _Float16* Wqkv, hipStream_t s);
-hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s);
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,
                             hipStream_t s);

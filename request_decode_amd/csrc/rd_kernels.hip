@@ -83,7 +83,7 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
     const int lane = lane_id(), j = lane % Geo::LPR;
     const int p0 = s * chunk, p1 = min(L, p0 + chunk), open0 = pos / SEG * SEG;
     KvBuf<HD> kb, vb;
-    attn_wave_first<HD, KVF, false, NW>(T, g, p0, p1, open0, w, kb, vb);
+    attn_wave_first<HD, KVF, false, NW>(T, g, p0, p1, open0, pos, w, kb, vb);
     const float qs = T.scale * LOG2E;
     float qv[G][8];
 #pragma unroll
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
         for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
     AttnAcc<HD, G> acc;
     acc.clear();
-    attn_wave_run<HD, G, KVF, false, NW>(T, g, p0, p1, open0, w, qv, acc, kb, vb,
+    attn_wave_run<HD, G, KVF, false, NW>(T, g, p0, p1, open0, pos, w, qv, acc, kb, vb,
                                          [](int, float (&)[Geo::U][8], float (&)[Geo::U][8]) {});
     acc.finish();
     attn_part_store<HD, G>(s_att, w, acc);
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(WG) void k_merge(AttnArgs T0) {
     }
     T.out[h * HD + d] = num / mw.den;
     if constexpr (KVF == KV_INT8) {
-        if ((pos + 1) % SEG == 0 && part == 0 && h % G == 0) seal_head<HD, false>(T, h / G, pos);
+        if (T.seal && (pos + 1) % SEG == 0 && part == 0 && h % G == 0) seal_head<HD, false>(T, h / G, pos);
     }
 }
 
@@ -390,8 +390,8 @@ hipError_t launch_step(const StepArgs& A, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attention_f16(const AttnArgs& A, int hd, int G, hipStream_t s) {
-    return launch_attn_any(A, KV_FP16, hd, G, s);
+hipError_t launch_attention(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s) {
+    return launch_attn_any(A, kvfmt, hd, G, s);
 }
 
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s) {

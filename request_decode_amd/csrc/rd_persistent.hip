@@ -622,7 +622,7 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
         }
         AttnAcc<HD, G> acc;
         acc.clear();
-        attn_wave_run<HD, G, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, w, qv, acc, kb, vb,
+        attn_wave_run<HD, G, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sp.pos, w, qv, acc, kb, vb,
                                              [&](int pb, float (&kf)[AttnGeo<HD>::U][8],
                                                  float (&vf)[AttnGeo<HD>::U][8]) {
                                                  fix_new_row<HD, G>(pb, sp.pos, kn, vn, kf, vf);
@@ -649,7 +649,7 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
             KvBuf<HD> kb, vb;
             // after its QKV rows: the raw K/V rows of its first attention batch
             stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr, [&] {
-                if (sp.t >= 0) attn_wave_first<HD, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sw, kb, vb);
+                if (sp.t >= 0) attn_wave_first<HD, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sp.pos, sw, kb, vb);
             });
             attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, vb);
             stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none);
@@ -992,58 +992,6 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
         stream_role<KD, KA, KF, HD, G, KVF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, s_nev);
 }
 
-// ---- exchange latency probe ------------------------------------------------------------
-// mode 0: every workgroup raises its epoch flag, one wave polls all flags,
-// then the workgroup reads N plain (agent-coherent) words; mode 1: every
-// workgroup publishes its share of N tagged words and polls all N (the
-// decode kernel's scheme; rounds alternate between two buffers, because
-// back-to-back rounds of one object, unlike the decode step's phases, are not
-// separated by a read of everyone's output).  N = 2048 words, n rounds.
-__global__ __launch_bounds__(WG) void k_xchg_probe(uint64_t* words, int* flags, int n, int mode, StepArgs A,
-                                                   int spin_limit) {
-    constexpr int N = 2048;
-    const int lane = lane_id(), b = blockIdx.x, nwg = gridDim.x, per = N / nwg;
-    Waiter wt{A.abort_word, &A.st->err, spin_limit, 0};
-    float acc = 0.f;
-    for (int r = 0; r < n; ++r) {
-        const uint32_t tag = (uint32_t)r + 1u;
-        if (threadIdx.x < WAVE) {
-            if (mode == 0) {
-                for (int i = lane; i < per; i += WAVE)
-                    st_agent(reinterpret_cast<float*>(words) + b * per + i, (float)r);
-                drain_vmem();
-                if (lane == 0) st_agent(&flags[b], (int)tag);
-                wt.n = 0;
-                while (true) {
-                    bool ok = true;
-                    int f[LB_MAX / WAVE];
-#pragma unroll
-                    for (int k = 0; k < LB_MAX / WAVE; ++k)
-                        if (k * WAVE + lane < nwg) f[k] = ld_agent(&flags[k * WAVE + lane]);
-#pragma unroll
-                    for (int k = 0; k < LB_MAX / WAVE; ++k)
-                        if (k * WAVE + lane < nwg) ok &= (int)((uint32_t)f[k] - tag) >= 0;
-                    if (__all(ok) || !wt.again()) break;
-                }
-                float v[N / WAVE];
-#pragma unroll
-                for (int k = 0; k < N / WAVE; ++k) v[k] = ld_agent(reinterpret_cast<const float*>(words) + k * WAVE + lane);
-#pragma unroll
-                for (int k = 0; k < N / WAVE; ++k) acc += v[k];
-            } else {
-                uint64_t* buf = words + (r & 1) * N;
-                for (int i = lane; i < per; i += WAVE) publish(&buf[b * per + i], (float)r, tag);
-                float xr[4][8];
-                poll_vec<4>(wt, buf, N, tag, xr);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) acc += xr[c][0];
-            }
-        }
-        lds_barrier();
-    }
-    if (acc == -1.0f) A.x[0] = acc;   // keeps the loads alive
-}
-
 // ---- host side ------------------------------------------------------------------------
 namespace {
 struct Shape {
@@ -1126,43 +1074,6 @@ hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, h
     PersistArgs p = P;
     void* args[] = {&a, &p};
     return hipLaunchCooperativeKernel(k, dim3(nwg), dim3(PWG), args, 0, s);
-}
-
-hipError_t barrier_probe(int nwg, int n, int mode, float* us, int* errbits) {
-    if (nwg < 1 || nwg > LB_MAX || 2048 % nwg != 0 || (mode != 0 && mode != 1)) return hipErrorInvalidValue;
-    uint8_t* buf = nullptr;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    hipError_t e;
-    const size_t bytes = 2 * 2048 * 8 + LB_MAX * 4 + sizeof(StepState) + 256;
-    if ((e = hipMalloc(&buf, bytes)) != hipSuccess) return e;
-    if ((e = hipMemset(buf, 0, bytes)) != hipSuccess) goto out;
-    (void)hipEventCreate(&e0);
-    (void)hipEventCreate(&e1);
-    {
-        uint64_t* words = reinterpret_cast<uint64_t*>(buf);
-        int* flags = reinterpret_cast<int*>(buf + 2 * 2048 * 8);
-        StepArgs A{};
-        A.st = reinterpret_cast<StepState*>(buf + 2 * 2048 * 8 + LB_MAX * 4);
-        A.abort_word = &A.st->pad;
-        A.x = reinterpret_cast<float*>(buf + bytes - 256);
-        int nn = n, md = mode, spin = 1 << 22;
-        void* args[] = {&words, &flags, &nn, &md, &A, &spin};
-        (void)hipEventRecord(e0, nullptr);
-        e = hipLaunchCooperativeKernel((const void*)&k_xchg_probe, dim3(nwg), dim3(WG), args, 0, nullptr);
-        (void)hipEventRecord(e1, nullptr);
-        if (e == hipSuccess) e = hipEventSynchronize(e1);
-        float ms = 0.f;
-        (void)hipEventElapsedTime(&ms, e0, e1);
-        *us = ms * 1000.0f / (float)n;
-        StepState st{};
-        (void)hipMemcpy(&st, A.st, sizeof st, hipMemcpyDeviceToHost);
-        *errbits = st.err;
-    }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
-out:
-    (void)hipFree(buf);
-    return e;
 }
 
 }  // namespace rd

@@ -270,8 +270,11 @@ __device__ __forceinline__ void split_plan(int L, int S, int& chunk, int& nact) 
 // dequantization.  Under P the reads that can meet a stale line are
 // agent-coherent: INT8 open-segment rows (the staging buffer is reused every
 // 128 steps), INT8 scales (several segments share a line), head_dim-64 E5M2
-// rows (two rows share a 128-byte line).  fp16 rows and sealed codes are
-// written once and first read afterwards.
+// rows (two rows share a 128-byte line, so fetching an older row can bring in
+// the line of the row being written).  The other rows (fp16 rows, head_dim-128
+// E5M2 rows, sealed codes: whole lines of one row, or of one sealed segment)
+// are first fetched in a step after the one that wrote them: the row of the
+// current step is never fetched from the cache under P (kv_batch_raw).
 struct KvRaw {
     u4v d;         // fp16: 8 halves; E5M2: 8 bytes in d.x, d.y; INT8: codes in d.x, d.y or 8 fp16
     float scale;   // INT8 sealed row: its segment's scale and zero point; < 0: an fp16 open-segment row
@@ -289,7 +292,7 @@ __device__ __forceinline__ KvRaw kv_raw(const AttnArgs& A, int which, int g, int
             reinterpret_cast<const u4v*>(reinterpret_cast<const _Float16*>(base) + row * HD + j * 8));
     } else if constexpr (KVF == KV_E5M2) {
         const uint64_t* src = reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(base) + row * HD + j * 8);
-        const uint64_t u = P ? ld_agent(src) : *src;
+        const uint64_t u = (P && HD == 64) ? ld_agent(src) : __builtin_nontemporal_load(src);
         r.d = u4v{(unsigned)u, (unsigned)(u >> 32), 0u, 0u};
     } else {
         if (p < open0) {
@@ -334,8 +337,14 @@ __device__ __forceinline__ int batch_row(int pb, int u, int slot) { return pb + 
 
 // The raw K and V elements of this lane's U rows of the batch starting at pb
 // (rows at or past p1 read row p0 instead; they are masked when reduced).
+// Under P (one launch, several steps), row pos, the one this step writes, is
+// not fetched from the fp16 or E5M2 cache either: its value comes from the
+// exchange (the caller's fix), and a fetch racing its store could leave a copy
+// of the line from before the store in this XCD's L2, which a later step of
+// the same launch would then read.  Such rows fetch an older row instead (p0,
+// or pos - 1 when the split starts at pos); at pos 0 nothing is fetched.
 template <int HD, int KVF, bool P>
-__device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, int p0, int p1, int open0,
+__device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, int p0, int p1, int open0, int pos,
                                              KvRaw (&kr)[AttnGeo<HD>::U], KvRaw (&vr)[AttnGeo<HD>::U]) {
     using Geo = AttnGeo<HD>;
     const int lane = lane_id(), slot = lane / Geo::LPR, j = lane % Geo::LPR;
@@ -388,10 +397,18 @@ __device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, i
             }
         }
     } else {
+        if constexpr (P) {
+            if (pos == 0) {   // the only row is the new one (wave-uniform)
+#pragma unroll
+                for (int u = 0; u < Geo::U; ++u) kr[u] = vr[u] = KvRaw{u4v{0u, 0u, 0u, 0u}, -1.f, 0.f};
+                return;
+            }
+        }
+        const int alt = P && p0 == pos ? pos - 1 : p0;
 #pragma unroll
         for (int u = 0; u < Geo::U; ++u) {
             const int p = batch_row<HD>(pb, u, slot);
-            const int pc = p < p1 ? p : p0;
+            const int pc = p < p1 && !(P && p == pos) ? p : alt;
             kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
             vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
         }
@@ -511,27 +528,27 @@ template <int HD>
 using KvBuf = KvRaw[3][AttnGeo<HD>::U];
 
 template <int HD, int KVF, bool P, int NW>
-__device__ __forceinline__ void attn_wave_first(const AttnArgs& T, int g, int p0, int p1, int open0, int w,
+__device__ __forceinline__ void attn_wave_first(const AttnArgs& T, int g, int p0, int p1, int open0, int pos, int w,
                                                 KvBuf<HD>& kb, KvBuf<HD>& vb) {
     const int pb = p0 + w * AttnGeo<HD>::BATCH;
-    if (pb < p1) kv_batch_raw<HD, KVF, P>(T, g, pb, p0, p1, open0, kb[0], vb[0]);
+    if (pb < p1) kv_batch_raw<HD, KVF, P>(T, g, pb, p0, p1, open0, pos, kb[0], vb[0]);
 }
 template <int HD, int G, int KVF, bool P, int NW, class Fix>
-__device__ __forceinline__ void attn_wave_run(const AttnArgs& T, int g, int p0, int p1, int open0, int w,
+__device__ __forceinline__ void attn_wave_run(const AttnArgs& T, int g, int p0, int p1, int open0, int pos, int w,
                                               const float (&qv)[G][8], AttnAcc<HD, G>& acc, KvBuf<HD>& kb,
                                               KvBuf<HD>& vb, Fix fix) {
     using Geo = AttnGeo<HD>;
     constexpr int STEP = NW * Geo::BATCH;
     const int pf = p0 + w * Geo::BATCH;
     if (pf >= p1) return;
-    if (pf + STEP < p1) kv_batch_raw<HD, KVF, P>(T, g, pf + STEP, p0, p1, open0, kb[1], vb[1]);
+    if (pf + STEP < p1) kv_batch_raw<HD, KVF, P>(T, g, pf + STEP, p0, p1, open0, pos, kb[1], vb[1]);
     for (int i = 0;; i += 3) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
             const int pb = pf + (i + r) * STEP;
             if (pb >= p1) return;
             const int pn = pb + 2 * STEP;
-            if (pn < p1) kv_batch_raw<HD, KVF, P>(T, g, pn, p0, p1, open0, kb[(r + 2) % 3], vb[(r + 2) % 3]);
+            if (pn < p1) kv_batch_raw<HD, KVF, P>(T, g, pn, p0, p1, open0, pos, kb[(r + 2) % 3], vb[(r + 2) % 3]);
             float kf[Geo::U][8], vf[Geo::U][8];
             bool valid[Geo::U];
             kv_batch_cvt<HD, KVF>(pb, p1, kb[r], vb[r], kf, vf, valid);
@@ -642,8 +659,8 @@ __device__ __forceinline__ void merge_acc(float& num, int c, const MergeW& mw, c
 // Adaptive-range quantization of one segment of n fp16 values ("Grok-3
 // v3.2.4 hot update deep dive", §3.2): scale = (max-min)/255,
 // zp = round(-min/scale), code = clamp(round(x/scale) + zp, 0, 255), all in
-// fp32 with IEEE division and round-half-to-even (rint); scale 1 when
-// max == min.  n % 8 == 0.  Under P the inputs are read and the codes and
+// fp32 with IEEE division and round-half-to-even (rint); when max == min,
+// scale |min| (1 for zeros), so the value is reproduced exactly.  n % 8 == 0.  Under P the inputs are read and the codes and
 // (scale, zp) written agent-coherently.
 template <bool P>
 __device__ __forceinline__ void seal_segment(const uint16_t* __restrict__ in, int n, uint8_t* __restrict__ codes,
@@ -666,7 +683,9 @@ __device__ __forceinline__ void seal_segment(const uint16_t* __restrict__ in, in
     mn = wave_min(mn);
     mx = wave_max(mx);
     float scale = (mx - mn) / 255.0f;
-    if (!(scale > 0.0f)) scale = 1.0f;
+    // one repeated value: its magnitude is the unit (every code 0, exact);
+    // an all-zero segment takes scale 1
+    if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;
     const float zp = rintf(-mn / scale);
     for (int i = lane * 8; i < n; i += 512) {
         const h8 v = ld8h(i);

@@ -52,6 +52,10 @@ def main():
     torch.add(src, 0.0, out=dst)         # an elementwise kernel: n bytes read, n written
     torch.cuda.synchronize()
     print(f"copy: {n} bytes read and {n} bytes written", flush=True)
+    # device memory handed back before the interpreter's teardown
+    del src, dst
+    rd.release_scratch()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -164,3 +164,85 @@ def test_argmax_exact(rd, orc):
         rd.rd_argmax_f32(vd.data_ptr(), n, out.data_ptr())
         sync()
         assert int(out.item()) == orc.argmax(v.astype(np.float64)), n
+
+
+# ---- attention over the 8-bit caches (the step's k_attn / k_merge for E5M2 and INT8) -------
+
+def _e5m2_bytes(rng, shape):
+    # E5M2 codes with exponent fields 10..16 (magnitudes 2^-5 .. 3.5), random
+    # sign and fraction: finite values of the cache's own range
+    s = rng.integers(0, 2, shape, dtype=np.uint8) << 7
+    e = rng.integers(10, 17, shape, dtype=np.uint8) << 2
+    f = rng.integers(0, 4, shape, dtype=np.uint8)
+    return s | e | f
+
+
+def _int8_cache(rng, Hk, ld, hd, L):
+    """Codes, per-segment (scale, zero point) and the open segment's fp16
+    staging rows of an INT8 cache holding L positions."""
+    nseg = -(-ld // 128)
+    codes = rng.integers(0, 256, (Hk, ld, hd), dtype=np.uint8)
+    meta = np.empty((Hk, nseg, 2), np.float32)
+    meta[..., 0] = rng.uniform(0.004, 0.03, (Hk, nseg)).astype(np.float32)
+    meta[..., 1] = rng.integers(40, 216, (Hk, nseg)).astype(np.float32)
+    stage = rng.standard_normal((Hk, 128, hd)).astype(np.float16)
+    return codes, meta, stage
+
+
+def _dequant_rows(orc, kv, parts, g, L):
+    """The oracle's view of rows 0..L-1 of kv head g as attended (binary64)."""
+    if kv == "e5m2":
+        return orc.h2d(orc.h_from_e5m2(parts["rows"][g, :L]))
+    codes, meta, stage = parts["rows"], parts["meta"], parts["stage"]
+    open0 = (L - 1) // 128 * 128
+    out = np.empty((L, codes.shape[2]), np.float64)
+    for seg in range(open0 // 128):
+        out[seg * 128:(seg + 1) * 128] = orc.seg_dequant(codes[g, seg * 128:(seg + 1) * 128], *meta[g, seg])
+    for p in range(open0, L):
+        out[p] = orc.h2d(stage[g, p % 128].view(np.uint16))
+    return out
+
+
+@pytest.mark.parametrize("kv", ["e5m2", "int8"])
+@pytest.mark.parametrize("H,Hk,hd,L,splits", [(16, 8, 128, 1, 32), (16, 8, 128, 128, 32), (16, 8, 128, 129, 7),
+                                              (16, 8, 128, 700, 32), (16, 8, 128, 2000, 5), (16, 8, 128, 8320, 32),
+                                              (4, 4, 64, 300, 64), (8, 2, 64, 1000, 3)])
+def test_attention_8bit_vs_oracle(rd, orc, kv, H, Hk, hd, L, splits):
+    """k_attn / k_merge for the E5M2 and INT8 caches (the 2B model's
+    128-dim, two-query-head groups up to 8320 keys, the config-5 context)
+    against the oracle's attention over the same rows dequantized by the
+    oracle's own decoders."""
+    import torch
+    print(f"attention {kv} H={H} Hk={Hk} hd={hd} L={L} S={splits}", flush=True)
+    rng = np.random.default_rng(L * 7 + H + (kv == "int8"))
+    ld = L + 77
+    q = rng.standard_normal((H, hd)).astype(np.float32)
+    if kv == "e5m2":
+        parts = {"rows": _e5m2_bytes(rng, (Hk, ld, hd))}
+        vparts = {"rows": _e5m2_bytes(rng, (Hk, ld, hd))}
+    else:
+        c, m, s = _int8_cache(rng, Hk, ld, hd, L)
+        parts = {"rows": c, "meta": m, "stage": s}
+        c, m, s = _int8_cache(rng, Hk, ld, hd, L)
+        vparts = {"rows": c, "meta": m, "stage": s}
+    out = torch.full((H, hd), float("nan"), dtype=torch.float32, device="cuda")
+    qd, Kd, Vd = dev(q), dev(parts["rows"]), dev(vparts["rows"])
+    extra = {}
+    if kv == "int8":
+        ks, vs = dev(parts["stage"].view(np.int16)), dev(vparts["stage"].view(np.int16))
+        km, vm = dev(parts["meta"]), dev(vparts["meta"])
+        extra = dict(k_stage=ks.data_ptr(), v_stage=vs.data_ptr(), k_meta=km.data_ptr(), v_meta=vm.data_ptr())
+    rd.rd_attention(qd.data_ptr(), Kd.data_ptr(), Vd.data_ptr(), out.data_ptr(), H, Hk, hd, L, ld, kv,
+                    float(1.0 / np.sqrt(hd)), splits, **extra)
+    sync()
+    got = out.cpu().numpy().astype(np.float64)
+    # the cache is read-only: an INT8 call at a segment end seals nothing
+    assert np.array_equal(Kd.cpu().numpy(), parts["rows"])
+    G = H // Hk
+    for g in range(Hk):
+        Kr = _dequant_rows(orc, kv, parts, g, L)
+        Vr = _dequant_rows(orc, kv, vparts, g, L)
+        vmax = max(1.0, float(np.abs(Vr).max()))
+        for h in range(g * G, (g + 1) * G):
+            ref = orc.attention(q[h].astype(np.float64), Kr, Vr)
+            assert np.allclose(got[h], ref, rtol=2e-5, atol=2e-5 * vmax), (g, h, np.abs(got[h] - ref).max())
