@@ -95,15 +95,18 @@ def test_2b_decode_512_prompt_256_steps_teacher_forced(rd, orc, blob2b):
     assert n == 768 and graded > 100
 
 
-def _e5m2_within_one_step(orc, g, o):
-    """E5M2 bytes whose values differ by at most one step of the format at
-    the larger magnitude: 2^(e-2) for a normal value with exponent e, 2^-16
-    in the subnormal range (values of opposite sign near zero included)."""
+def _e5m2_close(orc, g, o):
+    """E5M2 bytes g (the GPU's) and o (the oracle's encoding of its binary64
+    row) whose values differ by at most the layer-0 row tolerance of the
+    unrounded values (2e-3 + 2e-3 |x|: the fp16 GEMV operand, see the fp16
+    row checks) plus one step of the format at the larger magnitude (each
+    side rounds by at most half a step): a step is 2^(e-2) for a normal
+    value with exponent e, 2^-16 in the subnormal range."""
     dg = orc.h2d(orc.h_from_e5m2(g))
     do = orc.h2d(orc.h_from_e5m2(o))
     a = np.maximum(np.abs(dg), np.abs(do))
     step = np.where(a < 2.0 ** -14, 2.0 ** -16, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 2))
-    return np.abs(dg - do) <= step
+    return np.abs(dg - do) <= 2e-3 + 2e-3 * np.abs(do) + step
 
 
 @pytest.mark.parametrize("kv", ["e5m2", "int8"])
@@ -126,7 +129,8 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
     oracle's quantizer, run on the same staging rows, must give the GPU's
     codes and (scale, zero point) bit for bit.  The rows themselves are
     checked at layer 0 against the oracle's own layer-0 path: E5M2 values
-    within one step of the format, INT8 staging rows within the fp16 tolerance."""
+    within the fp16 row tolerance plus one step of the format, INT8
+    staging rows within the fp16 tolerance."""
     prompt = synth.prompt(105, 300, SHAPE.vocab)
     n = 320
     ctx = n + 8
@@ -181,7 +185,7 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
             h = orc.d2h(ref)
             got = l0_rows[i, w]
             if kv == "e5m2":
-                ok = _e5m2_within_one_step(orc, got, orc.e5m2_from_h(h))
+                ok = _e5m2_close(orc, got, orc.e5m2_from_h(h))
                 assert np.all(ok), (i, w, got[~ok][:4], orc.e5m2_from_h(h)[~ok][:4])
             else:
                 g64 = got.view(np.float16).astype(np.float64)
