@@ -293,6 +293,21 @@ rd_status rd_attention(const float* q, const void* K, const void* V, const uint1
                        int32_t n_heads, int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, int32_t kv_format,
                        float scale, int32_t splits, void* stream);
 
+/* rd_attention for callers that cannot allocate device memory (code under
+ * hipGraph stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the split partials in a
+ * fixed 4 MiB device array of the library instead of an allocated scratch.
+ * Nothing is allocated, on the first call either (the array's address on the
+ * current device is looked up then).  Limit: 256 + n_heads * splits *
+ * (hd + 2) * 4 bytes <= 4 MiB, else INVALID_ARG with nothing enqueued.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on
+ * one GPU (several streams or threads) race; calls in order on one stream
+ * are safe (each call rewrites everything it reads). */
+rd_status rd_attention_noalloc(const float* q, const void* K, const void* V, const uint16_t* k_stage,
+                               const uint16_t* v_stage, const float* k_meta, const float* v_meta, float* out,
+                               int32_t n_heads, int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld,
+                               int32_t kv_format, float scale, int32_t splits, void* stream);
+
 /* rd_attention with kv_format FP16 (same kernels, same scratch, same rules). */
 rd_status rd_attention_f16(const float* q, const void* K, const void* V, float* out, int32_t n_heads,
                            int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,

@@ -80,6 +80,8 @@ SIGNATURES = [
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
     ("rd_attention", _I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, C.c_float,
                             _I32, _VP]),
+    ("rd_attention_noalloc", _I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
+                                    C.c_float, _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
     ("rd_seg_quant", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
     ("rd_argmax_f32", _I32, [_VP, _I32, _VP, _VP]),
@@ -299,6 +301,14 @@ def rd_attention(q: int, K: int, V: int, out: int, n_heads: int, n_kv_heads: int
                  v_meta: int = 0, stream: int = 0):
     check(lib().rd_attention(q, K, V, k_stage or None, v_stage or None, k_meta or None, v_meta or None, out, n_heads,
                              n_kv_heads, hd, L, ld, KV_FORMATS[kv_format], scale, splits, stream or None))
+
+
+def rd_attention_noalloc(q: int, K: int, V: int, out: int, n_heads: int, n_kv_heads: int, hd: int, L: int,
+                         ld: int, kv_format: str, scale: float, splits: int, k_stage: int = 0, v_stage: int = 0,
+                         k_meta: int = 0, v_meta: int = 0, stream: int = 0):
+    check(lib().rd_attention_noalloc(q, K, V, k_stage or None, v_stage or None, k_meta or None, v_meta or None, out,
+                                     n_heads, n_kv_heads, hd, L, ld, KV_FORMATS[kv_format], scale, splits,
+                                     stream or None))
 
 
 def rd_e5m2_encode(inp: int, out: int, n: int, stream: int = 0):

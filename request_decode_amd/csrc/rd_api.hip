@@ -974,6 +974,53 @@ extern "C" rd_status rd_attention(const float* q, const void* Kc, const void* Vc
                           (hipStream_t)stream, s->part, s->pos);
 }
 
+// ---- rd_attention without any allocation ---------------------------------------
+// The split partials and the position word live in a fixed device array (one
+// copy per GPU, held until the process ends).  In host code `scratch` names a
+// host-side stand-in, not the device copy: its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only
+// that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_static_mu;
+void* g_static_ptr[64];
+
+hipError_t static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void* p = nullptr;
+        if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_static_ptr[dev] = p;
+    }
+    *out = g_static_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" rd_status rd_attention_noalloc(const float* q, const void* Kc, const void* Vc, const uint16_t* kst,
+                                          const uint16_t* vst, const float* kmeta, const float* vmeta, float* out,
+                                          int32_t H, int32_t Hk, int32_t hd, int32_t L, int32_t ld,
+                                          int32_t kv_format, float scale, int32_t splits, void* stream) {
+    rd_status r = attention_args_ok(q, Kc, Vc, kst, vst, kmeta, vmeta, out, H, Hk, hd, L, ld, kv_format, splits);
+    if (r) return r;
+    const size_t need = 256 + (size_t)H * splits * (hd + 2) * sizeof(float);
+    if (need > kNoAllocScratchBytes)
+        return fail(RD_ERR_INVALID_ARG, "n_heads * splits * (hd + 2) * 4 bytes of split partials exceed the " +
+                                            std::to_string(kNoAllocScratchBytes - 256) + "-byte static scratch");
+    void* p = nullptr;
+    K_TRY(static_scratch(&p));
+    uint8_t* b = (uint8_t*)p;
+    return attention_call(q, Kc, Vc, kst, vst, kmeta, vmeta, out, H, Hk, hd, L, ld, kv_format, scale, splits,
+                          (hipStream_t)stream, (float*)(b + 256), (int*)b);
+}
+
 extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void* Vc, float* out, int32_t H,
                                       int32_t Hk, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
                                       void* stream) {
