@@ -74,6 +74,8 @@ def lib():
         L.orc_step.restype = C.c_int
         L.orc_step.argtypes = [C.c_void_p, i32p, dp, i32p]
         L.orc_layer0_kv.argtypes = [C.c_void_p, C.c_int32, C.c_int, dp, dp]
+        L.orc_prefill.restype = C.c_int
+        L.orc_prefill.argtypes = [C.c_void_p, i32p, C.c_int]
         for f in (L.orc_get_rows, L.orc_set_rows):
             f.restype = C.c_int
             f.argtypes = [C.c_void_p] + [C.c_int] * 6 + [C.c_void_p]
@@ -231,6 +233,12 @@ class OracleModel:
         if rc != 0:
             raise ValueError("oracle: " + lib().orc_last_error().decode())
         return logits, nxt
+
+    def prefill(self, tokens):
+        """Teacher-forced prompt steps, loop-interchanged (orc_prefill)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if lib().orc_prefill(self._h, _p(t, C.c_int32), t.size) != 0:
+            raise ValueError("oracle: " + lib().orc_last_error().decode())
 
     def layer0_kv(self, token: int, pos: int):
         n = self.n_kv_heads * self.head_dim

@@ -551,3 +551,113 @@ int orc_step(orc_model* m, const int32_t* tokens, double* logits, int32_t* next)
     free(x); free(r); free(q); free(k); free(v); free(a); free(o); free(gt); free(up); free(lg);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Blocked prefill: the decode steps of a prompt, loop-interchanged          */
+
+/* y[t*n + r] = W[r] . x_t for the nt tokens of a block, x held transposed
+ * (xt[c*nt + t]).  Each token's sum runs over the columns in order, exactly
+ * as orc_gemv's; only the loops are interchanged, so that a weight row is
+ * used for every token while it is in cache. */
+static void gemv_block(const uint16_t* W, const double* xt, int n, int k, int nt, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < n; ++r) {
+        double acc[ORC_SEG];
+        for (int t = 0; t < nt; ++t) acc[t] = 0.0;
+        const uint16_t* w = W + (size_t)r * k;
+        for (int c = 0; c < k; ++c) {
+            const double wc = g_h2d_tab[w[c]];
+            const double* xc = xt + (size_t)c * nt;
+            for (int t = 0; t < nt; ++t) acc[t] += wc * xc[t];
+        }
+        for (int t = 0; t < nt; ++t) y[(size_t)t * n + r] = acc[t];
+    }
+}
+
+static void transpose_block(const double* x, int nt, int k, double* xt) {
+    for (int t = 0; t < nt; ++t)
+        for (int c = 0; c < k; ++c) xt[(size_t)c * nt + t] = x[(size_t)t * k + c];
+}
+
+int orc_prefill(orc_model* m, const int32_t* tokens, int n) {
+    if (m->batch != 1) { set_err("prefill: batch-1 models only"); return -1; }
+    if (n < 0 || m->pos[0] + n > m->max_ctx) { set_err("prefill: tokens do not fit the context"); return -1; }
+    for (int i = 0; i < n; ++i)
+        if (tokens[i] < 0 || tokens[i] >= m->V) { set_err("token out of range"); return -1; }
+    const int D = m->D, H = m->H, Hk = m->Hk, hd = m->hd, F = m->F, G = H / Hk;
+    const int kmax = F > D ? (F > H * hd ? F : H * hd) : (D > H * hd ? D : H * hd);
+    const int nmax = 2 * F > (H + 2 * Hk) * hd ? 2 * F : (H + 2 * Hk) * hd;
+    double* x = (double*)malloc(sizeof(double) * ORC_SEG * D);
+    double* r = (double*)malloc(sizeof(double) * ORC_SEG * kmax);
+    double* xt = (double*)malloc(sizeof(double) * ORC_SEG * kmax);
+    double* y = (double*)malloc(sizeof(double) * ORC_SEG * (size_t)nmax);
+    double* q = (double*)malloc(sizeof(double) * ORC_SEG * H * hd);
+    double* a = (double*)malloc(sizeof(double) * ORC_SEG * H * hd);
+    int done = 0;
+    while (done < n) {
+        /* a block never crosses a 128-position boundary: all of its rows
+         * belong to one INT8 segment, which is sealed after the block */
+        const int p0 = m->pos[0];
+        int nt = ORC_SEG - p0 % ORC_SEG;
+        if (nt > n - done) nt = n - done;
+        for (int t = 0; t < nt; ++t)
+            for (int i = 0; i < D; ++i) x[(size_t)t * D + i] = orc_h2d(m->embed[(size_t)tokens[done + t] * D + i]);
+        for (int l = 0; l < m->L; ++l) {
+            const orc_layer* w = &m->layer[l];
+            for (int t = 0; t < nt; ++t) orc_rmsnorm(x + (size_t)t * D, w->attn_norm, D, m->eps, r + (size_t)t * D);
+            transpose_block(r, nt, D, xt);
+            const int Nq = H * hd, Nk = Hk * hd;
+            gemv_block(w->wq, xt, Nq, D, nt, q);
+            gemv_block(w->wk, xt, Nk, D, nt, y);
+            gemv_block(w->wv, xt, Nk, D, nt, y + (size_t)nt * Nk);
+            for (int t = 0; t < nt; ++t) {
+                const int pos = p0 + t;
+                double* kt = y + (size_t)t * Nk;
+                double* vt = y + (size_t)nt * Nk + (size_t)t * Nk;
+                for (int h = 0; h < H; ++h) orc_rope(q + (size_t)t * Nq + (size_t)h * hd, hd, pos, m->base);
+                for (int g = 0; g < Hk; ++g) orc_rope(kt + (size_t)g * hd, hd, pos, m->base);
+                if (m->store)
+                    for (int g = 0; g < Hk; ++g) {
+                        store_row(m, 0, l, 0, g, pos, kt + (size_t)g * hd);
+                        store_row(m, 0, l, 1, g, pos, vt + (size_t)g * hd);
+                    }
+            }
+            /* token t attends to positions 0..p0+t as stored */
+#pragma omp parallel for schedule(dynamic, 1)
+            for (int tg = 0; tg < nt * Hk; ++tg) {
+                const int t = tg / Hk, g = tg % Hk, L = p0 + t + 1;
+                double* Kd = (double*)malloc(sizeof(double) * (size_t)L * hd);
+                double* Vd = (double*)malloc(sizeof(double) * (size_t)L * hd);
+                for (int p = 0; p < L; ++p) {
+                    orc_read_row(m, 0, l, 0, g, p, Kd + (size_t)p * hd);
+                    orc_read_row(m, 0, l, 1, g, p, Vd + (size_t)p * hd);
+                }
+                for (int h = g * G; h < (g + 1) * G; ++h)
+                    orc_attention(q + (size_t)t * Nq + (size_t)h * hd, Kd, Vd, L, hd, a + (size_t)t * Nq + (size_t)h * hd);
+                free(Kd);
+                free(Vd);
+            }
+            transpose_block(a, nt, Nq, xt);
+            gemv_block(w->wo, xt, D, Nq, nt, y);
+            for (size_t i = 0; i < (size_t)nt * D; ++i) x[i] += y[i];
+            for (int t = 0; t < nt; ++t) orc_rmsnorm(x + (size_t)t * D, w->ffn_norm, D, m->eps, r + (size_t)t * D);
+            transpose_block(r, nt, D, xt);
+            gemv_block(w->wg, xt, F, D, nt, y);
+            gemv_block(w->wu, xt, F, D, nt, y + (size_t)nt * F);
+            for (int t = 0; t < nt; ++t)
+                for (int i = 0; i < F; ++i) {
+                    const size_t j = (size_t)t * F + i;
+                    r[j] = orc_silu(y[j]) * y[(size_t)nt * F + j];
+                }
+            transpose_block(r, nt, F, xt);
+            gemv_block(w->wd, xt, D, F, nt, y);
+            for (size_t i = 0; i < (size_t)nt * D; ++i) x[i] += y[i];
+        }
+        m->pos[0] = p0 + nt;
+        if (m->fmt == ORC_KV_INT8_SEG128 && (p0 + nt) % ORC_SEG == 0) seal_segment(m, 0, (p0 + nt) / ORC_SEG - 1);
+        done += nt;
+    }
+    free(x); free(r); free(xt); free(y); free(q); free(a);
+    return 0;
+}
+

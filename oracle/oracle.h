@@ -81,6 +81,16 @@ void        orc_dims(const orc_model* m, int* out7);
  * of range. */
 int orc_step(orc_model* m, const int32_t* tokens, double* logits, int32_t* next);
 
+/* Teacher-forced prompt: tokens[0..n) at positions pos .. pos+n-1 of a
+ * batch-1 model, the same decode steps as n calls of orc_step (bit for bit:
+ * cache, and every later step) with the loops interchanged: per block of
+ * tokens within one 128-position segment, each layer runs for all of the
+ * block's tokens (weight rows reused across tokens, each dot product still
+ * summed in order), token t attending to positions 0..pos+t as stored; the
+ * INT8 seal follows a block that completes a segment.  No logits.  Returns 0,
+ * or -1 (batch > 1, context full, token out of range; nothing run). */
+int orc_prefill(orc_model* m, const int32_t* tokens, int n);
+
 /* K/V rows of layer 0 for a token at a position, before any cache rounding
  * ([n_kv_heads*head_dim] each, post-RoPE K).  Layer 0 depends on the token
  * alone, so this samples the cache at any position without a prefill. */

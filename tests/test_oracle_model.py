@@ -297,3 +297,37 @@ def test_store_off_step_is_the_same_step(orc, kv):
     c.step([int(toks[0])])
     c.set_pos(0)
     assert np.array_equal(c.get_rows(0, 0, 0, 0, 1), before)
+
+
+@pytest.mark.parametrize("kv", ["fp16", "e5m2", "int8", "exact"])
+@pytest.mark.parametrize("start", [0, 50])
+def test_blocked_prefill_is_the_steps(orc, kv, start):
+    """orc_prefill is the decode steps loop-interchanged: after it, the
+    cache (every layer, head, row; INT8 codes and tables) and the next
+    steps' logits are bit-identical to feeding the tokens one step at a
+    time; the prompt crosses two segment boundaries, starting at position 0
+    or part-way into a segment (after `start` single steps)."""
+    shape = SEAL64
+    blob = synth.make_blob(shape, seed=19)
+    toks = synth.prompt(20, 300, shape.vocab)
+    a = orc.OracleModel(blob, 320, kv_format=kv)
+    b = orc.OracleModel(blob, 320, kv_format=kv)
+    for t in toks[:start]:
+        a.step([t])
+        b.step([t])
+    for t in toks[start:290]:
+        a.step([t])
+    b.prefill(toks[start:290])
+    assert a.pos() == b.pos() == 290
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(shape.n_kv_heads):
+                for p0, n in ((0, 256), (256, 34)):
+                    assert np.array_equal(a.get_rows(l, w, g, p0, n), b.get_rows(l, w, g, p0, n)), (l, w, g, p0)
+                if kv == "int8":
+                    for seg in (0, 1):
+                        assert a.seg_meta(l, w, g, seg) == b.seg_meta(l, w, g, seg)
+    for t in toks[290:]:
+        la, na = a.step([t])
+        lb, nb = b.step([t])
+        assert np.array_equal(la, lb) and na[0] == nb[0]
