@@ -84,6 +84,10 @@ def lib():
         L.orc_read_row.restype = C.c_int
         L.orc_read_row.argtypes = [C.c_void_p] + [C.c_int] * 5 + [dp]
         L.orc_set_store.argtypes = [C.c_void_p, C.c_int]
+        L.orc_record_rows.restype = C.c_int
+        L.orc_record_rows.argtypes = [C.c_void_p, C.c_int]
+        L.orc_get_computed.restype = C.c_int
+        L.orc_get_computed.argtypes = [C.c_void_p] + [C.c_int] * 6 + [dp]
         L.orc_set_pos.restype = C.c_int
         L.orc_set_pos.argtypes = [C.c_void_p, C.c_int, C.c_int]
         _lib = L
@@ -224,6 +228,17 @@ class OracleModel:
     def set_store(self, store: bool):
         """False: steps keep the rows already at their position (orc_set_store)."""
         lib().orc_set_store(self._h, 1 if store else 0)
+
+    def record_rows(self, on: bool = True):
+        """Keep the K/V rows every later step computes (orc_record_rows)."""
+        if lib().orc_record_rows(self._h, 1 if on else 0) != 0:
+            raise MemoryError("oracle: no memory for the row record")
+
+    def computed_rows(self, layer, which, head, pos0, n, b=0) -> np.ndarray:
+        out = np.empty((n, self.head_dim), np.float64)
+        if lib().orc_get_computed(self._h, b, layer, which, head, pos0, n, _p(out, C.c_double)) != 0:
+            raise ValueError("no record, or bad row region")
+        return out
 
     def step(self, tokens):
         t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(self.batch))

@@ -245,6 +245,7 @@ struct orc_model {
     orc_layer* layer;
     int max_ctx, batch, fmt;
     int store;         /* 0: a step keeps the row already at its position (see orc_set_store) */
+    double* computed;  /* optional [lane][max_ctx][hd]: the K/V rows the steps computed (orc_record_rows) */
     int* pos;
     void* kv;          /* [b][layer][which][head][max_ctx][hd] of the format's element */
     uint16_t* stage;   /* INT8: [b][layer][which][head][128][hd] open segment */
@@ -347,7 +348,7 @@ orc_model* orc_create(const void* blob_v, size_t bytes, int max_ctx, int batch, 
 
 void orc_destroy(orc_model* m) {
     if (!m) return;
-    free(m->blob); free(m->layer); free(m->pos); free(m->kv); free(m->stage); free(m->meta);
+    free(m->blob); free(m->layer); free(m->pos); free(m->kv); free(m->stage); free(m->meta); free(m->computed);
     free(m);
 }
 
@@ -362,6 +363,32 @@ void orc_dims(const orc_model* m, int* o) {
 }
 
 void orc_set_store(orc_model* m, int store) { m->store = store != 0; }
+
+int orc_record_rows(orc_model* m, int on) {
+    free(m->computed);
+    m->computed = NULL;
+    if (!on) return 0;
+    m->computed = (double*)calloc((size_t)m->batch * m->L * 2 * m->Hk * (size_t)m->max_ctx * m->hd, sizeof(double));
+    return m->computed ? 0 : -1;
+}
+
+static int rows_region_ok(const orc_model* m, int b, int layer, int which, int head, int pos0, int n);
+
+int orc_get_computed(const orc_model* m, int b, int layer, int which, int head, int pos0, int n, double* dst) {
+    if (!m->computed || !rows_region_ok(m, b, layer, which, head, pos0, n)) return -1;
+    const size_t lane = lane_index(m, b, layer, which, head);
+    memcpy(dst, m->computed + (lane * m->max_ctx + pos0) * m->hd, sizeof(double) * (size_t)n * m->hd);
+    return 0;
+}
+
+/* The computed (unrounded) K/V rows of one position into the record. */
+static void record_rows(orc_model* m, int b, int layer, int pos, const double* k, const double* v) {
+    if (!m->computed) return;
+    for (int which = 0; which < 2; ++which)
+        for (int g = 0; g < m->Hk; ++g)
+            memcpy(m->computed + (lane_index(m, b, layer, which, g) * m->max_ctx + pos) * m->hd,
+                   (which ? v : k) + (size_t)g * m->hd, sizeof(double) * m->hd);
+}
 
 int orc_set_pos(orc_model* m, int b, int pos) {
     if (b < 0 || b >= m->batch || pos < 0 || pos > m->max_ctx) return -1;
@@ -513,6 +540,7 @@ int orc_step(orc_model* m, const int32_t* tokens, double* logits, int32_t* next)
             orc_gemv(y->wv, r, Hk * hd, D, v);
             for (int h = 0; h < H; ++h) orc_rope(q + (size_t)h * hd, hd, pos, m->base);
             for (int g = 0; g < Hk; ++g) orc_rope(k + (size_t)g * hd, hd, pos, m->base);
+            record_rows(m, b, l, pos, k, v);
             if (m->store)
                 for (int g = 0; g < Hk; ++g) {
                     store_row(m, b, l, 0, g, pos, k + (size_t)g * hd);
@@ -545,7 +573,7 @@ int orc_step(orc_model* m, const int32_t* tokens, double* logits, int32_t* next)
         orc_gemv(m->lm_head, r, V, D, lg);
         if (logits) memcpy(logits + (size_t)b * V, lg, sizeof(double) * V);
         if (next) next[b] = orc_argmax(lg, V);
-        if (m->fmt == ORC_KV_INT8_SEG128 && (pos + 1) % ORC_SEG == 0) seal_segment(m, b, pos / ORC_SEG);
+        if (m->store && m->fmt == ORC_KV_INT8_SEG128 && (pos + 1) % ORC_SEG == 0) seal_segment(m, b, pos / ORC_SEG);
         m->pos[b] = pos + 1;
     }
     free(x); free(r); free(q); free(k); free(v); free(a); free(o); free(gt); free(up); free(lg);
@@ -616,6 +644,7 @@ int orc_prefill(orc_model* m, const int32_t* tokens, int n) {
                 double* vt = y + (size_t)nt * Nk + (size_t)t * Nk;
                 for (int h = 0; h < H; ++h) orc_rope(q + (size_t)t * Nq + (size_t)h * hd, hd, pos, m->base);
                 for (int g = 0; g < Hk; ++g) orc_rope(kt + (size_t)g * hd, hd, pos, m->base);
+                record_rows(m, 0, l, pos, kt, vt);
                 if (m->store)
                     for (int g = 0; g < Hk; ++g) {
                         store_row(m, 0, l, 0, g, pos, kt + (size_t)g * hd);
@@ -654,7 +683,8 @@ int orc_prefill(orc_model* m, const int32_t* tokens, int n) {
             for (size_t i = 0; i < (size_t)nt * D; ++i) x[i] += y[i];
         }
         m->pos[0] = p0 + nt;
-        if (m->fmt == ORC_KV_INT8_SEG128 && (p0 + nt) % ORC_SEG == 0) seal_segment(m, 0, (p0 + nt) / ORC_SEG - 1);
+        if (m->store && m->fmt == ORC_KV_INT8_SEG128 && (p0 + nt) % ORC_SEG == 0)
+            seal_segment(m, 0, (p0 + nt) / ORC_SEG - 1);
         done += nt;
     }
     free(x); free(r); free(xt); free(y); free(q); free(a);

@@ -109,12 +109,17 @@ int orc_seg_meta(orc_model* m, int b, int layer, int which, int head, int seg, f
 /* Dequantized (as-attended) value of one cache row, binary64 [hd]. */
 int orc_read_row(const orc_model* m, int b, int layer, int which, int head, int pos, double* dst);
 int orc_set_pos(orc_model* m, int b, int pos);
-/* store = 0: orc_step computes the K/V rows of its position but does not
- * store them; attention reads whatever row that position already holds
- * (set with orc_set_rows), and the INT8 seal quantizes the staging rows as
- * they are.  A test of the 8-bit formats uses it to run a step over the
- * exact stored bytes of another implementation's cache.  Default 1. */
+/* store = 0: orc_step and orc_prefill compute the K/V rows of their
+ * positions but store nothing in the cache (no row, no INT8 seal);
+ * attention reads whatever the cache already holds (set with orc_set_rows
+ * and orc_seg_meta).  Tests of the 8-bit formats use it to run steps over
+ * the exact stored bytes of another implementation's cache.  Default 1. */
 void orc_set_store(orc_model* m, int store);
+/* on = 1: from now on every step (orc_step, orc_prefill) also records the
+ * K/V rows it computes, before any rounding (binary64, post-RoPE K), for
+ * orc_get_computed; on = 0 drops the record.  Returns -1 if out of memory. */
+int orc_record_rows(orc_model* m, int on);
+int orc_get_computed(const orc_model* m, int b, int layer, int which, int head, int pos0, int n, double* dst);
 
 #ifdef __cplusplus
 }

@@ -257,10 +257,10 @@ def test_batch_step_equals_independent_sequences(orc, kv, n):
 
 @pytest.mark.parametrize("kv", ["fp16", "e5m2", "int8"])
 def test_store_off_step_is_the_same_step(orc, kv):
-    """With its row store switched off, a step whose position already holds
-    the rows the step would store gives bit-identical logits, argmax and
-    cache (int8: the seal quantizes the staging rows as they are).  Model B
-    gets A's rows of each position before its step, A stores its own."""
+    """With its store switched off, a step whose position already holds the
+    rows the step would store gives bit-identical logits and argmax; it
+    stores nothing (no row, no seal), so model B gets A's rows of each
+    position before its step and, after a seal, A's codes and tables."""
     shape = SEAL64
     blob = synth.make_blob(shape, seed=17)
     toks = synth.prompt(18, 140, shape.vocab)
@@ -269,12 +269,12 @@ def test_store_off_step_is_the_same_step(orc, kv):
     b.set_store(False)
     for i, t in enumerate(toks):
         la, na = a.step([t])
+        sealed = kv == "int8" and i % 128 == 127
         b.set_pos(i)
         for l in range(shape.n_layers):
             for w in (0, 1):
                 for g in range(shape.n_kv_heads):
-                    if kv == "int8" and i % 128 == 127:
-                        # A's segment is sealed by now: give B the staging row A held
+                    if sealed:               # A's segment is sealed by now: B gets the staging row A held
                         a.set_pos(i)
                         row = a.get_rows(l, w, g, i, 1)
                         a.set_pos(i + 1)
@@ -283,20 +283,49 @@ def test_store_off_step_is_the_same_step(orc, kv):
                     b.set_rows(l, w, g, i, row)
         lb, nb = b.step([t])
         assert np.array_equal(la, lb) and na[0] == nb[0], (kv, i)
+        if sealed:                           # B sealed nothing: its codes and tables come from A
+            for l in range(shape.n_layers):
+                for w in (0, 1):
+                    for g in range(shape.n_kv_heads):
+                        b.set_rows(l, w, g, 0, a.get_rows(l, w, g, 0, 128))
+                        b.seg_meta(l, w, g, 0, set_to=a.seg_meta(l, w, g, 0))
+    n = 128 if kv == "int8" else 140
     for l in range(shape.n_layers):
         for w in (0, 1):
             for g in range(shape.n_kv_heads):
-                assert np.array_equal(a.get_rows(l, w, g, 0, 128 if kv == "int8" else 140),
-                                      b.get_rows(l, w, g, 0, 128 if kv == "int8" else 140))
-                if kv == "int8":
-                    assert a.seg_meta(l, w, g, 0) == b.seg_meta(l, w, g, 0)
-    # and switched off it really stores nothing: a fresh position keeps what it held
+                assert np.array_equal(a.get_rows(l, w, g, 0, n), b.get_rows(l, w, g, 0, n))
+    # switched off it stores nothing: a fresh position keeps what it held
     c = orc.OracleModel(blob, 8, kv_format=kv)
     c.set_store(False)
     before = c.get_rows(0, 0, 0, 0, 1).copy()
     c.step([int(toks[0])])
     c.set_pos(0)
     assert np.array_equal(c.get_rows(0, 0, 0, 0, 1), before)
+
+
+@pytest.mark.parametrize("path", ["steps", "prefill"])
+def test_recorded_rows_are_the_stored_rows_unrounded(orc, path):
+    """The row record holds each position's K/V rows before rounding: a
+    model with the exact cache stores the same binary64 values, one with the
+    fp16 cache their binary16 rounding (every layer, head and position, by
+    single steps and by the blocked prefill)."""
+    shape = SEAL64
+    blob = synth.make_blob(shape, seed=25)
+    toks = synth.prompt(26, 150, shape.vocab)
+    ex = orc.OracleModel(blob, 160, kv_format="exact")
+    h = orc.OracleModel(blob, 160, kv_format="fp16")
+    for m in (ex, h):
+        m.record_rows(True)
+        if path == "steps":
+            for t in toks:
+                m.step([t])
+        else:
+            m.prefill(toks)
+    for l in range(shape.n_layers):
+        for w in (0, 1):
+            for g in range(shape.n_kv_heads):
+                assert np.array_equal(ex.computed_rows(l, w, g, 0, 150), ex.get_rows(l, w, g, 0, 150))
+                assert np.array_equal(orc.d2h(h.computed_rows(l, w, g, 0, 150)), h.get_rows(l, w, g, 0, 150))
 
 
 @pytest.mark.parametrize("kv", ["fp16", "e5m2", "int8", "exact"])
