@@ -164,6 +164,24 @@ rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, floa
  * if the tokens do not fit; INVALID_ARG (nothing run) for an id out of range. */
 rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batch, int32_t n);
 
+/* Batched prefill of sequence 0 (max_batch 1): tokens (host [n]) at
+ * positions pos .. pos+n-1, the prompt processed together instead of one
+ * decode step per token ("LLM inference architecture rebuild", batch
+ * planner: prefill separated from decode; "How the xAI engineering team cut
+ * Grok Bot latency to milliseconds", §2.1: block-wise FlashAttention).  It
+ * computes what the decode steps would for those positions -- each
+ * position's K/V rows, and each position's attention over positions 0..p as
+ * stored in the cache format (INT8: segments sealed as they complete) --
+ * with the layer products as matrix products on the matrix cores (fp16
+ * operands, fp32 sums) in chunks of 2048 tokens, so the cache rows agree
+ * with the decode steps' within rounding, not bit for bit.  No logits; the
+ * next rd_decode_step continues at pos+n.  Allocates a workspace on the
+ * first call (about 100 MB for the 2B-class shape), kept by the model.
+ * Synchronises.  Errors: INVALID_ARG (NULL, n < 0, a token out of range;
+ * nothing run), CONTEXT_FULL (nothing run), UNSUPPORTED (max_batch > 1, or
+ * d_model / d_ff not multiples of 32), OUT_OF_MEMORY, DEVICE. */
+rd_status rd_prefill_batched(rd_model* m, const int32_t* tokens, int32_t n);
+
 /* n_steps greedy steps with the token fed back on the device (no host round
  * trip between steps: the whole sequence is decoded without the CPU in the
  * loop, "Real-time LLM inference on standard GPUs", last section).  first: host [batch], the token at the current

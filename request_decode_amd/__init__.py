@@ -76,6 +76,7 @@ SIGNATURES = [
     ("rd_debug_trace_step_all", _I32, [_VP, _I32, C.POINTER(C.c_uint64), _I32, _I32P]),
     ("rd_last_error", C.c_char_p, []),
     ("rd_prefill", _I32, [_VP, _I32P, _I32, _I32]),
+    ("rd_prefill_batched", _I32, [_VP, _I32P, _I32]),
     ("rd_gemv_f16", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP]),
     ("rd_attention_f16", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_float, _I32, _VP]),
     ("rd_attention", _I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32, C.c_float,
@@ -232,6 +233,12 @@ class Model:
         if t.size % self.batch:
             raise ValueError("token count must be a multiple of the batch")
         check(lib().rd_prefill(self._h, t.ctypes.data_as(_I32P), self.batch, int(t.size // self.batch)))
+
+    def prefill_batched(self, tokens):
+        """The prompt `tokens` ([n], batch-1 models) through the batched
+        prefill (matrix products per layer, chunked), one sync."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        check(lib().rd_prefill_batched(self._h, t.ctypes.data_as(_I32P), int(t.size)))
 
     def generate(self, first, n_steps: int) -> np.ndarray:
         """n_steps greedy steps from `first` (int, or [B]): tokens [n_steps]

@@ -145,6 +145,10 @@ struct rd_model {
     hipGraph_t graph = nullptr;
     hipGraphExec_t gexec = nullptr;
 
+    // batched prefill workspace (allocated on the first rd_prefill_batched)
+    void* pf_buf = nullptr;
+    PrefillWs pf{};
+
     // persistent executor
     long long layer_stride = 0;     // bytes between consecutive layers' weight blocks
     int nwg = 0;                    // workgroups of the cooperative launch (0: not available)
@@ -197,6 +201,7 @@ void free_model(rd_model* m) {
     (void)hipFree(m->stage);
     (void)hipFree(m->meta);
     (void)hipFree(m->act);
+    (void)hipFree(m->pf_buf);
     if (m->gen_host) (void)hipHostFree(m->gen_host);
     if (m->logits_host) (void)hipHostFree(m->logits_host);
     if (m->state_host) (void)hipHostFree(m->state_host);
@@ -703,6 +708,52 @@ extern "C" rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batc
     if (st) return st;
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
     return finish_sync(m);
+}
+
+// Chunk of the batched prefill: 2048 tokens (the workspace for the 2B-class
+// model is about 100 MB).
+constexpr int kPrefillChunk = 2048;
+
+extern "C" rd_status rd_prefill_batched(rd_model* m, const int32_t* tokens, int32_t n) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!tokens && n > 0) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
+    if (n < 0) return fail(RD_ERR_INVALID_ARG, "n < 0");
+    if (!prefill_supported(m->d.D, m->d.H, m->d.hd, m->d.F, m->opt.max_batch))
+        return fail(RD_ERR_UNSUPPORTED, "batched prefill needs batch 1 and d_model, d_ff multiples of 32");
+    if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "tokens do not fit the context");
+    if (!tokens_ok(m, tokens, n)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (n == 0) return RD_OK;
+    HIP_TRY(hipSetDevice(m->dev));
+    if (!m->pf_buf) {
+        const size_t tc = kPrefillChunk, D = m->d.D, H = m->d.H, Hk = m->d.Hk, hd = m->d.hd, F = m->d.F;
+        size_t a = 0;
+        auto carve = [&](size_t bytes) {
+            size_t o = a;
+            a = align256(a + bytes);
+            return o;
+        };
+        const size_t o_tok = carve((size_t)m->opt.max_context * 4), o_x = carve(tc * D * 4), o_xn = carve(tc * D * 2);
+        const size_t o_q = carve(tc * H * hd * 4), o_a = carve(tc * H * hd * 2), o_m = carve(tc * F * 2);
+        const size_t o_kt = carve(2 * Hk * tc * hd * 2);
+        hipError_t e = hipMalloc(&m->pf_buf, a);
+        if (e == hipErrorOutOfMemory) return fail(RD_ERR_OUT_OF_MEMORY, "prefill workspace");
+        if (e != hipSuccess) return dev_fail(m, "hipMalloc (prefill workspace)", e);
+        uint8_t* b = (uint8_t*)m->pf_buf;
+        m->pf = PrefillWs{(int*)(b + o_tok), (float*)(b + o_x), (_Float16*)(b + o_xn), (float*)(b + o_q),
+                          (_Float16*)(b + o_a), (_Float16*)(b + o_m), (_Float16*)(b + o_kt), (int)tc};
+    }
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    HIP_TRY(hipMemcpy(m->pf.tok, tokens, (size_t)n * 4, hipMemcpyHostToDevice));
+    for (int done = 0; done < n; done += kPrefillChunk) {
+        const int T = std::min(kPrefillChunk, n - done);
+        PrefillWs ws = m->pf;
+        ws.tok = m->pf.tok + done;
+        HIP_TRY(prefill_chunk(m->A, ws, m->host_pos + done, T, m->stream));
+    }
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    m->host_pos += n;
+    return RD_OK;
 }
 
 static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t batch, int32_t n) {

@@ -177,6 +177,22 @@ bool persistent_supported(const StepArgs& A);
 hipError_t launch_persistent(const StepArgs& A, const PersistArgs& P, int nwg, hipStream_t s);
 hipError_t persistent_max_grid(const StepArgs& A, int device, int* nwg);
 
+// Batched prefill (rd_prefill.hip): workspace of one chunk of up to tc
+// prompt tokens.
+struct PrefillWs {
+    int* tok;       // [tc] token ids of the chunk (device)
+    float* x;       // [tc][D] residual rows
+    _Float16* xn;   // [tc][D] normalised rows (GEMM operand)
+    float* q;       // [tc][H*hd] rotated queries
+    _Float16* a;    // [tc][H*hd] attention output (GEMM operand)
+    _Float16* m;    // [tc][F] SwiGLU output (GEMM operand)
+    _Float16* kt;   // [2][Hk][tc][hd] the chunk's new K and V rows in fp16
+    int tc;
+};
+bool prefill_supported(int D, int H, int hd, int F, int B);
+// Positions p0 .. p0+T-1 (T <= ws.tc) of sequence 0, tokens in ws.tok.
+hipError_t prefill_chunk(const StepArgs& A, const PrefillWs& ws, int p0, int T, hipStream_t s);
+
 // Host launchers (rd_kernels.hip).
 int kch_for(int K);
 hipError_t launch_step(const StepArgs& A, hipStream_t s);

@@ -123,19 +123,22 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
     away from the GPU's, and over 24 layers that moves the logits well past
     the comparison rule (E5M2: 0.44 at the first step).  So before the
     oracle decodes position i it is given the bytes the GPU stored at
-    position i (E5M2 rows; INT8: the fp16 staging row), stores none of its
-    own (orc_set_store), and attends over exactly the GPU's cache; every
+    position i (E5M2 rows; INT8: the fp16 staging row), stores nothing of
+    its own (orc_set_store), and attends over exactly the GPU's cache; every
     step's logits are then compared by the rule.  At an INT8 seal the
-    oracle's quantizer, run on the same staging rows, must give the GPU's
-    codes and (scale, zero point) bit for bit.  The rows themselves are
-    checked at layer 0 against the oracle's own layer-0 path: E5M2 values
-    within the fp16 row tolerance plus one step of the format, INT8
-    staging rows within the fp16 tolerance."""
+    oracle's quantizer, run on the GPU's staging rows, must give the GPU's
+    codes and (scale, zero point) bit for bit, and the oracle takes them.
+    The rows: the oracle records the rows it computes from that same cache
+    (orc_record_rows), and the GPU's row of every layer at every position
+    must be within the row tolerance (layer 0: 2e-3 + 2e-3 |x|, below:
+    2e-2 + 1e-2 |x|) plus, for E5M2, one step of the format; layer 0 is
+    also checked against the oracle's independent layer-0 path."""
     prompt = synth.prompt(105, 300, SHAPE.vocab)
     n = 320
     ctx = n + 8
     om = orc.OracleModel(blob2b, ctx, kv_format=kv)
     om.set_store(False)
+    om.record_rows(True)
     exs = ("persistent", "graph")
     gms = {ex: rd.Model(blob2b, max_context=ctx, kv_format=kv, executor=ex) for ex in exs}
     for ex, gm in gms.items():
@@ -144,6 +147,8 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
     NL, Hk = SHAPE.n_layers, SHAPE.n_kv_heads
     worst, graded = {ex: 0.0 for ex in exs}, 0
     l0_rows = {}
+    worst_row = 0.0
+    gpu_row = {}
     for i in range(n):
         out = {ex: gm.decode_step(toks[i]) for ex, gm in gms.items()}
         seal = kv == "int8" and i % 128 == 127
@@ -157,6 +162,7 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
                     assert np.array_equal(parts["graph"][k], parts["persistent"][k]), (i, l, w, k)
                 if l == 0:
                     l0_rows[i, w] = row.copy()
+                gpu_row[l, w] = row.copy()
                 for g in range(Hk):
                     om.set_rows(l, w, g, i, row[g:g + 1])
         ol, on = om.step([toks[i]])
@@ -164,16 +170,33 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
             e, gr = compare_step(out[ex][0], ol[0], out[ex][1], (kv, ex, i))
             worst[ex] = max(worst[ex], e)
         graded += gr
+        # the GPU's rows of position i against the rows the oracle computed from the same cache
+        for l in range(NL):
+            for w in (0, 1):
+                ref = np.stack([om.computed_rows(l, w, g, i, 1)[0] for g in range(Hk)])
+                tol = (2e-3 + 2e-3 * np.abs(ref)) if l == 0 else (ATOL + RTOL * np.abs(ref))
+                if kv == "e5m2":
+                    got = orc.h2d(orc.h_from_e5m2(gpu_row[l, w]))
+                    a = np.maximum(np.abs(got), np.abs(ref))
+                    tol = tol + np.where(a < 2.0 ** -14, 2.0 ** -16,
+                                         2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -14))) - 2))
+                else:
+                    got = gpu_row[l, w].view(np.float16).astype(np.float64)
+                err = np.abs(got - ref)
+                assert np.all(err <= tol), (kv, i, l, w, float(err.max()))
+                worst_row = max(worst_row, float(err.max()))
         if seal:
+            # the GPU's seal of its own staging rows, bit for bit; the oracle takes its codes
             seg = i // 128
             for l in range(NL):
                 for w in (0, 1):
                     got = gms["persistent"].export_kv(l, w)
                     for g in range(Hk):
-                        codes = om.get_rows(l, w, g, seg * 128, 128)
-                        scale, zp = om.seg_meta(l, w, g, seg)
+                        codes, scale, zp = orc.seg_quant(got["stage"][g])
                         assert np.array_equal(got["rows"][g, seg * 128:(seg + 1) * 128], codes), (i, l, w, g)
                         assert got["meta"][g, seg, 0] == scale and got["meta"][g, seg, 1] == zp, (i, l, w, g)
+                        om.set_rows(l, w, g, seg * 128, codes)
+                        om.seg_meta(l, w, g, seg, set_to=(scale, zp))
         if i == len(toks) - 1 and len(toks) < n:
             toks.append(int(on[0]))
         if i % 64 == 63:
@@ -193,7 +216,8 @@ def test_2b_quantized_kv_teacher_forced(rd, orc, blob2b, kv):
     for gm in gms.values():
         gm.close()
     om.close()
-    print(f"2b {kv} 300+20 (cache-synchronised): steps={n} graded={graded} max|dlogit|={worst}")
+    print(f"2b {kv} 300+20 (cache-synchronised): steps={n} graded={graded} max|dlogit|={worst} "
+          f"rows max|d| {worst_row:.3e}")
     assert graded > 20
 
 
