@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV microbench")
+    ap.add_argument("--prefill", default="batched", choices=["batched", "steps"],
+                    help="how the prompt is fed: the batched prefill (matrix products per layer), or one "
+                         "teacher-forced decode step per token")
     ap.add_argument("--trace", type=int, default=0,
                     help="persistent executor: trace this many steps in the middle of the timed range and "
                          "report where a layer's time goes (exchange waits and per-phase work)")
@@ -295,9 +298,17 @@ def main():
                  batch=B, attn_splits=args.attn_splits)
     executor = m.get_info().executor
     persistent = executor == rd.RD_EXEC_PERSISTENT
-    t0 = time.time()
-    m.prefill(prompt[:-1] if B == 1 else prompt[:, :-1].T)   # teacher-forced, on the graph path
-    print(f"[bench] prompt of {PROMPT} fed in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    batched = args.prefill == "batched" and B == 1
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if batched:
+        m.prefill_batched(prompt[:-1])
+    else:
+        m.prefill(prompt[:-1] if B == 1 else prompt[:, :-1].T)   # teacher-forced decode steps (graph path)
+    pf_s = time.perf_counter() - t0
+    n_pf = PROMPT - 1
+    print(f"[bench] prompt of {PROMPT} fed in {pf_s:.2f}s ({'batched prefill' if batched else 'decode steps'}, "
+          f"{n_pf / pf_s:.0f} tokens/s)", file=sys.stderr, flush=True)
     first = int(prompt[-1]) if B == 1 else prompt[:, -1].copy()
     base = PROMPT - 1
     out = torch.empty(max(args.steps, args.warmup, 1) * B, dtype=torch.int32, device="cuda")
@@ -394,6 +405,15 @@ def main():
     }
     if k_us is not None:
         res["gateup_phase_kernel"] = {"us_per_launch": round(k_us, 3), "gbps": round(k_gbps, 1)}
+    # prefill: matrix-product FLOPs (2 per weight and token; attention: QK^T
+    # and PV over positions 0..p of every prompt position)
+    D, H, Hk, hd, F, NL = (shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim, shape.d_ff,
+                           shape.n_layers)
+    w_tok = NL * ((H + 2 * Hk) * hd * D + D * H * hd + 2 * F * D + D * F)
+    attn = NL * H * hd * 4 * (n_pf * (n_pf + 1) // 2)
+    res["prefill"] = {"mode": "batched" if batched else "decode steps", "tokens": n_pf, "seconds": round(pf_s, 4),
+                      "tokens_per_s": round(n_pf / pf_s, 1),
+                      "tflops": round((2 * w_tok * n_pf + attn) / pf_s / 1e12, 2)}
     if trace is not None:
         res["layer_trace_us"] = trace
     if gemv is not None:
