@@ -1,7 +1,7 @@
 """A short run for hardware-counter collection under rocprofv3.
 
 Builds the 2B-class model (the bench's seeded weights), feeds a prompt with
-the kernel-per-phase executor (no graph launches), then makes one persistent launch of --steps greedy steps;
+the batched prefill (no graph launches), then makes one persistent launch of --steps greedy steps;
 afterwards one plain copy kernel (out = in + 0, elementwise) of --copy-mib
 MiB whose input was written before the run (its HBM traffic is known: that
 many bytes read and written) to calibrate FETCH_SIZE / WRITE_SIZE.  Prints the algorithmic bytes of the persistent
@@ -39,9 +39,7 @@ def main():
     blob = synth.make_blob(shape, seed=2)
     prompt = synth.prompt(103, args.prompt, shape.vocab)
     m = rd.Model(blob, max_context=args.prompt + args.steps, kv_format=args.kv, executor="persistent")
-    m.set_executor("eager")              # counter collection and graph launches do not mix in the profiler
-    m.prefill(prompt[:-1])
-    m.set_executor("persistent")
+    m.prefill_batched(prompt[:-1])       # (counter collection and graph launches do not mix in the profiler)
     m.generate(int(prompt[-1]), args.steps)
     Ls = range(args.prompt, args.prompt + args.steps)
     nbytes = sum(bench.step_bytes(shape, L, args.kv) for L in Ls)
