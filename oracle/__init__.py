@@ -55,6 +55,10 @@ def lib():
         L.orc_seg_dequant.restype = C.c_float
         L.orc_seg_dequant.argtypes = [C.c_uint8, C.c_float, C.c_float]
         L.orc_seg_dequant_n.argtypes = [u8p, C.c_size_t, C.c_float, C.c_float, fp]
+        L.orc_q4_quant.argtypes = [u16p, C.c_int, C.c_int, u8p, fp]
+        L.orc_q4_dequant.argtypes = [u8p, fp, C.c_int, C.c_int, u16p]
+        L.orc_q4_code.restype = C.c_int
+        L.orc_q4_code.argtypes = [u8p, C.c_size_t]
         L.orc_rmsnorm.argtypes = [dp, u16p, C.c_int, C.c_double, dp]
         L.orc_rope.argtypes = [dp, C.c_int, C.c_int, C.c_double]
         L.orc_gemv.argtypes = [u16p, dp, C.c_int, C.c_int, dp]
@@ -143,6 +147,26 @@ def seg_dequant(codes: np.ndarray, scale, zp) -> np.ndarray:
     out = np.empty(c.shape, np.float32)
     lib().orc_seg_dequant_n(_p(c, C.c_uint8), c.size, float(scale), float(zp), _p(out, C.c_float))
     return out
+
+
+def q4_quant(W_f16):
+    """fp16 [n][k] (k % 128 == 0) -> (codes uint8 [n][k/2], scales float32 [n][k/128])."""
+    W = np.ascontiguousarray(np.asarray(W_f16, dtype=np.float16).view(np.uint16))
+    n, k = W.shape
+    codes = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, k // 128), np.float32)
+    lib().orc_q4_quant(_p(W, C.c_uint16), n, k, _p(codes, C.c_uint8), _p(scales, C.c_float))
+    return codes, scales
+
+
+def q4_dequant(codes, scales) -> np.ndarray:
+    """-> fp16 [n][k]: fp16(float(code) * scale)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    n, k = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, k), np.uint16)
+    lib().orc_q4_dequant(_p(codes, C.c_uint8), _p(scales, C.c_float), n, k, _p(out, C.c_uint16))
+    return out.view(np.float16)
 
 
 # ---- building blocks ---------------------------------------------------------

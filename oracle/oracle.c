@@ -158,6 +158,55 @@ void orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, fl
 }
 
 /* ------------------------------------------------------------------------ */
+/* Weight-only INT4, groups of 128 columns, fp32 scales                      */
+/* The rebuild page (section 5.2) dequantizes an INT4 weight as
+ * int4_value * scale with the scale in fp32 and rounds the product to fp16
+ * (round to nearest) before use; its quantizer is not given.  Here: per
+ * (row, group of 128 columns) the symmetric scale amax / 7 in fp32 (1 when
+ * the group is all zeros), codes rint(w / scale) clamped to [-8, 7], stored
+ * as 4-bit two's complement, column 2j in the low nibble of byte j.         */
+
+void orc_q4_quant(const uint16_t* W, int n, int k, uint8_t* codes, float* scales) {
+    const int ng = k / ORC_Q4_GROUP;
+    for (int r = 0; r < n; ++r)
+        for (int g = 0; g < ng; ++g) {
+            const uint16_t* w = W + (size_t)r * k + (size_t)g * ORC_Q4_GROUP;
+            float amax = 0.0f;
+            for (int i = 0; i < ORC_Q4_GROUP; ++i) {
+                const float a = fabsf((float)orc_h2d(w[i]));
+                if (a > amax) amax = a;
+            }
+            float scale = amax / 7.0f;
+            if (!(scale > 0.0f)) scale = 1.0f;
+            scales[(size_t)r * ng + g] = scale;
+            for (int i = 0; i < ORC_Q4_GROUP; i += 2) {
+                int q[2];
+                for (int h = 0; h < 2; ++h) {
+                    float v = rintf((float)orc_h2d(w[i + h]) / scale);
+                    if (v < -8.0f) v = -8.0f;
+                    if (v > 7.0f) v = 7.0f;
+                    q[h] = (int)v;
+                }
+                codes[((size_t)r * k + (size_t)g * ORC_Q4_GROUP + i) / 2] = (uint8_t)((q[0] & 15) | ((q[1] & 15) << 4));
+            }
+        }
+}
+
+int orc_q4_code(const uint8_t* codes, size_t idx) {
+    const int nib = (codes[idx / 2] >> ((idx & 1) * 4)) & 15;
+    return nib >= 8 ? nib - 16 : nib;
+}
+
+void orc_q4_dequant(const uint8_t* codes, const float* scales, int n, int k, uint16_t* out) {
+    const int ng = k / ORC_Q4_GROUP;
+    for (int r = 0; r < n; ++r)
+        for (int c = 0; c < k; ++c) {
+            const float prod = (float)orc_q4_code(codes, (size_t)r * k + c) * scales[(size_t)r * ng + c / ORC_Q4_GROUP];
+            out[(size_t)r * k + c] = orc_d2h((double)prod);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Building blocks                                                           */
 
 static double g_h2d_tab[65536];

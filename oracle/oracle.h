@@ -49,6 +49,19 @@ void  orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale, floa
 float orc_seg_dequant(uint8_t code, float scale, float zp);
 void  orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, float* out);
 
+/* ---- weight-only INT4 (groups of 128 columns, fp32 scales) ---------------
+ * "LLM inference architecture rebuild", §5.2: an INT4 weight is used as
+ * fp16(int4_value * scale) with an fp32 scale and round-to-nearest.  The
+ * quantizer (not on the pages): per (row, 128-column group) scale =
+ * amax / 7 in binary32 (1 for an all-zero group), code = clamp(rint(w /
+ * scale), -8, 7), 4-bit two's complement, column 2j in the low nibble of
+ * byte j of the row.  k % 128 == 0.  codes: [n][k/2]; scales: [n][k/128]. */
+#define ORC_Q4_GROUP 128
+void orc_q4_quant(const uint16_t* W, int n, int k, uint8_t* codes, float* scales);
+int  orc_q4_code(const uint8_t* codes, size_t idx);     /* signed code of element idx */
+/* out (binary16 bits) = fp16(float(code) * scale): binary32 product, then RNE */
+void orc_q4_dequant(const uint8_t* codes, const float* scales, int n, int k, uint16_t* out);
+
 /* ---- building blocks (binary64) ----------------------------------------- */
 void   orc_rmsnorm(const double* x, const uint16_t* gain, int d, double eps, double* out);
 void   orc_rope(double* v, int hd, int pos, double base);      /* in place, pairs (j, j+hd/2) */
