@@ -195,7 +195,8 @@ COLD_BYTES = 768 << 20   # > 2x the 256 MB last-level (MALL) cache
 
 def gemv_microbench(rd, torch, stream, iters: int = 3):
     """The weight-streaming GEMV alone: y = W x (fp16 in, fp32 out) at batch
-    1 and 8 on the listed shapes.  Cold cache: launches rotate over distinct
+    1 and 8 on the listed shapes, and at batch 1 with the weights in INT4
+    (groups of 128 columns, fp32 scales: 0.53 bytes per weight).  Cold cache: launches rotate over distinct
     copies of W totalling >= 768 MiB, so every launch streams W from HBM.
     Kernel time: the launches are captured into one graph and replayed
     back to back between one pair of events, so no per-launch host or event
@@ -235,7 +236,38 @@ def gemv_microbench(rd, torch, stream, iters: int = 3):
             gbps = nbytes / (us * 1e-6) / 1e9
             row[f"b{batch}"] = {"us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
             print(f"[bench] gemv [{N},{K}] batch {batch}: {us:.2f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
-        del copies, Wd
+        # weight-only INT4 (groups of 128 columns, fp32 scales) at batch 1
+        qbytes = N * K // 2 + N * (K // 128) * 4
+        nq = max(2, -(-COLD_BYTES // qbytes))
+        qc = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+        qs = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")
+        rd.rd_q4_quantize(Wd.data_ptr(), N, K, qc.data_ptr(), qs.data_ptr(), stream.cuda_stream)
+        del copies
+        qcopies = [(qc, qs)] + [(qc.clone(), qs.clone()) for _ in range(nq - 1)]
+        for c, sc in qcopies:
+            rd.rd_gemv_q4(c.data_ptr(), sc.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, stream.cuda_stream)
+        torch.cuda.synchronize()
+        n = nq * iters
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                c, sc = qcopies[i % nq]
+                rd.rd_gemv_q4(c.data_ptr(), sc.data_ptr(), Xd.data_ptr(), y.data_ptr(), N, K, stream.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        del g
+        nbytes = qbytes + K * 2 + N * 4
+        gbps = nbytes / (us * 1e-6) / 1e9
+        row["q4_b1"] = {"us": round(us, 3), "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "bytes": nbytes, "copies": nq}
+        print(f"[bench] gemv int4 [{N},{K}] batch 1: {us:.2f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+        del qcopies, qc, qs, Wd
         torch.cuda.empty_cache()
         out.append(row)
     return out

@@ -331,6 +331,27 @@ rd_status rd_attention_f16(const float* q, const void* K, const void* V, float* 
                            int32_t n_kv_heads, int32_t hd, int32_t L, int32_t ld, float scale, int32_t splits,
                            void* stream);
 
+/* Weight-only INT4 with fp32 scales ("LLM inference architecture
+ * rebuild", §5.2: an INT4 weight is used as fp16(int4_value * scale), the
+ * scale in fp32, round-to-nearest; "Real-time LLM inference on standard
+ * GPUs", section on memory bandwidth: about 4 FLOP per weight byte at 4
+ * bits).  Quantizer (the library's reading; the pages give none): per
+ * (row, group of 128 columns) scale = amax / 7 in fp32 (1 for an all-zero
+ * group), code = clamp(rint(w / scale), -8, 7), 4-bit two's complement,
+ * column 2j in the low nibble of byte j of the row.
+ * W: device fp16 [N][K] (16-byte aligned); codes: device u8 [N][K/2];
+ * scales: device f32 [N][K/128] (4-byte aligned).  128 <= K <= 8192,
+ * K % 128 == 0. */
+rd_status rd_q4_quantize(const void* W, int32_t N, int32_t K, uint8_t* codes, float* scales, void* stream);
+
+/* y[n] = sum_k fp16(code[n][k] * scale[n][k/128]) * x[k], fp16 x, fp32
+ * accumulation (v_dot2_f32_f16 steps, as the fp16 GEMV), batch 1: the
+ * weight-streaming GEMV at 0.53 bytes per weight.  codes, scales as
+ * rd_q4_quantize writes them; x: device fp16 [K]; y: device f32 [N].
+ * codes and x 16-byte aligned.  Nothing is allocated. */
+rd_status rd_gemv_q4(const uint8_t* codes, const float* scales, const void* x, float* y, int32_t N, int32_t K,
+                     void* stream);
+
 /* out[i] = E5M2 encoding of the fp16 value in[i] (round to nearest even on
  * the dropped mantissa bits, overflow to inf, NaN to quiet NaN): the KV
  * format of "How the xAI engineering team cut Grok Bot latency to

@@ -83,6 +83,8 @@ SIGNATURES = [
                             _I32, _VP]),
     ("rd_attention_noalloc", _I32, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, _I32,
                                     C.c_float, _I32, _VP]),
+    ("rd_q4_quantize", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
+    ("rd_gemv_q4", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
     ("rd_seg_quant", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
     ("rd_argmax_f32", _I32, [_VP, _I32, _VP, _VP]),
@@ -316,6 +318,14 @@ def rd_attention_noalloc(q: int, K: int, V: int, out: int, n_heads: int, n_kv_he
     check(lib().rd_attention_noalloc(q, K, V, k_stage or None, v_stage or None, k_meta or None, v_meta or None, out,
                                      n_heads, n_kv_heads, hd, L, ld, KV_FORMATS[kv_format], scale, splits,
                                      stream or None))
+
+
+def rd_q4_quantize(W: int, N: int, K: int, codes: int, scales: int, stream: int = 0):
+    check(lib().rd_q4_quantize(W, N, K, codes, scales, stream or None))
+
+
+def rd_gemv_q4(codes: int, scales: int, x: int, y: int, N: int, K: int, stream: int = 0):
+    check(lib().rd_gemv_q4(codes, scales, x, y, N, K, stream or None))
 
 
 def rd_e5m2_encode(inp: int, out: int, n: int, stream: int = 0):

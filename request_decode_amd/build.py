@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librd.so")
-SOURCES = ["rd_kernels.hip", "rd_gemv.hip", "rd_batch.hip", "rd_persistent.hip", "rd_prefill.hip", "rd_api.hip"]
+SOURCES = ["rd_kernels.hip", "rd_gemv.hip", "rd_batch.hip", "rd_persistent.hip", "rd_prefill.hip", "rd_q4.hip", "rd_api.hip"]
 
 # Packed fp32 VALU ops are kept out of the generated code on purpose.
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

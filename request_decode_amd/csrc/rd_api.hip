@@ -1079,6 +1079,28 @@ extern "C" rd_status rd_attention_f16(const float* q, const void* Kc, const void
                         splits, stream);
 }
 
+extern "C" rd_status rd_q4_quantize(const void* W, int32_t N, int32_t K, uint8_t* codes, float* scales, void* stream) {
+    if (!W || !codes || !scales) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (N < 1 || K < 128 || K % 128 || K > 8192) return fail(RD_ERR_INVALID_ARG, "need N >= 1, K a multiple of 128 in [128, 8192]");
+    if (((uintptr_t)W & 15) || ((uintptr_t)codes & 3) || ((uintptr_t)scales & 3))
+        return fail(RD_ERR_INVALID_ARG, "W must be 16-byte aligned, codes and scales 4-byte aligned");
+    K_TRY(launch_q4_quant(W, N, K, codes, scales, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_gemv_q4(const uint8_t* codes, const float* scales, const void* x, float* y, int32_t N,
+                                int32_t K, void* stream) {
+    if (!codes || !scales || !x || !y) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (N < 1 || K < 128 || K % 128 || K > 8192) return fail(RD_ERR_INVALID_ARG, "need N >= 1, K a multiple of 128 in [128, 8192]");
+    if (((uintptr_t)codes | (uintptr_t)x) & 15) return fail(RD_ERR_INVALID_ARG, "codes and x must be 16-byte aligned");
+    if ((uintptr_t)scales & 3) return fail(RD_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+    int dev = 0, ncu = 0;
+    K_TRY(hipGetDevice(&dev));
+    K_TRY(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+    K_TRY(launch_gemv_q4(codes, scales, x, y, N, K, ncu, (hipStream_t)stream));
+    return RD_OK;
+}
+
 extern "C" rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* stream) {
     if ((!in || !out) && n) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
     K_TRY(launch_e5m2(in, out, n, (hipStream_t)stream));

@@ -193,6 +193,11 @@ bool prefill_supported(int D, int H, int hd, int F, int B);
 // Positions p0 .. p0+T-1 (T <= ws.tc) of sequence 0, tokens in ws.tok.
 hipError_t prefill_chunk(const StepArgs& A, const PrefillWs& ws, int p0, int T, hipStream_t s);
 
+// Weight-only INT4 (rd_q4.hip): codes [N][K/2], scales [N][K/128]; K % 128 == 0, K <= 8192.
+hipError_t launch_q4_quant(const void* W, int N, int K, uint8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_gemv_q4(const uint8_t* codes, const float* scales, const void* x, float* y, int N, int K, int ncu,
+                          hipStream_t s);
+
 // Host launchers (rd_kernels.hip).
 int kch_for(int K);
 hipError_t launch_step(const StepArgs& A, hipStream_t s);

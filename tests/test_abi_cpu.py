@@ -120,3 +120,15 @@ def test_blob_layout_matches_shapes():
     assert params == 1_263_634_432
     assert all(off % 256 == 0 for *_, off in lay)
     assert total >= 256 + 2 * params
+
+
+def test_q4_argument_checks(rd):
+    # rejected before anything touches a device: fake aligned pointers
+    L, p = rd.lib(), C.c_void_p(256)
+    assert L.rd_gemv_q4(p, p, p, p, 16, 100, None) == rd.RD_ERR_INVALID_ARG     # K % 128
+    assert L.rd_gemv_q4(p, p, p, p, 16, 8320, None) == rd.RD_ERR_INVALID_ARG    # K > 8192
+    assert L.rd_gemv_q4(p, p, p, p, 0, 128, None) == rd.RD_ERR_INVALID_ARG
+    assert L.rd_gemv_q4(C.c_void_p(258), p, p, p, 16, 128, None) == rd.RD_ERR_INVALID_ARG   # alignment
+    assert L.rd_q4_quantize(p, 16, 64, p, p, None) == rd.RD_ERR_INVALID_ARG
+    assert L.rd_q4_quantize(None, 16, 128, p, p, None) == rd.RD_ERR_INVALID_ARG
+
