@@ -118,7 +118,7 @@ def cpu_baseline(blob, shape, seconds: float, base: int, first: int):
                       f"greedy decode steps at positions {base}..{base + n - 1} (the timed positions' start)"}
 
 
-def layer_trace(m, token: int, reps: int):
+def layer_trace(m, token: int, reps: int, rewind: bool = True):
     """Where a layer of one persistent step spends its time, from the kernel's
     in-kernel event trace of every workgroup (rd_debug_trace_step_all; the
     wall clock is shared by all CUs).  Per workgroup and layer (the middle
@@ -129,11 +129,13 @@ def layer_trace(m, token: int, reps: int):
     attention split <- QKV (attention workgroups), the merge <- attention
     (merge workgroups), O <- merge (merge workgroups), gate/up <- O and
     down <- gate/up.  Reported: medians over workgroups and layers, in us,
-    of the last of `reps` traced steps (the first is not used)."""
+    of the last of `reps` traced steps (the first is not used).  A cache
+    that cannot be rewound (INT8) is traced on consecutive positions."""
     import numpy as np
     for _ in range(max(2, reps)):
         tr = m.trace_step_all(token)
-        m.set_position(m.position() - 1)
+        if rewind:
+            m.set_position(m.position() - 1)
     per = []
     for codes, clk in tr:
         d, occ = {}, {}
@@ -325,7 +327,8 @@ def main():
     # INT8 KV can only be rewound to a segment start: there the timed steps
     # follow the warmup steps instead of repeating their positions
     rewind = args.kv != "int8"
-    ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup) + 1   # +1: the phase run
+    # +1: the phase run; an INT8 cache is traced on further positions
+    ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup + max(2, args.trace)) + 1
     m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream,
                  batch=B, attn_splits=args.attn_splits)
     executor = m.get_info().executor
@@ -372,10 +375,13 @@ def main():
           f"{gbps:.0f} GB/s (host wall clock {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
 
     trace = None
-    if args.trace and persistent and rewind:
-        m.set_position(base + args.steps // 2)
-        tok = int(out[args.steps // 2 - 1].item()) if args.steps >= 2 else first
-        trace = layer_trace(m, tok, args.trace)
+    if args.trace and persistent and B == 1:
+        if rewind:
+            m.set_position(base + args.steps // 2)
+            tok = int(out[args.steps // 2 - 1].item()) if args.steps >= 2 else first
+        else:
+            tok = int(out[args.steps - 1].item())
+        trace = layer_trace(m, tok, args.trace, rewind)
         print(f"[bench] layer trace (us, medians over workgroups and layers 2..21): {trace}", file=sys.stderr,
               flush=True)
 

@@ -95,9 +95,11 @@ typedef struct {
     int32_t executor;     /* rd_executor */
     int32_t attn_splits;  /* maximum key-axis splits per kv-head, 1..256; 0 = default: CUs / kv-heads
                              at batch 1, 2 * CUs / (kv-heads * max_batch) above, within 1..64.
-                             Each split covers at least 48 keys.  The persistent kernels merge at
-                             most 32 (2B-class shape) or 64 (test shapes) splits: with more, AUTO
-                             takes GRAPH and PERSISTENT is UNSUPPORTED. */
+                             Each split covers at least 48 keys.  INT8_SEG128: at least 2 (the
+                             open segment is a split of its own; its sealed positions use at most
+                             attn_splits - 1).  The persistent kernels merge at most 32
+                             (2B-class shape) or 64 (test shapes) splits: with more, AUTO takes
+                             GRAPH and PERSISTENT is UNSUPPORTED. */
 } rd_options;
 
 typedef struct {
@@ -126,7 +128,9 @@ void rd_options_init(rd_options* opt);
  * blob: host, borrowed for the call only (copied and re-tiled).
  * The QKV rows are re-ordered (RoPE pairs adjacent) and the gate/up rows
  * interleaved once, here, into the layout the kernels stream.
- * Errors: INVALID_ARG (NULL, bad options), BAD_BLOB, UNSUPPORTED (a shape the
+ * Errors: INVALID_ARG (NULL, bad options; attn_splits 1 with INT8_SEG128;
+ * n_kv_heads * max_context * head_dim * element bytes above 2^31 - 1, the
+ * 32-bit offsets of the attention's row loads), BAD_BLOB, UNSUPPORTED (a shape the
  * kernels do not cover: head_dim must be 64 or 128, n_heads / n_kv_heads 1,
  * 2, 4 or 8, d_model and d_ff multiples of 8, d_model <= 4096,
  * n_heads * head_dim <= 4096, d_ff <= 8192; max_batch > 1 with the
@@ -301,7 +305,9 @@ rd_status rd_gemv_f16(const void* W, const void* x, float* y, int32_t N, int32_t
  *     k_stage/v_stage, device u16 [n_kv_heads][128][hd] (fp16, row p % 128).
  *     Other formats: the four pointers are ignored (may be NULL).
  * scale: the softmax scale (1/sqrt(hd) in the model); hd 64 or 128;
- * 1 <= L <= ld; 1 <= splits <= 256; n_heads <= 128.  q, K, V and the
+ * 1 <= L <= ld; 1 <= splits <= 256 (INT8_SEG128: >= 2, the open segment
+ * being a split of its own); n_kv_heads * ld * hd * element bytes below
+ * 2 GiB; n_heads <= 128.  q, K, V and the
  * staging rows 16-byte aligned, the tables 8-byte aligned.  Uses a library
  * scratch buffer (split partials), allocated on the device's first call and
  * kept until the process ends: calls that overlap on one device (several

@@ -293,12 +293,17 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
         return fail(RD_ERR_INVALID_ARG, "bad kv_format");
     if (opt.executor < RD_EXEC_AUTO || opt.executor > RD_EXEC_PERSISTENT) return fail(RD_ERR_INVALID_ARG, "bad executor");
     if (opt.attn_splits < 0 || opt.attn_splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "attn_splits out of range");
+    if (opt.kv_format == RD_KV_INT8_SEG128 && opt.attn_splits == 1)
+        return fail(RD_ERR_INVALID_ARG, "the INT8 cache needs at least 2 attention splits (the open segment has its own)");
 
     BlobDims d;
     std::string err;
     if (!parse_blob((const uint8_t*)blob, blob_bytes, d, err)) return fail(RD_ERR_BAD_BLOB, err);
     const char* why = nullptr;
     if (!step_supported(d.D, d.H, d.Hk, d.hd, d.F, &why)) return fail(RD_ERR_UNSUPPORTED, why);
+    // attention reads a layer's K or V with 32-bit byte offsets
+    if ((uint64_t)d.Hk * opt.max_context * d.hd * (opt.kv_format == RD_KV_FP16 ? 2 : 1) > 0x7fffffffull)
+        return fail(RD_ERR_INVALID_ARG, "n_kv_heads * max_context * head_dim * element bytes must stay below 2 GiB");
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(RD_ERR_DEVICE, "no HIP device");
@@ -317,7 +322,8 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, opt.device) != hipSuccess || cus < 1)
         cus = 1;
     const int s_def = opt.max_batch > 1 ? 2 * cus / ((int)d.Hk * opt.max_batch) : cus / (int)d.Hk;
-    m->S = opt.attn_splits ? opt.attn_splits : std::max(1, std::min(64, s_def));
+    m->S = opt.attn_splits ? opt.attn_splits
+                           : std::max(opt.kv_format == RD_KV_INT8_SEG128 ? 2 : 1, std::min(64, s_def));
     auto bail = [&](rd_status st) {
         std::string keep = g_err;
         free_model(m);
@@ -981,6 +987,7 @@ rd_status attention_call(const float* q, const void* Kc, const void* Vc, const u
         A.vmeta = const_cast<float*>(vmeta);
     }
     A.part = part;
+    A.ro = q;     // fetched in place of past-the-end rows (values never used)
     A.pos_ptr = posw;
     A.ld = ld;
     A.nseg = (ld + SEG - 1) / SEG;
@@ -1006,6 +1013,10 @@ rd_status attention_args_ok(const float* q, const void* Kc, const void* Vc, cons
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(RD_ERR_INVALID_ARG, "n_heads/n_kv_heads must be 1, 2, 4 or 8");
     if (L < 1 || L > ld) return fail(RD_ERR_INVALID_ARG, "need 1 <= L <= ld");
     if (splits < 1 || splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "splits out of range");
+    if (kvf == RD_KV_INT8_SEG128 && splits < 2)
+        return fail(RD_ERR_INVALID_ARG, "the INT8 cache needs at least 2 splits (the open segment has its own)");
+    if ((uint64_t)Hk * ld * hd * (kvf == RD_KV_FP16 ? 2 : 1) > 0x7fffffffull)
+        return fail(RD_ERR_INVALID_ARG, "n_kv_heads * ld * hd * element bytes must stay below 2 GiB");
     if (((uintptr_t)q | (uintptr_t)Kc | (uintptr_t)Vc | (uintptr_t)kst | (uintptr_t)vst) & 15)
         return fail(RD_ERR_INVALID_ARG, "q, K, V and the staging rows must be 16-byte aligned");
     if (((uintptr_t)kmeta | (uintptr_t)vmeta) & 7) return fail(RD_ERR_INVALID_ARG, "meta tables must be 8-byte aligned");

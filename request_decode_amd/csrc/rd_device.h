@@ -159,6 +159,17 @@ __device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
 // Wait until this wave's outstanding vector-memory operations completed
 // (loads returned, stores acknowledged at the coherence point).
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order, so every older one is done).
+// A real s_waitcnt the compiler sees and accounts for: where its own count
+// is lost (loads behind a loop of unknown trip count) it would otherwise
+// wait for all of them.  vmcnt is 6 bits on gfx9: bits 3:0 and 15:14;
+// expcnt (6:4) and lgkmcnt (11:8) at their maxima do not wait.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Count this workgroup's arrival on *cnt after all of its threads' stores
 // completed; true in every thread of the workgroup that arrives last of

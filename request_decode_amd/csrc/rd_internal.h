@@ -45,6 +45,11 @@ struct AttnArgs {
     void* kcw;               // INT8: writable code rows of K and V (sealed by the merge)
     void* vcw;
     float* part;             // [H][S][hd+2] split partials: o[hd], m, l
+    // at least hd*2 bytes that no attention step changes and that decode to
+    // finite fp16 and E5M2 values (position 0's RoPE row: cos 1, sin 0; the
+    // standalone attention entry point: its queries, whose values are never
+    // used there): fetched in place of cache rows whose values are not used
+    const void* ro;
     const int* pos_ptr;      // L = *pos_ptr + 1
     int ld, nseg, H, Hk, S;
     float scale;
@@ -135,6 +140,7 @@ __host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
         T.vmeta = A.meta + ((size_t)l * 2 + 1) * A.Hk * A.nseg * 2;
     }
     T.part = A.part;
+    T.ro = A.rope;
     T.pos_ptr = &A.st->pos;
     T.ld = A.max_ctx;
     T.nseg = A.nseg;

@@ -75,25 +75,27 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
     constexpr int NW = ATT_WAVES;
     __shared__ float s_att[NW * G * (HD + 2)];
     const int pos = *T.pos_ptr, L = pos + 1;
-    int chunk, nact;
-    split_plan(L, T.S, chunk, nact);
+    const SplitPlan pl = split_plan(L, T.S, KVF);
     const int t = blockIdx.x;   // one split of one kv-head per workgroup
-    if (t >= T.Hk * nact) return;
-    const int g = t / nact, s = t % nact, w = wave_id();
+    if (t >= T.Hk * pl.nact) return;
+    const int g = t / pl.nact, s = t % pl.nact, w = wave_id();
     const int lane = lane_id(), j = lane % Geo::LPR;
-    const int p0 = s * chunk, p1 = min(L, p0 + chunk), open0 = pos / SEG * SEG;
-    KvBuf<HD> kb, vb;
-    attn_wave_first<HD, KVF, false, NW>(T, g, p0, p1, open0, pos, w, kb, vb);
-    const float qs = T.scale * LOG2E;
-    float qv[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
+    int p0, p1;
+    split_range(pl, L, s, p0, p1);
     AttnAcc<HD, G> acc;
     acc.clear();
-    attn_wave_run<HD, G, KVF, false, NW>(T, g, p0, p1, open0, pos, w, qv, acc, kb, vb,
-                                         [](int, float (&)[Geo::U][8], float (&)[Geo::U][8]) {});
+    with_src<HD, KVF, false>(T, g, pos, s == pl.ncut, [&](auto src) {
+        using Src = decltype(src);
+        typename Src::Buf kb[3];
+        attn_wave_first<Src, NW>(src, p0, p1, w, kb);
+        const float qs = T.scale * LOG2E;
+        float qv[G][8];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
+        attn_wave_run<Src, NW>(src, p0, p1, w, qv, acc, kb, NoFix{});
+    });
     acc.finish();
     attn_part_store<HD, G>(s_att, w, acc);
     __syncthreads();
@@ -121,8 +123,7 @@ __global__ __launch_bounds__(WG) void k_merge(AttnArgs T0) {
     using Geo = AttnGeo<HD>;
     const AttnArgs T = attn_seq(T0, blockIdx.y);   // sequence blockIdx.y
     const int pos = *T.pos_ptr;
-    int chunk, nact;
-    split_plan(pos + 1, T.S, chunk, nact);
+    const int nact = split_plan(pos + 1, T.S, KVF).nact;
     const int t = blockIdx.x * (WG / WAVE) + wave_id();
     if (t >= T.H * Geo::NPART) return;
     const int h = t / Geo::NPART, part = t % Geo::NPART, lane = lane_id();

@@ -570,42 +570,41 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
 constexpr int NWA = NSW;
 static_assert(NWA == ATT_WAVES, "the graph executor's attention uses the same number of waves");
 struct AttnSplit {
-    int pos, L, t, g, s, p0, p1, open0;
+    int pos, L, t, g, s, p0, p1, nact;
+    bool open;   // INT8: the split over the open segment (fp16 staging rows)
 };
+template <int KVF>
 __device__ __forceinline__ AttnSplit attn_split(const StepArgs& A, const PersistArgs& P, int step) {
     AttnSplit r;
     r.pos = P.pos0 + step;
     r.L = r.pos + 1;
-    int chunk, nact;
-    split_plan(r.L, A.S, chunk, nact);
-    r.t = (int)blockIdx.x < A.Hk * nact ? (int)blockIdx.x : -1;
-    r.g = r.t / nact;
-    r.s = r.t % nact;
-    r.p0 = r.s * chunk;
-    r.p1 = min(r.L, r.p0 + chunk);
-    r.open0 = r.pos / SEG * SEG;
+    const SplitPlan pl = split_plan(r.L, A.S, KVF);
+    r.nact = pl.nact;
+    r.t = (int)blockIdx.x < A.Hk * pl.nact ? (int)blockIdx.x : -1;
+    r.g = r.t / pl.nact;
+    r.s = r.t % pl.nact;
+    split_range(pl, r.L, r.s, r.p0, r.p1);
+    r.open = KVF == KV_INT8 && r.s == pl.ncut;
     return r;
 }
 template <int HD, int G>
 constexpr int attn_nq() { return G * 8 + 16; }
-// Row pos of the batch: this step's K/V row, from the exchange (it may not
-// be visible in the cache yet).
-template <int HD, int G>
-__device__ __forceinline__ void fix_new_row(int pb, int pos, const float (&kn)[8], const float (&vn)[8],
-                                            float (&kf)[AttnGeo<HD>::U][8], float (&vf)[AttnGeo<HD>::U][8]) {
-    const int slot = lane_id() / AttnGeo<HD>::LPR;
+// Row pos: this step's K/V row, from the exchange (it may not be visible in
+// the cache yet; the sources never fetch it under P).
+struct FixNewRow {
+    int pos;
+    const float (&kn)[8];
+    const float (&vn)[8];
+    __device__ __forceinline__ bool active(int pb, int n) const { return pb <= pos && pos < pb + n; }
+    __device__ __forceinline__ void apply(int p, int which, float (&f)[8]) const {
+        if (p == pos)
 #pragma unroll
-    for (int u = 0; u < AttnGeo<HD>::U; ++u)
-        if (batch_row<HD>(pb, u, slot) == pos)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                kf[u][i] = kn[i];
-                vf[u][i] = vn[i];
-            }
-}
+            for (int i = 0; i < 8; ++i) f[i] = which ? vn[i] : kn[i];
+    }
+};
 template <int HD, int G, int KVF>
 __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A, const AttnSplit& sp, int w,
-                                            float* s_r, KvBuf<HD>& kb, KvBuf<HD>& vb) {
+                                            float* s_r, KvBuf<KVF> (&kb)[3]) {
     constexpr int NQ = attn_nq<HD, G>();
     lds_barrier();   // q and the new row staged
     if (sp.t >= 0) {
@@ -622,11 +621,10 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
         }
         AttnAcc<HD, G> acc;
         acc.clear();
-        attn_wave_run<HD, G, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sp.pos, w, qv, acc, kb, vb,
-                                             [&](int pb, float (&kf)[AttnGeo<HD>::U][8],
-                                                 float (&vf)[AttnGeo<HD>::U][8]) {
-                                                 fix_new_row<HD, G>(pb, sp.pos, kn, vn, kf, vf);
-                                             });
+        with_src<HD, KVF, true>(T, sp.g, sp.pos, sp.open, [&](auto src) {
+            using Src = decltype(src);
+            attn_wave_run<Src, NWA>(src, sp.p0, sp.p1, w, qv, acc, kb, FixNewRow{sp.pos, kn, vn});
+        });
         acc.finish();
         attn_part_store<HD, G>(s_r + NQ * 64, w, acc);
     }
@@ -643,15 +641,18 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
     const int NL = A.n_layers;
     auto none = [] {};
     for (int step = 0; step < P.n_steps; ++step) {
-        const AttnSplit sp = attn_split(A, P, step);
+        const AttnSplit sp = attn_split<KVF>(A, P, step);
         for (int l = 0; l < NL; ++l) {
             const AttnArgs T = attn_args(A, l);
-            KvBuf<HD> kb, vb;
+            KvBuf<KVF> kb[3];
             // after its QKV rows: the raw K/V rows of its first attention batch
             stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr, [&] {
-                if (sp.t >= 0) attn_wave_first<HD, KVF, true, NWA>(T, sp.g, sp.p0, sp.p1, sp.open0, sp.pos, sw, kb, vb);
+                if (sp.t >= 0)
+                    with_src<HD, KVF, true>(T, sp.g, sp.pos, sp.open, [&](auto src) {
+                        attn_wave_first<decltype(src), NWA>(src, sp.p0, sp.p1, sw, kb);
+                    });
             });
-            attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, vb);
+            attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb);
             stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none);
             stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none);
             stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none);
@@ -668,7 +669,7 @@ template <int KD, int KA, int KF, int HD, int G, int KVF, int SMAX>
 __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArgs& P, float* s_r,
                                              const float* s_part, float* s_own, int* s_nev) {
     using Geo = AttnGeo<HD>;
-    constexpr int U = Geo::U, LPR = Geo::LPR, RPW = Geo::RPW;
+    constexpr int LPR = Geo::LPR;
     const int lane = lane_id(), NL = A.n_layers, b = blockIdx.x, nwg = gridDim.x;
     Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
     const Tracer TR = make_tracer(P, s_nev);
@@ -694,10 +695,8 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     }
 
     for (int step = 0; step < P.n_steps; ++step) {
-        const AttnSplit sp = attn_split(A, P, step);
-        const int pos = sp.pos, L = sp.L, t = sp.t, g = sp.g, s = sp.s, p0 = sp.p0, p1 = sp.p1, open0 = sp.open0;
-        int chunk, nact;
-        split_plan(L, A.S, chunk, nact);
+        const AttnSplit sp = attn_split<KVF>(A, P, step);
+        const int pos = sp.pos, L = sp.L, t = sp.t, g = sp.g, s = sp.s, p1 = sp.p1, nact = sp.nact;
         const float2* rope = A.rope + (size_t)pos * (HD / 2);
         // gains of the first RMSNorm (later ones are loaded while the wait before
         // them is pending, so that their latency hides in the wait)

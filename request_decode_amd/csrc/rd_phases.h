@@ -250,187 +250,209 @@ template <int HD>
 struct AttnGeo {
     static constexpr int LPR = HD / 8;
     static constexpr int RPW = WAVE / LPR;
-    static constexpr int U = 4;                 // rows per lane per batch
-    static constexpr int BATCH = RPW * U;       // rows per batch
     static constexpr int NPART = HD / 64;       // merge tasks per query head (64 dims each)
 };
 
-// Splits of L attended positions: at most S of them, each a multiple of 4
-// keys and at least 48 (one 16-row batch for each of the three waves that
-// reduce a split): below that, a split's latency no longer shrinks, and every
-// extra split is one more partial for the merge to wait for.
-__device__ __forceinline__ void split_plan(int L, int S, int& chunk, int& nact) {
-    chunk = (L + S - 1) / S;
-    chunk = (chunk + 3) & ~3;
-    chunk = chunk < 48 ? 48 : chunk;
-    nact = (L + chunk - 1) / chunk;
-}
-
-// One lane's 8 elements (dims j*8..+7) of K or V row p as stored, and their
-// dequantization.  Under P the reads that can meet a stale line are
-// agent-coherent: INT8 open-segment rows (the staging buffer is reused every
-// 128 steps), INT8 scales (several segments share a line), head_dim-64 E5M2
-// rows (two rows share a 128-byte line, so fetching an older row can bring in
-// the line of the row being written).  The other rows (fp16 rows, head_dim-128
-// E5M2 rows, sealed codes: whole lines of one row, or of one sealed segment)
-// are first fetched in a step after the one that wrote them: the row of the
-// current step is never fetched from the cache under P (kv_batch_raw).
-struct KvRaw {
-    u4v d;         // fp16: 8 halves; E5M2: 8 bytes in d.x, d.y; INT8: codes in d.x, d.y or 8 fp16
-    float scale;   // INT8 sealed row: its segment's scale and zero point; < 0: an fp16 open-segment row
-    float zp;
+// ---- splits ---------------------------------------------------------------
+// The L attended positions of a step are cut into splits, one workgroup
+// each.  fp16 and E5M2: at most S splits of `chunk` positions, a multiple of
+// 4 and at least 48 (one 16-row batch for each of the three waves that reduce
+// a split: below that a split's latency no longer shrinks, and every extra
+// split is one more partial for the merge to wait for).  INT8: the sealed
+// positions [0, open0) in at most S - 1 such splits, then one split over the
+// open segment [open0, L), whose rows are fp16 staging rows, so that every
+// split reads one kind of row (S >= 2).
+struct SplitPlan {
+    int chunk;   // positions per split of the cut range
+    int ncut;    // splits of the cut range [0, end)
+    int end;     // L (fp16, E5M2) or open0 (INT8)
+    int nact;    // splits in use: ncut, plus the open-segment split for INT8
 };
-template <int HD, int KVF, bool P>
-__device__ __forceinline__ KvRaw kv_raw(const AttnArgs& A, int which, int g, int p, int open0, int j) {
-    const size_t row = (size_t)g * A.ld + p;
-    const void* base = which ? A.vc : A.kc;
-    KvRaw r;
-    r.scale = -1.f;
-    r.zp = 0.f;
-    if constexpr (KVF == KV_FP16) {
-        r.d = __builtin_nontemporal_load(
-            reinterpret_cast<const u4v*>(reinterpret_cast<const _Float16*>(base) + row * HD + j * 8));
-    } else if constexpr (KVF == KV_E5M2) {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(base) + row * HD + j * 8);
-        const uint64_t u = (P && HD == 64) ? ld_agent(src) : __builtin_nontemporal_load(src);
-        r.d = u4v{(unsigned)u, (unsigned)(u >> 32), 0u, 0u};
-    } else {
-        if (p < open0) {
-            const u2v u = ld8(reinterpret_cast<const uint8_t*>(base) + row * HD + j * 8);
-            const float* mt = (which ? A.vmeta : A.kmeta) + ((size_t)g * A.nseg + p / SEG) * 2;
-            r.scale = P ? ld_agent(mt) : mt[0];
-            r.zp = P ? ld_agent(mt + 1) : mt[1];
-            r.d = u4v{u.x, u.y, 0u, 0u};
-        } else {
-            const uint16_t* st = which ? A.vst : A.kst;
-            const uint64_t* src = reinterpret_cast<const uint64_t*>(st + ((size_t)g * SEG + p % SEG) * HD + j * 8);
-            const uint64_t lo = P ? ld_agent(src) : src[0], hi = P ? ld_agent(src + 1) : src[1];
-            r.d = u4v{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi, (unsigned)(hi >> 32)};
-        }
-    }
-    return r;
+__device__ __forceinline__ SplitPlan split_plan(int L, int S, int kvf) {
+    SplitPlan sp;
+    const bool i8 = kvf == KV_INT8;
+    sp.end = i8 ? (L - 1) / SEG * SEG : L;
+    const int n = i8 ? S - 1 : S;
+    int chunk = (sp.end + n - 1) / n;
+    chunk = (chunk + 3) & ~3;
+    sp.chunk = chunk < 48 ? 48 : chunk;
+    sp.ncut = (sp.end + sp.chunk - 1) / sp.chunk;
+    sp.nact = sp.ncut + (i8 ? 1 : 0);
+    return sp;
 }
+// Positions [p0, p1) of split s < nact.
+__device__ __forceinline__ void split_range(const SplitPlan& sp, int L, int s, int& p0, int& p1) {
+    if (s < sp.ncut) {
+        p0 = s * sp.chunk;
+        p1 = min(sp.end, p0 + sp.chunk);
+    } else {
+        p0 = sp.end;
+        p1 = L;
+    }
+}
+
+// ---- K/V rows of a split ----------------------------------------------------
+// A source reads the rows of one kind of split with buffer loads.  A row that
+// must not be fetched (past the split, in a batch past the wave's last one,
+// or, in the persistent kernel (P), the row this step writes, whose value
+// comes from the exchange) gets an offset past the end of its buffer, and its
+// load returns zeros without touching memory.  So every batch of a source
+// issues the same loads, with no branch between a load and its registers: the
+// compiler's count of outstanding loads stays exact, and a batch waits only
+// for its own rows while the two batches after it stay in flight.
+//
+// Under P the reads that can meet a stale line are agent-coherent: INT8
+// open-segment rows (the staging buffer is reused every 128 steps), INT8
+// (scale, zp) pairs (several segments share a line), head_dim-64 E5M2 rows
+// (two rows share a 128-byte line, so fetching an older row can bring in the
+// line of the row being written).  The other rows (fp16 rows, head_dim-128
+// E5M2 rows, sealed codes: whole lines of one row, or of one sealed segment)
+// are first fetched in a step after the one that wrote them.
+enum { SRC_F16 = 0, SRC_E5M2 = 1, SRC_I8 = 2, SRC_STAGE = 3 };
+constexpr uint32_t ROW_NONE = 0x80000000u;   // past every attention buffer (each below 2 GiB)
+constexpr int AUX_PLAIN = 0, AUX_NT = 2, AUX_AGENT = 16;   // cache bits: none, nt, sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t attn_rsrc(const void* base, size_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                             0x00020000);
+}
+// Registers of one batch's raw rows, shared by the sources of a cache format
+// (the INT8 sealed and open-segment sources use the same words).
 template <int KVF>
-__device__ __forceinline__ void kv_cvt(const KvRaw& r, float (&f)[8]) {
-    if constexpr (KVF == KV_E5M2) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (float)e5m2_decode((uint8_t)(r.d[i >> 2] >> ((i & 3) * 8)));
-    } else if constexpr (KVF == KV_INT8) {
-        if (r.scale >= 0.f) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) f[i] = ((float)((r.d[i >> 2] >> ((i & 3) * 8)) & 0xffu) - r.zp) * r.scale;
-            return;
-        }
-        const h8 v = as_h8(r.d);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
-    } else {
-        const h8 v = as_h8(r.d);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
-    }
-}
+struct KvBuf {
+    uint32_t w[KVF == KV_INT8 ? 40 : 32];
+};
 
-// Row of slot `slot`, batch position u, of the batch starting at pb.
-template <int HD>
-__device__ __forceinline__ int batch_row(int pb, int u, int slot) { return pb + u * AttnGeo<HD>::RPW + slot; }
-
-// The raw K and V elements of this lane's U rows of the batch starting at pb
-// (rows at or past p1 read row p0 instead; they are masked when reduced).
-// Under P (one launch, several steps), row pos, the one this step writes, is
-// not fetched from the fp16 or E5M2 cache either: its value comes from the
-// exchange (the caller's fix), and a fetch racing its store could leave a copy
-// of the line from before the store in this XCD's L2, which a later step of
-// the same launch would then read.  Such rows fetch an older row instead (p0,
-// or pos - 1 when the split starts at pos); at pos 0 nothing is fetched.
-template <int HD, int KVF, bool P>
-__device__ __forceinline__ void kv_batch_raw(const AttnArgs& A, int g, int pb, int p0, int p1, int open0, int pos,
-                                             KvRaw (&kr)[AttnGeo<HD>::U], KvRaw (&vr)[AttnGeo<HD>::U]) {
+template <int HD, int SRC, bool P>
+struct KvSrc {
     using Geo = AttnGeo<HD>;
-    const int lane = lane_id(), slot = lane / Geo::LPR, j = lane % Geo::LPR;
-    if constexpr (KVF == KV_INT8) {
-        // the (scale, zp) pairs of the at most two segments the batch's rows
-        // fall in, one 8-byte load each for K and V (the same address in
-        // every lane), instead of two loads per row
-        const int last = min(pb + Geo::BATCH, p1) - 1;
-        const int s0 = pb / SEG, s1 = last / SEG;
-        const bool sealed0 = s0 * SEG < open0, sealed1 = s1 != s0 && s1 * SEG < open0;
-        auto meta = [&](const float* m, int sg) {
-            const uint64_t* q = reinterpret_cast<const uint64_t*>(m + ((size_t)g * A.nseg + sg) * 2);
-            return P ? ld_agent(q) : *q;
-        };
-        const uint64_t mk0 = sealed0 ? meta(A.kmeta, s0) : 0ull, mv0 = sealed0 ? meta(A.vmeta, s0) : 0ull;
-        const uint64_t mk1 = sealed1 ? meta(A.kmeta, s1) : mk0, mv1 = sealed1 ? meta(A.vmeta, s1) : mv0;
-        // every row of the batch sealed (the common case, decided for the
-        // whole wave): no branch between a row's load and its registers, so
-        // that all of the batch's loads stay in flight together
-        if (last < open0 && p0 < open0) {
-#pragma unroll
-            for (int u = 0; u < Geo::U; ++u) {
-                const int p = batch_row<HD>(pb, u, slot);
-                const int pc = p < p1 ? p : p0;
-                const size_t row = (size_t)g * A.ld + pc;
-                const u2v ck = ld8(reinterpret_cast<const uint8_t*>(A.kc) + row * HD + j * 8);
-                const u2v cv = ld8(reinterpret_cast<const uint8_t*>(A.vc) + row * HD + j * 8);
-                const bool hi = pc / SEG != s0;
-                const uint64_t mk = hi ? mk1 : mk0, mv = hi ? mv1 : mv0;
-                kr[u] = KvRaw{u4v{ck.x, ck.y, 0u, 0u}, __uint_as_float((uint32_t)mk), __uint_as_float((uint32_t)(mk >> 32))};
-                vr[u] = KvRaw{u4v{cv.x, cv.y, 0u, 0u}, __uint_as_float((uint32_t)mv), __uint_as_float((uint32_t)(mv >> 32))};
-            }
-            return;
-        }
-#pragma unroll
-        for (int u = 0; u < Geo::U; ++u) {
-            const int p = batch_row<HD>(pb, u, slot);
-            const int pc = p < p1 ? p : p0;
-            const size_t row = (size_t)g * A.ld + pc;
-            if (pc < open0) {
-                const u2v ck = ld8(reinterpret_cast<const uint8_t*>(A.kc) + row * HD + j * 8);
-                const u2v cv = ld8(reinterpret_cast<const uint8_t*>(A.vc) + row * HD + j * 8);
-                const bool hi = pc / SEG != s0;
-                const uint64_t mk = hi ? mk1 : mk0, mv = hi ? mv1 : mv0;
-                kr[u] = KvRaw{u4v{ck.x, ck.y, 0u, 0u}, __uint_as_float((uint32_t)mk), __uint_as_float((uint32_t)(mk >> 32))};
-                vr[u] = KvRaw{u4v{cv.x, cv.y, 0u, 0u}, __uint_as_float((uint32_t)mv), __uint_as_float((uint32_t)(mv >> 32))};
-            } else {
-                kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
-                vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
-            }
-        }
-    } else {
-        if constexpr (P) {
-            if (pos == 0) {   // the only row is the new one (wave-uniform)
-#pragma unroll
-                for (int u = 0; u < Geo::U; ++u) kr[u] = vr[u] = KvRaw{u4v{0u, 0u, 0u, 0u}, -1.f, 0.f};
-                return;
-            }
-        }
-        const int alt = P && p0 == pos ? pos - 1 : p0;
-#pragma unroll
-        for (int u = 0; u < Geo::U; ++u) {
-            const int p = batch_row<HD>(pb, u, slot);
-            const int pc = p < p1 && !(P && p == pos) ? p : alt;
-            kr[u] = kv_raw<HD, KVF, P>(A, 0, g, pc, open0, j);
-            vr[u] = kv_raw<HD, KVF, P>(A, 1, g, pc, open0, j);
-        }
-    }
-}
-template <int HD, int KVF>
-__device__ __forceinline__ void kv_batch_cvt(int pb, int p1, const KvRaw (&kr)[AttnGeo<HD>::U],
-                                             const KvRaw (&vr)[AttnGeo<HD>::U], float (&kf)[AttnGeo<HD>::U][8],
-                                             float (&vf)[AttnGeo<HD>::U][8], bool (&valid)[AttnGeo<HD>::U]) {
-    const int slot = lane_id() / AttnGeo<HD>::LPR;
-#pragma unroll
-    for (int u = 0; u < AttnGeo<HD>::U; ++u) {
-        valid[u] = batch_row<HD>(pb, u, slot) < p1;
-        kv_cvt<KVF>(kr[u], kf[u]);
-        kv_cvt<KVF>(vr[u], vf[u]);
-    }
-}
+    // rows per lane per batch: 16 bytes per lane and row for fp16 rows, 8 for
+    // the 8-bit codes, whose batches hold twice the rows (the same bytes)
+    static constexpr int U = (SRC == SRC_E5M2 || SRC == SRC_I8) ? 8 : 4;
+    static constexpr int BATCH = Geo::RPW * U;
+    static constexpr bool WIDE = SRC == SRC_F16 || SRC == SRC_STAGE;
+    static constexpr int RW = WIDE ? 4 : 2;   // words per row
+    static constexpr int LOADS = 2 * U + (SRC == SRC_I8 ? 4 : 0);
+    static constexpr int ES = WIDE ? 2 : 1;   // bytes per element
+    static constexpr int AUX = SRC == SRC_F16    ? AUX_NT
+                               : SRC == SRC_E5M2 ? ((P && HD == 64) ? AUX_AGENT : AUX_NT)
+                               : SRC == SRC_I8   ? AUX_NT
+                                                 : (P ? AUX_AGENT : AUX_PLAIN);
+    static constexpr int AUX_META = P ? AUX_AGENT : AUX_PLAIN;
+    static constexpr int KVF = SRC == SRC_I8 || SRC == SRC_STAGE ? KV_INT8 : SRC;
+    using Buf = KvBuf<KVF>;
+    static_assert(2 * U * RW + (SRC == SRC_I8 ? 8 : 0) <= (int)(sizeof(Buf) / 4), "KvBuf");
 
+    __amdgpu_buffer_rsrc_t rk, rv, rmk, rmv;
+    int g, ld, nseg, pos;
+
+    __device__ __forceinline__ KvSrc(const AttnArgs& A, int g_, int pos_) : g(g_), pos(pos_) {
+        nseg = A.nseg;
+        if constexpr (SRC == SRC_STAGE) {
+            ld = SEG;
+            rk = attn_rsrc(A.kst, (size_t)A.Hk * SEG * HD * 2);
+            rv = attn_rsrc(A.vst, (size_t)A.Hk * SEG * HD * 2);
+        } else {
+            ld = A.ld;
+            rk = attn_rsrc(A.kc, (size_t)A.Hk * A.ld * HD * ES);
+            rv = attn_rsrc(A.vc, (size_t)A.Hk * A.ld * HD * ES);
+        }
+        if constexpr (SRC == SRC_I8) {
+            rmk = attn_rsrc(A.kmeta, (size_t)A.Hk * A.nseg * 8);
+            rmv = attn_rsrc(A.vmeta, (size_t)A.Hk * A.nseg * 8);
+        }
+    }
+    __device__ __forceinline__ uint32_t row_off(int p, int j) const {
+        const int r = SRC == SRC_STAGE ? p % SEG : p;
+        return ((uint32_t)(g * ld + r) * HD + j * 8) * ES;
+    }
+    // The raw rows of the batch starting at pb (pb <= p1; pb == p1: a batch
+    // past the split's end, nothing fetched).
+    __device__ __forceinline__ void load(int pb, int p1, Buf& b) const {
+        const int lane = lane_id(), slot = lane / Geo::LPR, j = lane % Geo::LPR;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = pb + u * Geo::RPW + slot;
+            const bool fetch = p < p1 && !(P && p == pos);
+            const uint32_t off = fetch ? row_off(p, j) : ROW_NONE;
+            if constexpr (WIDE) {
+                const u4v k = __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, AUX);
+                const u4v v = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, AUX);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    b.w[(2 * u) * 4 + i] = k[i];
+                    b.w[(2 * u + 1) * 4 + i] = v[i];
+                }
+            } else {
+                const u2v k = __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, AUX);
+                const u2v v = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, AUX);
+                b.w[(2 * u) * 2] = k.x;
+                b.w[(2 * u) * 2 + 1] = k.y;
+                b.w[(2 * u + 1) * 2] = v.x;
+                b.w[(2 * u + 1) * 2 + 1] = v.y;
+            }
+        }
+        if constexpr (SRC == SRC_I8) {
+            // the (scale, zp) pairs of the at most two segments the batch's
+            // rows fall in, one 8-byte load each for K and V (the same
+            // address in every lane)
+            const bool any = pb < p1;
+            const int s0 = pb / SEG, s1 = (min(pb + BATCH, p1) - 1) / SEG;
+            const uint32_t m0 = any ? (uint32_t)(g * nseg + s0) * 8 : ROW_NONE;
+            const uint32_t m1 = any ? (uint32_t)(g * nseg + s1) * 8 : ROW_NONE;
+            const u2v mk0 = __builtin_amdgcn_raw_buffer_load_b64(rmk, m0, 0, AUX_META);
+            const u2v mv0 = __builtin_amdgcn_raw_buffer_load_b64(rmv, m0, 0, AUX_META);
+            const u2v mk1 = __builtin_amdgcn_raw_buffer_load_b64(rmk, m1, 0, AUX_META);
+            const u2v mv1 = __builtin_amdgcn_raw_buffer_load_b64(rmv, m1, 0, AUX_META);
+            b.w[32] = mk0.x; b.w[33] = mk0.y; b.w[34] = mv0.x; b.w[35] = mv0.y;
+            b.w[36] = mk1.x; b.w[37] = mk1.y; b.w[38] = mv1.x; b.w[39] = mv1.y;
+        }
+    }
+    // Row u of the batch at pb as floats: which = 0 K, 1 V.
+    __device__ __forceinline__ void cvt(const Buf& b, int pb, int u, int which, float (&f)[8]) const {
+        const int base = (2 * u + which) * RW;
+        if constexpr (WIDE) {
+            const h8 v = as_h8(u4v{b.w[base], b.w[base + 1], b.w[base + 2], b.w[base + 3]});
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f[i] = (float)v[i];
+        } else if constexpr (SRC == SRC_E5M2) {
+            // an E5M2 byte is the high byte of the binary16 it encodes: two
+            // bytes become a pair of halves in one byte permute
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const uint32_t x = b.w[base + d];
+                const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0u, x, 0x010c000cu));
+                const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0u, x, 0x030c020cu));
+                f[4 * d] = (float)lo[0];
+                f[4 * d + 1] = (float)lo[1];
+                f[4 * d + 2] = (float)hi[0];
+                f[4 * d + 3] = (float)hi[1];
+            }
+        } else {
+            // INT8: (code - zp) * scale with the pair of the row's segment
+            const int p = pb + u * Geo::RPW + lane_id() / Geo::LPR;
+            const bool second = p / SEG != pb / SEG;
+            const int mo = 32 + 2 * which + (second ? 4 : 0);
+            const float scale = __uint_as_float(b.w[mo]), zp = __uint_as_float(b.w[mo + 1]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                f[i] = ((float)((b.w[base + (i >> 2)] >> ((i & 3) * 8)) & 0xffu) - zp) * scale;
+        }
+    }
+};
 // Scores are kept in log2 units: the query is pre-multiplied by
 // scale * log2(e), so every exponential is one hardware exp2 (v_exp_f32).
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A row replaced after conversion (the persistent kernel's row of the current
+// step, whose K and V come from the exchange): active(pb, n) says whether
+// rows [pb, pb + n) can hold it (the same in every lane), apply(p, which, f)
+// replaces row p's converted K (which = 0) or V.
+struct NoFix {
+    __device__ __forceinline__ bool active(int, int) const { return false; }
+    __device__ __forceinline__ void apply(int, int, float (&)[8]) const {}
+};
 
 template <int HD, int G>
 struct AttnAcc {
@@ -444,43 +466,67 @@ struct AttnAcc {
             for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
         }
     }
-    // Scores of the batch's rows against the pre-scaled queries; then per
-    // slot one online-softmax update for the whole batch: the new maximum,
-    // one rescale of the running sum and output, and the batch's rows added
-    // in order.
-    __device__ __forceinline__ void batch(const float (&qv)[G][8], const float (&kf)[AttnGeo<HD>::U][8],
-                                          const float (&vf)[AttnGeo<HD>::U][8], const bool (&valid)[AttnGeo<HD>::U]) {
-        constexpr int U = AttnGeo<HD>::U;
+    // One batch of U rows per lane: their scores against the pre-scaled
+    // queries; then per slot one online-softmax update for the whole batch:
+    // the new maximum, one rescale of the running sum and output, and the
+    // batch's rows added in order.  A row's K is converted for its scores and
+    // its V for the output, each once for all G heads; fix may replace a
+    // converted row.  A slot that has seen no key yet (maximum -inf) keeps
+    // its state.
+    // Every product-sum is an explicit fma and nothing else is contracted:
+    // the executors place this code in different blocks (the persistent
+    // kernel's row fix branches inside it), and contraction decided per
+    // block would round differently in each.
+    template <class Src, class Buf, class Fix>
+    __device__ __forceinline__ void batch(const float (&qv)[G][8], const Src& src, const Buf& b, int pb, int p1,
+                                          const Fix& fix) {
+#pragma clang fp contract(off)
+        constexpr int U = Src::U;
+        const int slot = lane_id() / AttnGeo<HD>::LPR;
+        const bool fx = fix.active(pb, Src::BATCH);
         float sc[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int p = pb + u * AttnGeo<HD>::RPW + slot;
+            float kf[8];
+            src.cvt(b, pb, u, 0, kf);
+            if (fx) fix.apply(p, 0, kf);
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float d = 0.f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) d += qv[h][i] * kf[u][i];
+                for (int i = 0; i < 8; ++i) d = __builtin_fmaf(qv[h][i], kf[i], d);
                 d = group_sum<AttnGeo<HD>::LPR>(d);
-                sc[u][h] = valid[u] ? d : -INFINITY;
+                sc[u][h] = p < p1 ? d : -INFINITY;
             }
         }
+        float e[U][G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mb = m[h];
 #pragma unroll
             for (int u = 0; u < U; ++u) mb = fmaxf(mb, sc[u][h]);
-            if (mb == -INFINITY) continue;   // this slot has seen no key yet
-            const float c = exp2_fast(m[h] - mb);
+            const bool none = mb == -INFINITY;
+            const float c = none ? 1.f : exp2_fast(m[h] - mb);
             l[h] *= c;
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[h][i] *= c;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float e = exp2_fast(sc[u][h] - mb);
-                l[h] += e;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) o[h][i] += e * vf[u][i];
-            }
+            for (int u = 0; u < U; ++u) e[u][h] = none ? 0.f : exp2_fast(sc[u][h] - mb);
             m[h] = mb;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = pb + u * AttnGeo<HD>::RPW + slot;
+            float vf[8];
+            src.cvt(b, pb, u, 1, vf);
+            if (fx) fix.apply(p, 1, vf);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                l[h] += e[u][h];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[h][i] = __builtin_fmaf(e[u][h], vf[i], o[h][i]);
+            }
         }
     }
     // Combine the RPW slots: M = max of the slot maxima, each slot weighted
@@ -522,39 +568,68 @@ constexpr int ATT_WAVES = 3;
 // Wave w takes the batches p0 + (w + NW*i)*BATCH of the split [p0, p1), with
 // the raw rows of the next two of its batches in flight while one is reduced
 // (three buffers).  The caller loads buffer 0 (attn_wave_first) before
-// attn_wave_run; fix(pb, kf, vf) may replace converted rows (the row being
-// written this step, taken from the exchange instead of the cache).
-template <int HD>
-using KvBuf = KvRaw[3][AttnGeo<HD>::U];
-
-template <int HD, int KVF, bool P, int NW>
-__device__ __forceinline__ void attn_wave_first(const AttnArgs& T, int g, int p0, int p1, int open0, int pos, int w,
-                                                KvBuf<HD>& kb, KvBuf<HD>& vb) {
-    const int pb = p0 + w * AttnGeo<HD>::BATCH;
-    if (pb < p1) kv_batch_raw<HD, KVF, P>(T, g, pb, p0, p1, open0, pos, kb[0], vb[0]);
+// attn_wave_run.  With three or more batches, every slot of a three-batch
+// group loads, also past the wave's last batch (nothing is fetched there),
+// and the loop exits only at the end of a group: an exit inside the group
+// would give the loop header a path on which a group's loads are still
+// pending, and the compiler would then wait for all of them there.
+template <class Src, int NW>
+__device__ __forceinline__ void attn_wave_first(const Src& src, int p0, int p1, int w, typename Src::Buf (&kb)[3]) {
+    src.load(min(p0 + w * Src::BATCH, p1), p1, kb[0]);
 }
-template <int HD, int G, int KVF, bool P, int NW, class Fix>
-__device__ __forceinline__ void attn_wave_run(const AttnArgs& T, int g, int p0, int p1, int open0, int pos, int w,
-                                              const float (&qv)[G][8], AttnAcc<HD, G>& acc, KvBuf<HD>& kb,
-                                              KvBuf<HD>& vb, Fix fix) {
-    using Geo = AttnGeo<HD>;
-    constexpr int STEP = NW * Geo::BATCH;
-    const int pf = p0 + w * Geo::BATCH;
+template <class Src, int NW, int HD, int G, class Fix>
+__device__ __forceinline__ void attn_wave_run(const Src& src, int p0, int p1, int w, const float (&qv)[G][8],
+                                              AttnAcc<HD, G>& acc, typename Src::Buf (&kb)[3], const Fix& fix) {
+    constexpr int STEP = NW * Src::BATCH;
+    const int pf = p0 + w * Src::BATCH;
     if (pf >= p1) return;
-    if (pf + STEP < p1) kv_batch_raw<HD, KVF, P>(T, g, pf + STEP, p0, p1, open0, pos, kb[1], vb[1]);
-    for (int i = 0;; i += 3) {
+    // one or two batches (short contexts): straight-line, nothing loaded past
+    // the wave's last batch
+    if (pf + 2 * STEP >= p1) {
+        if (pf + STEP >= p1) {
+            wait_vm<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            acc.batch(qv, src, kb[0], pf, p1, fix);
+        } else {
+            src.load(pf + STEP, p1, kb[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<Src::LOADS>();
+            __builtin_amdgcn_sched_barrier(0);
+            acc.batch(qv, src, kb[0], pf, p1, fix);
+            wait_vm<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            acc.batch(qv, src, kb[1], pf + STEP, p1, fix);
+        }
+        return;
+    }
+    src.load(pf + STEP, p1, kb[1]);
+    for (int pg = pf; pg < p1; pg += 3 * STEP) {
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-            const int pb = pf + (i + r) * STEP;
-            if (pb >= p1) return;
-            const int pn = pb + 2 * STEP;
-            if (pn < p1) kv_batch_raw<HD, KVF, P>(T, g, pn, p0, p1, open0, pos, kb[(r + 2) % 3], vb[(r + 2) % 3]);
-            float kf[Geo::U][8], vf[Geo::U][8];
-            bool valid[Geo::U];
-            kv_batch_cvt<HD, KVF>(pb, p1, kb[r], vb[r], kf, vf, valid);
-            fix(pb, kf, vf);
-            acc.batch(qv, kf, vf, valid);
+            const int pb = pg + r * STEP;
+            src.load(min(pb + 2 * STEP, p1), p1, kb[(r + 2) % 3]);
+            // all of them issued before the wait for batch pb's rows: the
+            // two batches loaded after it may stay in flight (the wait also
+            // settles a skipped slot's buffer, so that no path reaches the
+            // loop header with it pending)
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vm<2 * Src::LOADS>();
+            __builtin_amdgcn_sched_barrier(0);
+            if (pb < p1) acc.batch(qv, src, kb[r], pb, p1, fix);
         }
+    }
+}
+// Calls f with the row source of a split: the cache format's rows, or for
+// INT8 the sealed codes or (open: the open-segment split) the fp16 staging.
+template <int HD, int KVF, bool P, class F>
+__device__ __forceinline__ void with_src(const AttnArgs& T, int g, int pos, bool open, F f) {
+    if constexpr (KVF == KV_INT8) {
+        if (open)
+            f(KvSrc<HD, SRC_STAGE, P>(T, g, pos));
+        else
+            f(KvSrc<HD, SRC_I8, P>(T, g, pos));
+    } else {
+        f(KvSrc<HD, KVF == KV_FP16 ? SRC_F16 : SRC_E5M2, P>(T, g, pos));
     }
 }
 // The NW wave partials of a split, combined in wave order with the same

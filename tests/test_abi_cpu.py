@@ -82,6 +82,12 @@ def test_option_validation_on_host(rd):
     assert _create(rd, blob, kv_format=7)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, executor=9)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, attn_splits=1000)[0] == rd.RD_ERR_INVALID_ARG
+    # INT8: the open segment is a split of its own, so one split is too few
+    assert _create(rd, blob, kv_format=2, attn_splits=1)[0] == rd.RD_ERR_INVALID_ARG
+    # 4 kv heads x 64 dims x 2 bytes: at 2^22 positions one layer's K is 2 GiB,
+    # past the attention's 32-bit row offsets
+    assert _create(rd, blob, max_context=1 << 22)[0] == rd.RD_ERR_INVALID_ARG
+    assert "2 GiB" in rd.last_error()
     o = rd.rd_options()
     rd.lib().rd_options_init(C.byref(o))
     o.struct_size = 3
@@ -97,6 +103,12 @@ def test_null_arguments(rd):
     assert L.rd_generate(None, None, 1, 1, None) == rd.RD_ERR_INVALID_ARG
     assert L.rd_gemv_f16(None, None, None, 1, 8, 1, None) == rd.RD_ERR_INVALID_ARG
     assert L.rd_attention_f16(None, None, None, None, 1, 1, 64, 1, 1, 1.0, 1, None) == rd.RD_ERR_INVALID_ARG
+    # argument checks before any device work (the addresses are never read):
+    # INT8 with one split, and a cache past 2 GiB
+    a = 256
+    assert L.rd_attention(a, a, a, a, a, a, a, a, 2, 1, 64, 1, 1, 2, 1.0, 1, None) == rd.RD_ERR_INVALID_ARG
+    assert L.rd_attention(a, a, a, a, a, a, a, a, 16, 8, 128, 1, 1 << 20, 0, 1.0, 8, None) == rd.RD_ERR_INVALID_ARG
+    assert "2 GiB" in rd.last_error()
     assert L.rd_seg_quant(None, 1, 8, None, None, None) == rd.RD_ERR_INVALID_ARG
     assert L.rd_argmax_f32(None, 1, None, None) == rd.RD_ERR_INVALID_ARG
     L.rd_model_destroy(None)   # NULL-safe
