@@ -145,7 +145,7 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
             d[(c, k)] = t * 0.01        # 100 MHz clock -> us
         per.append(d)
     seg = {k: [] for k in ("layer", "qkv", "att", "merge", "o", "gu", "down", "x_qkv", "x_att", "x_merge", "x_o",
-                           "x_gu", "x_down")}
+                           "x_gu", "x_down", "att.start", "att.loop", "att.tail")}
     # inside each GEMV phase (stream wave 0's events 100 + 10 * kind + point:
     # released, first rows reduced, all rows reduced; kinds 0 QKV, 1 O,
     # 2 gate/up, 3 down): staging of the input, release of the stream waves,
@@ -181,6 +181,11 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
             if g(10) is not None and g(13) is not None:
                 seg["x_att"].append(g(10) - g(3))
                 seg["att"].append(g(13) - g(10))
+                # stream wave 0: attention start (q staged), its batches reduced
+                if g(140) is not None and g(141) is not None:
+                    seg["att.start"].append(g(140) - g(10))
+                    seg["att.loop"].append(g(141) - g(140))
+                    seg["att.tail"].append(g(13) - g(141))
             if g(20) is not None and g(23) is not None:
                 seg["x_merge"].append(g(20) - (g(13) if g(13) is not None else g(3)))
                 seg["merge"].append(g(23) - g(20))

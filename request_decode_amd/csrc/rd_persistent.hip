@@ -604,9 +604,10 @@ struct FixNewRow {
 };
 template <int HD, int G, int KVF>
 __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A, const AttnSplit& sp, int w,
-                                            float* s_r, KvBuf<KVF> (&kb)[3]) {
+                                            float* s_r, KvBuf<KVF> (&kb)[3], StreamTracer& tr) {
     constexpr int NQ = attn_nq<HD, G>();
     lds_barrier();   // q and the new row staged
+    if (w == 0) tr(140);
     if (sp.t >= 0) {
         const int lane = lane_id();
         float qv[G][8], kn[8], vn[8];
@@ -625,6 +626,7 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
             using Src = decltype(src);
             attn_wave_run<Src, NWA>(src, sp.p0, sp.p1, w, qv, acc, kb, FixNewRow{sp.pos, kn, vn});
         });
+        if (w == 0) tr(141);
         acc.finish();
         attn_part_store<HD, G>(s_r + NQ * 64, w, acc);
     }
@@ -652,7 +654,7 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
                         attn_wave_first<decltype(src), NWA>(src, sp.p0, sp.p1, sw, kb);
                     });
             });
-            attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb);
+            attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, tr);
             stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none);
             stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none);
             stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none);

@@ -407,8 +407,15 @@ struct KvSrc {
             b.w[36] = mk1.x; b.w[37] = mk1.y; b.w[38] = mv1.x; b.w[39] = mv1.y;
         }
     }
-    // Row u of the batch at pb as floats: which = 0 K, 1 V.
-    __device__ __forceinline__ void cvt(const Buf& b, int pb, int u, int which, float (&f)[8]) const {
+    // Row u (position p) of the batch at pb as floats: which = 0 K, 1 V.
+    // INT8 codes give code - zp; the row's scale is then applied once
+    // (mul), to the row's score for K and to its softmax weight for V.
+    static constexpr bool SCALED = SRC == SRC_I8;
+    __device__ __forceinline__ float mul(const Buf& b, int pb, int p, int which) const {
+        const int mo = 32 + 2 * which + (p >= (pb / SEG + 1) * SEG ? 4 : 0);
+        return __uint_as_float(b.w[mo]);
+    }
+    __device__ __forceinline__ void cvt(const Buf& b, int pb, int u, int p, int which, float (&f)[8]) const {
         const int base = (2 * u + which) * RW;
         if constexpr (WIDE) {
             const h8 v = as_h8(u4v{b.w[base], b.w[base + 1], b.w[base + 2], b.w[base + 3]});
@@ -429,14 +436,12 @@ struct KvSrc {
                 f[4 * d + 3] = (float)hi[1];
             }
         } else {
-            // INT8: (code - zp) * scale with the pair of the row's segment
-            const int p = pb + u * Geo::RPW + lane_id() / Geo::LPR;
-            const bool second = p / SEG != pb / SEG;
-            const int mo = 32 + 2 * which + (second ? 4 : 0);
-            const float scale = __uint_as_float(b.w[mo]), zp = __uint_as_float(b.w[mo + 1]);
+            // INT8: code - zp with the zero point of the row's segment (the
+            // batch's rows fall in the segment of pb or the next one)
+            const int mo = 32 + 2 * which + (p >= (pb / SEG + 1) * SEG ? 4 : 0);
+            const float zp = __uint_as_float(b.w[mo + 1]);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                f[i] = ((float)((b.w[base + (i >> 2)] >> ((i & 3) * 8)) & 0xffu) - zp) * scale;
+            for (int i = 0; i < 8; ++i) f[i] = (float)((b.w[base + (i >> 2)] >> ((i & 3) * 8)) & 0xffu) - zp;
         }
     }
 };
@@ -489,14 +494,16 @@ struct AttnAcc {
         for (int u = 0; u < U; ++u) {
             const int p = pb + u * AttnGeo<HD>::RPW + slot;
             float kf[8];
-            src.cvt(b, pb, u, 0, kf);
+            src.cvt(b, pb, u, p, 0, kf);
             if (fx) fix.apply(p, 0, kf);
+            const float km = Src::SCALED ? src.mul(b, pb, p, 0) : 1.f;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float d = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) d = __builtin_fmaf(qv[h][i], kf[i], d);
                 d = group_sum<AttnGeo<HD>::LPR>(d);
+                if constexpr (Src::SCALED) d *= km;
                 sc[u][h] = p < p1 ? d : -INFINITY;
             }
         }
@@ -519,13 +526,15 @@ struct AttnAcc {
         for (int u = 0; u < U; ++u) {
             const int p = pb + u * AttnGeo<HD>::RPW + slot;
             float vf[8];
-            src.cvt(b, pb, u, 1, vf);
+            src.cvt(b, pb, u, p, 1, vf);
             if (fx) fix.apply(p, 1, vf);
+            const float vm = Src::SCALED ? src.mul(b, pb, p, 1) : 1.f;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 l[h] += e[u][h];
+                const float ew = Src::SCALED ? e[u][h] * vm : e[u][h];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) o[h][i] = __builtin_fmaf(e[u][h], vf[i], o[h][i]);
+                for (int i = 0; i < 8; ++i) o[h][i] = __builtin_fmaf(ew, vf[i], o[h][i]);
             }
         }
     }
