@@ -287,6 +287,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=None, help="default: --steps (one equal-size warmup launch)")
     ap.add_argument("--kv", default="fp16", choices=["fp16", "e5m2", "int8"])
     ap.add_argument("--batch", type=int, default=1, help="sequences in lockstep (1..8; > 1: graph executor)")
+    ap.add_argument("--kv-pages", type=int, default=0,
+                    help="batch > 1: a paged KV cache of this many page groups (-1: just enough for the run)")
     ap.add_argument("--prompt", type=int, default=512,
                     help="prompt length (512: the 2B decode workload; 32768: long context; 8192: quantized KV)")
     ap.add_argument("--executor", default="auto", choices=["auto", "graph", "eager", "persistent"])
@@ -331,11 +333,15 @@ def main():
     prompt = synth.prompt(pseed, PROMPT, shape.vocab) if B == 1 else synth.prompts(pseed, PROMPT, shape.vocab, B)
     # INT8 KV can only be rewound to a segment start: there the timed steps
     # follow the warmup steps instead of repeating their positions
-    rewind = args.kv != "int8"
+    rewind = args.kv != "int8" and not args.kv_pages
     # +1: the phase run; an INT8 cache is traced on further positions
     ctx = PROMPT + (max(args.steps, args.warmup) if rewind else args.steps + args.warmup + max(2, args.trace)) + 1
+    kv_pages = args.kv_pages
+    if kv_pages < 0:   # every sequence's rows of the run, 4 KiB pages of one (layer, K/V, kv head)
+        page_rows = 4096 // (shape.head_dim * (2 if args.kv == "fp16" else 1))
+        kv_pages = B * -(-ctx // page_rows)
     m = rd.Model(blob, max_context=ctx, kv_format=args.kv, executor=args.executor, stream=stream.cuda_stream,
-                 batch=B, attn_splits=args.attn_splits)
+                 batch=B, attn_splits=args.attn_splits, kv_pages=kv_pages)
     executor = m.get_info().executor
     persistent = executor == rd.RD_EXEC_PERSISTENT
     batched = args.prefill == "batched" and B == 1
@@ -430,7 +436,7 @@ def main():
     workload = ("2b-dense-decode" if PROMPT == 512 and args.kv == "fp16" and B == 1 else
                 "2b-long-context-decode" if PROMPT >= 16384 else f"2b-{args.kv}-kv-decode")
     if B > 1:
-        workload += f"-batch{B}"
+        workload += f"-batch{B}" + ("-paged" if kv_pages else "")
     res = {
         "metric": ("batch-1 decode tokens/s + achieved HBM GB/s (MBU %) on 2B-class fp16 model" if B == 1 else
                    f"batch-{B} decode tokens/s (all sequences) + achieved HBM GB/s on 2B-class fp16 model"),
@@ -439,7 +445,7 @@ def main():
         "vs_baseline": None, "dtype": "fp16",
         "data": "synthetic: seeded N(0,0.02) fp16 weights, uniform random prompt ids",
         "config": {"workload": workload, "layers": 24, "d_model": 2048, "heads": 16, "kv_heads": 8,
-                   "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": B,
+                   "head_dim": 128, "d_ff": 5632, "vocab": 32000, "prompt": PROMPT, "batch": B, "kv_pages": kv_pages,
                    "kv_cache": args.kv, "executor": ["auto", "eager", "graph", "persistent"][executor],
                    "positions": [base, base + args.steps - 1]},
         "hbm_gbps": round(gbps, 1), "mbu": round(gbps / HBM_PEAK_GBPS, 4),

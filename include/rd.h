@@ -100,6 +100,16 @@ typedef struct {
                              attn_splits - 1).  The persistent kernels merge at most 32
                              (2B-class shape) or 64 (test shapes) splits: with more, AUTO takes
                              GRAPH and PERSISTENT is UNSUPPORTED. */
+    int32_t kv_pages;     /* 0: a contiguous cache of max_context rows per sequence.  > 0: a paged
+                             cache ("LLM inference architecture rebuild", §3.2: 4 KB pages, a page
+                             table per sequence, refcounts, prefix sharing) of this many page
+                             groups shared by all sequences.  A page is 4 KiB of one (layer, K/V,
+                             kv head): page_rows = 4096 / (head_dim * element bytes) positions; a
+                             page group is one page id across all layers, K/V and kv heads.
+                             Sequences then sit at their own positions (ragged lengths): a token of
+                             -1 in rd_decode_step / rd_prefill sits that sequence out of the step.
+                             Needs max_batch 2..8, FP16 or FP8_E5M2, the EAGER or GRAPH executor,
+                             and max_context <= 4094 * page_rows. */
 } rd_options;
 
 typedef struct {
@@ -110,6 +120,8 @@ typedef struct {
     uint64_t streamed_bytes;    /* weight bytes one step must read (all but the embedding table,
                                    plus one embedding row per sequence) */
     uint64_t kv_bytes;          /* device bytes of the KV cache (all formats' parts) */
+    int32_t kv_pages;           /* page groups of a paged cache (0: contiguous) */
+    int32_t page_rows;          /* positions per page (0: contiguous) */
 } rd_model_info;
 
 /* Initialise an options struct with defaults (device 0, NULL stream,
@@ -142,10 +154,12 @@ void rd_model_destroy(rd_model* m);
 
 rd_status rd_model_get_info(const rd_model* m, rd_model_info* out);
 
-/* Position := 0 for every sequence (cache contents become unreachable). */
+/* Position := 0 for every sequence (cache contents become unreachable; a
+ * paged cache releases every page). */
 rd_status rd_reset(rd_model* m);
 
-/* Position of the next token to be decoded (the same for every sequence). */
+/* Position of the next token to be decoded (the same for every sequence;
+ * a paged cache: sequence 0's, see rd_seq_position). */
 rd_status rd_get_position(const rd_model* m, int32_t* pos);
 
 /* One decode step: the per-token forward of "How the xAI engineering team
@@ -155,8 +169,12 @@ rd_status rd_get_position(const rd_model* m, int32_t* pos);
  * on standard GPUs", loss table).  tokens: host [batch] ids at the current position.
  * logits: host [batch*vocab] fp32 or NULL.  next: host [batch] greedy argmax
  * (lowest index on ties) or NULL.  batch must equal max_batch.
- * Errors: INVALID_ARG, CONTEXT_FULL (nothing changed), NUMERIC (a non-finite
- * logit or an out-of-range token was seen; the step still advanced), DEVICE. */
+ * Paged cache: each sequence decodes at its own position; a token of -1 sits
+ * the sequence out (its position and rows unchanged, its next is -1 and its
+ * logits meaningless).
+ * Errors: INVALID_ARG, CONTEXT_FULL (nothing changed), OUT_OF_MEMORY (paged:
+ * the pool is exhausted; nothing changed), NUMERIC (a non-finite logit or an
+ * out-of-range token was seen; the step still advanced), DEVICE. */
 rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t batch, float* logits, int32_t* next);
 
 /* Teacher-forced steps: tokens (host [n*batch], step-major) are fed at
@@ -207,6 +225,8 @@ rd_status rd_synchronize(rd_model* m);
  * memory dst (capacity cap bytes), in the formats of "How the xAI engineering
  * team cut Grok Bot latency to milliseconds", §2.3 (E5M2) and "Grok-3 v3.2.4
  * hot update deep dive", §3.2 (INT8 per 128-token segment).  Layout per format:
+ * A paged cache exports sequence seq's rows gathered through its page table
+ * in the FP16 / E5M2 layout below (rows of pages it does not hold: zeros).
  *  FP16:  u16 [n_kv_heads][max_context][head_dim]
  *  E5M2:  u8  [n_kv_heads][max_context][head_dim]
  *  INT8:  u8 codes [n_kv_heads][max_context][head_dim], then
@@ -215,6 +235,30 @@ rd_status rd_synchronize(rd_model* m);
  * *written receives the byte count.  Synchronises the stream. */
 rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer, int32_t which, void* dst, size_t cap,
                              size_t* written);
+
+/* Paged cache (rd_options.kv_pages > 0).  The host keeps each sequence's page
+ * table, a refcount per page group and a free list.  Before each step (or run
+ * of steps: rd_prefill, rd_generate) every participating sequence gets the
+ * pages its new rows need: a missing page from the free list, and a shared
+ * page (refcount > 1) that a row is about to be written into is copied first
+ * (copy on write).  All or nothing: OUT_OF_MEMORY, with no state changed, when
+ * the pool cannot cover the request.  Rows are read through the page table;
+ * the results equal the contiguous cache's bit for bit.  The calls below
+ * synchronise the model's stream first.  Contiguous models: UNSUPPORTED. */
+
+/* Sequence seq (< max_batch) back to position 0, its pages released. */
+rd_status rd_seq_reset(rd_model* m, int32_t seq);
+
+/* Prefix sharing: sequence dst (!= src) takes src's pages of positions
+ * 0..pos(src)-1 (refcounts + 1) and src's position; its own pages are
+ * released first.  The two then diverge by copy on write. */
+rd_status rd_seq_fork(rd_model* m, int32_t src, int32_t dst);
+
+/* Position (rows held) of sequence seq. */
+rd_status rd_seq_position(const rd_model* m, int32_t seq, int32_t* pos);
+
+/* Page groups free, in use (refcount > 0) and shared (refcount > 1). */
+rd_status rd_kv_page_stats(const rd_model* m, int32_t* free_pages, int32_t* used_pages, int32_t* shared_pages);
 
 /* Overwrite the raw KV storage of (seq, layer, which) from host memory, same
  * layout as rd_debug_export_kv, and set the position of every sequence to

@@ -36,7 +36,7 @@ SEG = 128
 class rd_options(C.Structure):
     _fields_ = [("struct_size", C.c_uint32), ("device", C.c_int32), ("stream", C.c_void_p),
                 ("max_context", C.c_int32), ("max_batch", C.c_int32), ("kv_format", C.c_int32),
-                ("executor", C.c_int32), ("attn_splits", C.c_int32)]
+                ("executor", C.c_int32), ("attn_splits", C.c_int32), ("kv_pages", C.c_int32)]
 
 
 class rd_model_info(C.Structure):
@@ -45,7 +45,7 @@ class rd_model_info(C.Structure):
                 ("rope_base", C.c_float), ("norm_eps", C.c_float), ("max_context", C.c_int32),
                 ("max_batch", C.c_int32), ("kv_format", C.c_int32), ("executor", C.c_int32),
                 ("attn_splits", C.c_int32), ("weight_bytes", C.c_uint64), ("streamed_bytes", C.c_uint64),
-                ("kv_bytes", C.c_uint64)]
+                ("kv_bytes", C.c_uint64), ("kv_pages", C.c_int32), ("page_rows", C.c_int32)]
 
 
 class RdError(RuntimeError):
@@ -63,6 +63,10 @@ SIGNATURES = [
     ("rd_model_get_info", _I32, [_VP, C.POINTER(rd_model_info)]),
     ("rd_reset", _I32, [_VP]),
     ("rd_get_position", _I32, [_VP, _I32P]),
+    ("rd_seq_reset", _I32, [_VP, _I32]),
+    ("rd_seq_fork", _I32, [_VP, _I32, _I32]),
+    ("rd_seq_position", _I32, [_VP, _I32, _I32P]),
+    ("rd_kv_page_stats", _I32, [_VP, _I32P, _I32P, _I32P]),
     ("rd_decode_step", _I32, [_VP, _I32P, _I32, _FP, _I32P]),
     ("rd_generate", _I32, [_VP, _I32P, _I32, _I32, _I32P]),
     ("rd_generate_async", _I32, [_VP, _I32P, _I32, _I32, _VP]),
@@ -131,7 +135,8 @@ class Model:
     """A decode-step model on one GPU (rd_model_create and friends)."""
 
     def __init__(self, blob: np.ndarray, max_context: int = 4096, kv_format: str = "fp16",
-                 executor: str = "auto", device: int = 0, stream: int = 0, attn_splits: int = 0, batch: int = 1):
+                 executor: str = "auto", device: int = 0, stream: int = 0, attn_splits: int = 0, batch: int = 1,
+                 kv_pages: int = 0):
         L = lib()
         o = rd_options()
         L.rd_options_init(C.byref(o))
@@ -142,6 +147,7 @@ class Model:
         o.kv_format = KV_FORMATS[kv_format]
         o.executor = EXECUTORS[executor]
         o.attn_splits = attn_splits
+        o.kv_pages = kv_pages
         blob = np.ascontiguousarray(blob, dtype=np.uint8)
         h = _VP()
         self._destroy = L.rd_model_destroy
@@ -175,6 +181,24 @@ class Model:
 
     def set_position(self, pos: int):
         check(lib().rd_set_position(self._h, pos))
+
+    # paged cache: per-sequence positions and prefix sharing
+    def seq_reset(self, seq: int):
+        check(lib().rd_seq_reset(self._h, seq))
+
+    def seq_fork(self, src: int, dst: int):
+        check(lib().rd_seq_fork(self._h, src, dst))
+
+    def seq_position(self, seq: int) -> int:
+        p = C.c_int32()
+        check(lib().rd_seq_position(self._h, seq, C.byref(p)))
+        return p.value
+
+    def page_stats(self):
+        """(free, used, shared) page groups of a paged cache."""
+        f, u, sh = C.c_int32(), C.c_int32(), C.c_int32()
+        check(lib().rd_kv_page_stats(self._h, C.byref(f), C.byref(u), C.byref(sh)))
+        return f.value, u.value, sh.value
 
     def set_executor(self, executor: str):
         check(lib().rd_set_executor(self._h, EXECUTORS[executor]))
@@ -260,7 +284,7 @@ class Model:
     def kv_region_bytes(self):
         i = self.info
         es = 2 if i.kv_format == RD_KV_FP16 else 1
-        main = i.n_kv_heads * i.max_context * i.head_dim * es
+        main = i.n_kv_heads * i.max_context * i.head_dim * es   # a paged cache exports this layout too
         if i.kv_format != RD_KV_INT8_SEG128:
             return main, 0, 0
         nseg = (i.max_context + SEG - 1) // SEG

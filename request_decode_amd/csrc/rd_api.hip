@@ -149,6 +149,15 @@ struct rd_model {
     void* pf_buf = nullptr;
     PrefillWs pf{};
 
+    // paged KV cache (opt.kv_pages > 0): host page tables, refcounts, free list
+    bool paged = false;
+    int npages = 0, prow = 0, pshift = 0, pt_ld = 0;
+    int* ptab_dev = nullptr;        // [max_batch][pt_ld] device copy of ptab
+    std::vector<int> ptab;          // [max_batch][pt_ld] page group per page of positions, -1: none
+    std::vector<int> refc;          // [npages] sequences holding the group
+    std::vector<int> freel;         // free groups (taken from the back)
+    std::vector<int> hpos;          // [max_batch] positions (rows held)
+
     // persistent executor
     long long layer_stride = 0;     // bytes between consecutive layers' weight blocks
     int nwg = 0;                    // workgroups of the cooperative launch (0: not available)
@@ -177,9 +186,12 @@ struct Tokens8 {
 };
 // clear_err = 0 keeps the error bits of earlier steps, so that a run of
 // teacher-forced steps synchronised once reports an error of any of them.
-__global__ void k_set_state(StepState* st, int pos, Tokens8 tk, int nb, int reset_gen, int clear_err) {
+__global__ void k_set_state(StepState* st, int pos, Tokens8 tk, int nb, int reset_gen, int clear_err, Tokens8 bp,
+                            int set_bpos) {
     st->pos = pos;
     for (int b = 0; b < nb; ++b) st->token[b] = tk.t[b];
+    if (set_bpos)
+        for (int b = 0; b < nb; ++b) st->bpos[b] = bp.t[b];
     if (clear_err) st->err = 0;
     if (reset_gen) st->n_gen = 0;
 }
@@ -202,6 +214,7 @@ void free_model(rd_model* m) {
     (void)hipFree(m->meta);
     (void)hipFree(m->act);
     (void)hipFree(m->pf_buf);
+    (void)hipFree(m->ptab_dev);
     if (m->gen_host) (void)hipHostFree(m->gen_host);
     if (m->logits_host) (void)hipHostFree(m->logits_host);
     if (m->state_host) (void)hipHostFree(m->state_host);
@@ -255,16 +268,71 @@ rd_status step_enqueue(rd_model* m) {
 // Tokens of every sequence (host [max_batch], or NULL for zeros) and the
 // position into the device step state.
 hipError_t set_state(rd_model* m, const int32_t* tokens, bool clear_err = true) {
-    Tokens8 tk{};
-    for (int b = 0; b < m->opt.max_batch; ++b) tk.t[b] = tokens ? tokens[b] : 0;
+    Tokens8 tk{}, bp{};
+    for (int b = 0; b < m->opt.max_batch; ++b) {
+        tk.t[b] = tokens ? tokens[b] : 0;
+        bp.t[b] = m->paged ? m->hpos[b] : 0;
+    }
     hipLaunchKernelGGL(k_set_state, dim3(1), dim3(1), 0, m->stream, m->A.st, m->host_pos, tk, m->opt.max_batch, 1,
-                       clear_err ? 1 : 0);
+                       clear_err ? 1 : 0, bp, m->paged ? 1 : 0);
     return hipGetLastError();
 }
-bool tokens_ok(const rd_model* m, const int32_t* t, int n) {
+// Token ids in range; a paged cache also takes -1 (the sequence sits the step out).
+bool tokens_ok(const rd_model* m, const int32_t* t, int n, bool allow_idle = false) {
     for (int i = 0; i < n; ++i)
-        if (t[i] < 0 || t[i] >= m->d.V) return false;
+        if (!(t[i] >= 0 && t[i] < m->d.V) && !(allow_idle && m->paged && t[i] == -1)) return false;
     return true;
+}
+
+// ---- paged KV cache: page groups on the host ----------------------------------
+void page_release(rd_model* m, int b) {
+    for (int j = 0; j < m->pt_ld; ++j) {
+        int& e = m->ptab[(size_t)b * m->pt_ld + j];
+        if (e >= 0 && --m->refc[e] == 0) m->freel.push_back(e);
+        e = -1;
+    }
+    m->hpos[b] = 0;
+}
+// Pages for the next steps[b] positions of each sequence b (from hpos[b]):
+// a missing page from the free list, a shared page that a row is about to be
+// written into copied first (copy on write; only the page of hpos[b] can be
+// shared, since a fork shares pages up to the source's position).  All or
+// nothing: OUT_OF_MEMORY with no change when the pool cannot cover it.  Then
+// the device page table is brought up to date (enqueued on the stream).
+rd_status page_prepare(rd_model* m, const int* steps) {
+    const int B = m->opt.max_batch;
+    int need = 0;
+    for (int b = 0; b < B; ++b) {
+        if (steps[b] <= 0) continue;
+        const int j0 = m->hpos[b] >> m->pshift, j1 = (m->hpos[b] + steps[b] - 1) >> m->pshift;
+        for (int j = j0; j <= j1; ++j) {
+            const int e = m->ptab[(size_t)b * m->pt_ld + j];
+            need += e < 0 || m->refc[e] > 1;
+        }
+    }
+    if (need > (int)m->freel.size())
+        return fail(RD_ERR_OUT_OF_MEMORY, "KV page pool exhausted: " + std::to_string(need) + " page groups needed, " +
+                                              std::to_string(m->freel.size()) + " free");
+    if (!need) return RD_OK;
+    for (int b = 0; b < B; ++b) {
+        if (steps[b] <= 0) continue;
+        const int j0 = m->hpos[b] >> m->pshift, j1 = (m->hpos[b] + steps[b] - 1) >> m->pshift;
+        for (int j = j0; j <= j1; ++j) {
+            int& e = m->ptab[(size_t)b * m->pt_ld + j];
+            if (e >= 0 && m->refc[e] == 1) continue;
+            const int fresh = m->freel.back();
+            m->freel.pop_back();
+            m->refc[fresh] = 1;
+            if (e >= 0) {   // shared: this sequence's copy of the rows so far
+                HIP_TRY(launch_page_copy(m->A, e, fresh, m->stream));
+                --m->refc[e];
+            }
+            e = fresh;
+        }
+    }
+    // pageable source: the copy takes the table's current contents
+    HIP_TRY(hipMemcpyAsync(m->ptab_dev, m->ptab.data(), m->ptab.size() * 4, hipMemcpyHostToDevice, m->stream));
+    return RD_OK;
 }
 
 rd_status check_model(const rd_model* m) {
@@ -293,6 +361,14 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
         return fail(RD_ERR_INVALID_ARG, "bad kv_format");
     if (opt.executor < RD_EXEC_AUTO || opt.executor > RD_EXEC_PERSISTENT) return fail(RD_ERR_INVALID_ARG, "bad executor");
     if (opt.attn_splits < 0 || opt.attn_splits > MAX_SPLITS) return fail(RD_ERR_INVALID_ARG, "attn_splits out of range");
+    if (opt.kv_pages < 0) return fail(RD_ERR_INVALID_ARG, "kv_pages < 0");
+    if (opt.kv_pages > 0) {
+        if (opt.kv_format == RD_KV_INT8_SEG128)
+            return fail(RD_ERR_UNSUPPORTED, "a paged cache holds fp16 or E5M2 rows (INT8: contiguous cache)");
+        if (opt.max_batch < 2) return fail(RD_ERR_UNSUPPORTED, "a paged cache serves the batch step (max_batch 2..8)");
+        if (opt.executor == RD_EXEC_PERSISTENT)
+            return fail(RD_ERR_UNSUPPORTED, "a paged cache runs on the EAGER or GRAPH executor");
+    }
     if (opt.kv_format == RD_KV_INT8_SEG128 && opt.attn_splits == 1)
         return fail(RD_ERR_INVALID_ARG, "the INT8 cache needs at least 2 attention splits (the open segment has its own)");
 
@@ -302,8 +378,16 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     const char* why = nullptr;
     if (!step_supported(d.D, d.H, d.Hk, d.hd, d.F, &why)) return fail(RD_ERR_UNSUPPORTED, why);
     // attention reads a layer's K or V with 32-bit byte offsets
-    if ((uint64_t)d.Hk * opt.max_context * d.hd * (opt.kv_format == RD_KV_FP16 ? 2 : 1) > 0x7fffffffull)
+    if (opt.kv_pages == 0 &&
+        (uint64_t)d.Hk * opt.max_context * d.hd * (opt.kv_format == RD_KV_FP16 ? 2 : 1) > 0x7fffffffull)
         return fail(RD_ERR_INVALID_ARG, "n_kv_heads * max_context * head_dim * element bytes must stay below 2 GiB");
+    if (opt.kv_pages > 0) {
+        const int prow = 4096 / (d.hd * (opt.kv_format == RD_KV_FP16 ? 2 : 1));
+        if ((opt.max_context + prow - 1) / prow > 4094)
+            return fail(RD_ERR_INVALID_ARG, "paged cache: max_context above 4094 pages per sequence");
+        if ((uint64_t)opt.kv_pages * d.Hk * 4096 > 0x7fffffffull)
+            return fail(RD_ERR_INVALID_ARG, "paged cache: kv_pages * n_kv_heads * 4 KiB must stay below 2 GiB");
+    }
 
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) return fail(RD_ERR_DEVICE, "no HIP device");
@@ -434,11 +518,32 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     const size_t kv_elems = NB * kv_seq;
     const size_t es = opt.kv_format == RD_KV_FP16 ? 2 : 1;
     m->nseg = (int)((ctx + SEG - 1) / SEG);
-    CREATE_TRY(hipMalloc(&m->kc, kv_elems * es));
-    CREATE_TRY(hipMalloc(&m->vc, kv_elems * es));
-    CREATE_TRY(hipMemset(m->kc, 0, kv_elems * es));
-    CREATE_TRY(hipMemset(m->vc, 0, kv_elems * es));
-    m->kv_bytes = 2 * kv_elems * es;
+    if (opt.kv_pages > 0) {
+        // page pools [layer][group][kv head][page_rows][hd], 4 KiB per page
+        m->paged = true;
+        m->npages = opt.kv_pages;
+        m->prow = (int)(4096 / (hd * es));
+        while ((1 << m->pshift) < m->prow) ++m->pshift;
+        m->pt_ld = (int)((ctx + m->prow - 1) / m->prow);
+        const size_t pool = NL * (size_t)m->npages * Hk * 4096;
+        CREATE_TRY(hipMalloc(&m->kc, pool));
+        CREATE_TRY(hipMalloc(&m->vc, pool));
+        CREATE_TRY(hipMemset(m->kc, 0, pool));
+        CREATE_TRY(hipMemset(m->vc, 0, pool));
+        CREATE_TRY(hipMalloc((void**)&m->ptab_dev, NB * m->pt_ld * 4));
+        CREATE_TRY(hipMemset(m->ptab_dev, 0xff, NB * m->pt_ld * 4));   // -1: no page
+        m->ptab.assign(NB * m->pt_ld, -1);
+        m->refc.assign(m->npages, 0);
+        for (int p = m->npages - 1; p >= 0; --p) m->freel.push_back(p);
+        m->hpos.assign(NB, 0);
+        m->kv_bytes = 2 * pool + NB * m->pt_ld * 4;
+    } else {
+        CREATE_TRY(hipMalloc(&m->kc, kv_elems * es));
+        CREATE_TRY(hipMalloc(&m->vc, kv_elems * es));
+        CREATE_TRY(hipMemset(m->kc, 0, kv_elems * es));
+        CREATE_TRY(hipMemset(m->vc, 0, kv_elems * es));
+        m->kv_bytes = 2 * kv_elems * es;
+    }
     if (opt.kv_format == RD_KV_INT8_SEG128) {
         const size_t st_elems = NB * NL * 2 * Hk * SEG * hd, meta_elems = NB * NL * 2 * Hk * m->nseg * 2;
         CREATE_TRY(hipMalloc(&m->stage, st_elems * 2));
@@ -509,6 +614,13 @@ extern "C" rd_status rd_model_create(const void* blob, size_t blob_bytes, const 
     A.st_bstride = NL * 2 * Hk * SEG * hd;
     A.meta_bstride = NL * 2 * Hk * (size_t)m->nseg * 2;
     A.xh = (_Float16*)(X + o_xh);
+    if (m->paged) {
+        A.ptab = m->ptab_dev;
+        A.pt_ld = m->pt_ld;
+        A.pshift = m->pshift;
+        A.npages = m->npages;
+        A.kv_bstride = 0;
+    }
 
     // ---- executor: the persistent kernel where its shape is built, else the graph
     if (NB > 1) {
@@ -546,19 +658,79 @@ extern "C" rd_status rd_model_get_info(const rd_model* m, rd_model_info* o) {
     o->weight_bytes = m->wbytes;
     o->streamed_bytes = m->streamed;
     o->kv_bytes = m->kv_bytes;
+    o->kv_pages = m->npages;
+    o->page_rows = m->paged ? m->prow : 0;
     return RD_OK;
 }
 
 extern "C" rd_status rd_reset(rd_model* m) {
     rd_status st = check_model(m);
     if (st) return st;
+    if (m->paged) {
+        HIP_TRY(hipSetDevice(m->dev));
+        HIP_TRY(hipStreamSynchronize(m->stream));
+        for (int b = 0; b < m->opt.max_batch; ++b) page_release(m, b);
+    }
     m->host_pos = 0;
     return RD_OK;
 }
 
 extern "C" rd_status rd_get_position(const rd_model* m, int32_t* pos) {
     if (!m || !pos) return fail(RD_ERR_INVALID_ARG, "NULL argument");
-    *pos = m->host_pos;
+    *pos = m->paged ? m->hpos[0] : m->host_pos;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_seq_reset(rd_model* m, int32_t seq) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!m->paged) return fail(RD_ERR_UNSUPPORTED, "a contiguous cache has no per-sequence pages (rd_reset)");
+    if (seq < 0 || seq >= m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "seq out of range");
+    HIP_TRY(hipSetDevice(m->dev));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    page_release(m, seq);
+    return RD_OK;
+}
+
+extern "C" rd_status rd_seq_fork(rd_model* m, int32_t src, int32_t dst) {
+    rd_status st = check_model(m);
+    if (st) return st;
+    if (!m->paged) return fail(RD_ERR_UNSUPPORTED, "prefix sharing needs a paged cache");
+    if (src < 0 || src >= m->opt.max_batch || dst < 0 || dst >= m->opt.max_batch || src == dst)
+        return fail(RD_ERR_INVALID_ARG, "src and dst must be distinct sequences");
+    HIP_TRY(hipSetDevice(m->dev));
+    HIP_TRY(hipStreamSynchronize(m->stream));
+    page_release(m, dst);
+    const int n = (m->hpos[src] + m->prow - 1) >> m->pshift;   // pages holding rows
+    for (int j = 0; j < n; ++j) {
+        const int e = m->ptab[(size_t)src * m->pt_ld + j];
+        m->ptab[(size_t)dst * m->pt_ld + j] = e;
+        if (e >= 0) ++m->refc[e];
+    }
+    m->hpos[dst] = m->hpos[src];
+    HIP_TRY(hipMemcpy(m->ptab_dev, m->ptab.data(), m->ptab.size() * 4, hipMemcpyHostToDevice));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_seq_position(const rd_model* m, int32_t seq, int32_t* pos) {
+    if (!m || !pos) return fail(RD_ERR_INVALID_ARG, "NULL argument");
+    if (seq < 0 || seq >= m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "seq out of range");
+    *pos = m->paged ? m->hpos[seq] : m->host_pos;
+    return RD_OK;
+}
+
+extern "C" rd_status rd_kv_page_stats(const rd_model* m, int32_t* free_pages, int32_t* used_pages,
+                                      int32_t* shared_pages) {
+    if (!m) return fail(RD_ERR_INVALID_ARG, "model is NULL");
+    if (!m->paged) return fail(RD_ERR_UNSUPPORTED, "a contiguous cache has no pages");
+    int used = 0, shared = 0;
+    for (int r : m->refc) {
+        used += r > 0;
+        shared += r > 1;
+    }
+    if (free_pages) *free_pages = (int32_t)m->freel.size();
+    if (used_pages) *used_pages = used;
+    if (shared_pages) *shared_pages = shared;
     return RD_OK;
 }
 
@@ -576,6 +748,7 @@ extern "C" rd_status rd_set_executor(rd_model* m, int32_t executor) {
 extern "C" rd_status rd_set_position(rd_model* m, int32_t pos) {
     rd_status st = check_model(m);
     if (st) return st;
+    if (m->paged) return fail(RD_ERR_UNSUPPORTED, "a paged cache keeps a position per sequence (rd_seq_reset)");
     if (pos < 0 || pos > m->host_pos) return fail(RD_ERR_INVALID_ARG, "position must be in [0, current]");
     if (m->opt.kv_format == RD_KV_INT8_SEG128 && pos % SEG != 0 && pos / SEG != m->host_pos / SEG)
         return fail(RD_ERR_INVALID_ARG, "INT8 cache: rewind only to a segment start or inside the open segment");
@@ -675,11 +848,19 @@ extern "C" rd_status rd_decode_step(rd_model* m, const int32_t* tokens, int32_t 
     if (st) return st;
     if (!tokens) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
-    if (m->host_pos >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
-    if (!tokens_ok(m, tokens, batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (!tokens_ok(m, tokens, batch, true)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    int steps[8] = {};
+    for (int b = 0; b < batch; ++b) {
+        steps[b] = tokens[b] != -1;
+        const int at = m->paged ? m->hpos[b] : m->host_pos;
+        if (steps[b] && at >= m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "context full");
+    }
     HIP_TRY(hipSetDevice(m->dev));
+    if (m->paged && (st = page_prepare(m, steps))) return st;
     HIP_TRY(set_state(m, tokens));
     if ((st = step_enqueue(m))) return st;
+    if (m->paged)
+        for (int b = 0; b < batch; ++b) m->hpos[b] += steps[b];
     const size_t nlog = (size_t)batch * m->d.V;
     if (logits) HIP_TRY(hipMemcpyAsync(m->logits_host, m->A.logits, nlog * 4, hipMemcpyDeviceToHost, m->stream));
     HIP_TRY(hipMemcpyAsync(m->state_host, m->A.st, sizeof(StepState), hipMemcpyDeviceToHost, m->stream));
@@ -698,17 +879,29 @@ extern "C" rd_status rd_prefill(rd_model* m, const int32_t* tokens, int32_t batc
     if (!tokens && n > 0) return fail(RD_ERR_INVALID_ARG, "tokens is NULL");
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
     if (n < 0) return fail(RD_ERR_INVALID_ARG, "n < 0");
-    if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "tokens do not fit the context");
-    if (!tokens_ok(m, tokens, n * batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    if (!tokens_ok(m, tokens, n * batch, true)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    int steps[8] = {};
+    for (int b = 0; b < batch; ++b) {
+        for (int i = 0; i < n; ++i) steps[b] += tokens[(size_t)i * batch + b] != -1;
+        if (!m->paged) steps[b] = n;
+        const int64_t at = m->paged ? m->hpos[b] : m->host_pos;
+        if (at + steps[b] > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "tokens do not fit the context");
+    }
     HIP_TRY(hipSetDevice(m->dev));
+    if (m->paged && (st = page_prepare(m, steps))) return st;
     // one step per token on the graph path (the persistent kernel reads its
     // token from the device state, which a prompt would overwrite per step)
     const int32_t ex = m->opt.executor;
     if (ex == RD_EXEC_PERSISTENT) m->opt.executor = RD_EXEC_GRAPH;
     for (int i = 0; i < n && !st; ++i) {
-        hipError_t e = set_state(m, tokens + (size_t)i * batch, i == 0);
+        const int32_t* row = tokens + (size_t)i * batch;
+        hipError_t e = set_state(m, row, i == 0);
         if (e != hipSuccess) st = dev_fail(m, "k_set_state", e);
-        else if (!(st = step_enqueue(m))) m->host_pos += 1;
+        else if (!(st = step_enqueue(m))) {
+            m->host_pos += 1;
+            if (m->paged)
+                for (int b = 0; b < batch; ++b) m->hpos[b] += row[b] != -1;
+        }
     }
     m->opt.executor = ex;
     if (st) return st;
@@ -768,10 +961,19 @@ static rd_status generate_enqueue(rd_model* m, const int32_t* first, int32_t bat
     if (!first) return fail(RD_ERR_INVALID_ARG, "first is NULL");
     if (batch != m->opt.max_batch) return fail(RD_ERR_INVALID_ARG, "batch must equal max_batch");
     if (n < 0) return fail(RD_ERR_INVALID_ARG, "n_steps < 0");
-    if ((int64_t)m->host_pos + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "steps do not fit the context");
+    // (a paged cache: every sequence takes part in every generated step)
     if (!tokens_ok(m, first, batch)) return fail(RD_ERR_INVALID_ARG, "token id out of range");
+    int steps[8] = {};
+    for (int b = 0; b < batch; ++b) {
+        steps[b] = n;
+        const int64_t at = m->paged ? m->hpos[b] : m->host_pos;
+        if (at + n > m->opt.max_context) return fail(RD_ERR_CONTEXT_FULL, "steps do not fit the context");
+    }
     HIP_TRY(hipSetDevice(m->dev));
+    if (m->paged && n > 0 && (st = page_prepare(m, steps))) return st;
     HIP_TRY(set_state(m, first));
+    if (m->paged)
+        for (int b = 0; b < batch; ++b) m->hpos[b] += n;
     if (m->opt.executor == RD_EXEC_PERSISTENT) {
         // whole runs of steps in one launch, in chunks that keep one kernel short
         constexpr int kChunk = 512;
@@ -846,6 +1048,29 @@ extern "C" rd_status rd_debug_export_kv(rd_model* m, int32_t seq, int32_t layer,
     if (st) return st;
     if (!dst || seq < 0 || seq >= m->opt.max_batch || layer < 0 || layer >= m->d.L || which < 0 || which > 1)
         return fail(RD_ERR_INVALID_ARG, "bad export arguments");
+    if (m->paged) {
+        // the sequence's rows gathered through its page table, the contiguous layout
+        const size_t Hk = m->d.Hk, ctx = m->opt.max_context, hd = m->d.hd, R = m->prow;
+        const size_t es = m->opt.kv_format == RD_KV_FP16 ? 2 : 1, row = hd * es;
+        const size_t total = Hk * ctx * row, pool = (size_t)m->npages * Hk * 4096;
+        if (cap < total) return fail(RD_ERR_INVALID_ARG, "destination too small: need " + std::to_string(total));
+        HIP_TRY(hipSetDevice(m->dev));
+        HIP_TRY(hipStreamSynchronize(m->stream));
+        std::vector<uint8_t> lay(pool);
+        HIP_TRY(hipMemcpy(lay.data(), (const uint8_t*)(which ? m->vc : m->kc) + (size_t)layer * pool, pool,
+                          hipMemcpyDeviceToHost));
+        uint8_t* out = (uint8_t*)dst;
+        memset(out, 0, total);
+        for (int j = 0; j < m->pt_ld; ++j) {
+            const int e = m->ptab[(size_t)seq * m->pt_ld + j];
+            if (e < 0) continue;
+            const size_t n = std::min(R, ctx - j * R);
+            for (size_t g = 0; g < Hk; ++g)
+                memcpy(out + (g * ctx + j * R) * row, lay.data() + ((size_t)e * Hk + g) * 4096, n * row);
+        }
+        if (written) *written = total;
+        return RD_OK;
+    }
     KvRegion r[3];
     const int nr = kv_regions(m, seq, layer, which, r);
     size_t total = 0;
@@ -869,6 +1094,7 @@ extern "C" rd_status rd_debug_import_kv(rd_model* m, int32_t seq, int32_t layer,
     if (!src || seq < 0 || seq >= m->opt.max_batch || layer < 0 || layer >= m->d.L || which < 0 || which > 1 ||
         pos < 0 || pos > m->opt.max_context)
         return fail(RD_ERR_INVALID_ARG, "bad import arguments");
+    if (m->paged) return fail(RD_ERR_UNSUPPORTED, "import into a paged cache");
     KvRegion r[3];
     const int nr = kv_regions(m, seq, layer, which, r);
     size_t total = 0;

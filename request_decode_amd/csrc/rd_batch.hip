@@ -22,9 +22,18 @@ namespace {
 constexpr int BW = 256;
 
 // x[b] = E[token[b]] (fp32); an out-of-range token flags ERR_TOKEN and reads row 0.
+// Paged cache: a token of -1 sits the step out (act[b] = 0, x[b] = 0).
 __global__ __launch_bounds__(BW) void k_b_embed(StepArgs A) {
     const int b = blockIdx.x;
     int tok = A.st->token[b];
+    if (A.ptab) {
+        const bool on = tok != -1;
+        if (threadIdx.x == 0) A.st->act[b] = on;
+        if (!on) {
+            for (int i = threadIdx.x; i < A.D; i += BW) A.x[(size_t)b * A.D + i] = 0.f;
+            return;
+        }
+    }
     if (tok < 0 || tok >= A.V) {
         if (threadIdx.x == 0) atomicOr(&A.st->err, ERR_TOKEN);
         tok = 0;
@@ -94,6 +103,7 @@ __global__ __launch_bounds__(BWA) void k_b_argmax(StepArgs A) {
     __shared__ float s_v[BWA / WAVE];
     __shared__ int s_i[BWA / WAVE];
     const int b = blockIdx.x, V = A.V;
+    if (A.ptab && !A.st->act[b]) return;   // sat the step out: token stays -1
     const float* lg = A.logits + (size_t)b * V;
     Best best{-INFINITY, INT_MAX};
     bool bad = false;
@@ -126,12 +136,30 @@ __global__ __launch_bounds__(BWA) void k_b_argmax(StepArgs A) {
     }
 }
 
-__global__ void k_b_advance(StepState* st) {
+__global__ void k_b_advance(StepState* st, int B, int paged) {
     st->n_gen += 1;
     st->pos += 1;
+    if (paged)
+        for (int b = 0; b < B; ++b) st->bpos[b] += st->act[b];
+}
+
+// Paged cache, copy on write: page group src copied to dst.  For every
+// (layer, K/V) the Hk pages of a group are contiguous (Hk * 4 KiB).
+__global__ __launch_bounds__(BW) void k_page_copy(StepArgs A, int src, int dst) {
+    const int l = blockIdx.x >> 1;
+    uint8_t* pool = reinterpret_cast<uint8_t*>((blockIdx.x & 1) ? A.vc : A.kc);
+    const size_t blk = (size_t)A.Hk * 4096;
+    const uint4* sp = reinterpret_cast<const uint4*>(pool + ((size_t)l * A.npages + src) * blk);
+    uint4* dp = reinterpret_cast<uint4*>(pool + ((size_t)l * A.npages + dst) * blk);
+    for (size_t i = threadIdx.x; i < blk / 16; i += BW) dp[i] = sp[i];
 }
 
 }  // namespace
+
+hipError_t launch_page_copy(const StepArgs& A, int src, int dst, hipStream_t s) {
+    hipLaunchKernelGGL(k_page_copy, dim3(2 * A.n_layers), dim3(BW), 0, s, A, src, dst);
+    return hipGetLastError();
+}
 
 #define B_TRY(expr)                          \
     do {                                     \
@@ -158,7 +186,7 @@ hipError_t launch_step_batch(const StepArgs& A, hipStream_t s) {
     B_TRY(launch_gemm_b8(A.lm_head, A.xh, false, D, A.logits, A.V, false, A.V, D, B, A.ncu, s));
     hipLaunchKernelGGL(k_b_argmax, dim3(B), dim3(BWA), 0, s, A);
     B_TRY(hipGetLastError());
-    hipLaunchKernelGGL(k_b_advance, dim3(1), dim3(1), 0, s, A.st);
+    hipLaunchKernelGGL(k_b_advance, dim3(1), dim3(1), 0, s, A.st, B, A.ptab ? 1 : 0);
     return hipGetLastError();
 }
 

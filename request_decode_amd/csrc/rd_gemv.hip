@@ -286,17 +286,26 @@ __global__ __launch_bounds__(T) void k_gemm_b8(const _Float16* __restrict__ W, c
                 for (int j = 0; j < 4; ++j) a1[j] = __shfl_xor(acc[j], 1);
                 const int on = blk * R + n;
                 if (n < R && (n & 1) == 0 && on < N) {
-                    const int pos = EA.st->pos;
-                    const float2* rope = EA.rope + (size_t)pos * (EA.hd / 2);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int ob = 4 * q + j;
                         if (ob >= B) continue;
+                        // paged cache: each sequence at its own position, and
+                        // one that sits the step out stores nothing
+                        if (EA.ptab && !EA.st->act[ob]) continue;
+                        const int pos = EA.ptab ? EA.st->bpos[ob] : EA.st->pos;
+                        const float2* rope = EA.rope + (size_t)pos * (EA.hd / 2);
                         const QkvPair o = qkv_pair(EA.hd, EA.H, EA.Hk, on, acc[j], a1[j], rope);
                         if (o.kind == 0) {
                             float* qv = EA.q + (size_t)ob * EA.H * EA.hd + o.head * EA.hd;
                             qv[o.d0] = o.y0;
                             qv[o.d1] = o.y1;
+                        } else if (EA.ptab) {
+                            if constexpr (EPI - EPI_QKV != KV_INT8) {
+                                const int which = o.kind == 2;
+                                kv_put_paged<EPI - EPI_QKV>(EA, ob, layer, which, o.head, pos, o.d0, o.y0);
+                                kv_put_paged<EPI - EPI_QKV>(EA, ob, layer, which, o.head, pos, o.d1, o.y1);
+                            }
                         } else {
                             StepArgs Ab = EA;   // sequence ob's cache
                             Ab.kc = reinterpret_cast<uint8_t*>(EA.kc) + (size_t)ob * EA.kv_bstride;

@@ -20,6 +20,11 @@ struct StepState {
     int err;        // ErrBits seen on the device
     int pad;
     int token[8];   // token at `pos` for each sequence
+    // paged KV cache (sequences at their own positions): sequence b decodes
+    // position bpos[b]; a token of -1 sits the step out (act[b] = 0: nothing
+    // stored, position kept)
+    int bpos[8];
+    int act[8];
 };
 
 // Weights of one layer in the device layout (see the re-tiling in rd_api.hip).
@@ -45,6 +50,13 @@ struct AttnArgs {
     void* kcw;               // INT8: writable code rows of K and V (sealed by the merge)
     void* vcw;
     float* part;             // [H][S][hd+2] split partials: o[hd], m, l
+    // paged KV cache: kc/vc are this layer's page pool [npages][Hk][R][hd]
+    // (R = 1 << pshift positions of one kv head per 4 KiB page), and row p of
+    // sequence b lies in page ptab[b*pt_ld + p/R] (-1: not allocated);
+    // positions and activity per sequence (pos_ptr + b, act_ptr + b)
+    const int* ptab;         // NULL: contiguous cache
+    int pt_ld, pshift, npages;
+    const int* act_ptr;
     // at least hd*2 bytes that no attention step changes and that decode to
     // finite fp16 and E5M2 values (position 0's RoPE row: cos 1, sin 0; the
     // standalone attention entry point: its queries, whose values are never
@@ -59,11 +71,17 @@ struct AttnArgs {
     // buffer, the cache ones in bytes)
     int nseq;
     size_t q_bstride, part_bstride, kv_bstride, st_bstride, meta_bstride;
+    int pos_bstride;         // 1: a position per sequence (paged), 0: one for all
 };
 // Sequence b's view of the attention arguments.
 __host__ __device__ inline AttnArgs attn_seq(AttnArgs T, int b) {
     T.q += (size_t)b * T.q_bstride;
     T.out += (size_t)b * T.q_bstride;
+    T.pos_ptr += b * T.pos_bstride;
+    if (T.ptab) {
+        T.ptab += (size_t)b * T.pt_ld;
+        T.act_ptr += b;
+    }
     T.part += (size_t)b * T.part_bstride;
     T.kc = reinterpret_cast<const uint8_t*>(T.kc) + (size_t)b * T.kv_bstride;
     T.vc = reinterpret_cast<const uint8_t*>(T.vc) + (size_t)b * T.kv_bstride;
@@ -89,6 +107,11 @@ struct StepArgs {
     size_t st_bstride;       // INT8: elements of one sequence's staging rows
     size_t meta_bstride;     // INT8: floats of one sequence's (scale, zp) table
     _Float16* xh;            // B > 1: [B][D] normalised inputs of the QKV and gate/up GEMMs
+    // paged KV cache (B > 1): kc/vc are page pools [n_layers][npages][Hk][R][hd],
+    // R = 1 << pshift positions per 4 KiB page; sequence b's page table is
+    // ptab[b*pt_ld ..] (device, -1: no page); positions per sequence (st->bpos)
+    int* ptab;               // NULL: contiguous cache
+    int pt_ld, pshift, npages;
     const _Float16* embed;
     const _Float16* g_final;
     const _Float16* lm_head;
@@ -125,8 +148,9 @@ struct StepArgs {
 // The attention view of layer l of the step's buffers.
 __host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
     AttnArgs T{};
-    const size_t lay = (size_t)l * A.Hk * A.max_ctx * A.hd;
     const size_t es = A.kvfmt == KV_FP16 ? 2 : 1;
+    const size_t lay = A.ptab ? (size_t)l * A.npages * A.Hk * ((size_t)1 << A.pshift) * A.hd
+                              : (size_t)l * A.Hk * A.max_ctx * A.hd;
     T.q = A.q;
     T.out = A.a;
     T.kc = reinterpret_cast<uint8_t*>(A.kc) + lay * es;
@@ -155,6 +179,17 @@ __host__ __device__ inline AttnArgs attn_args(const StepArgs& A, int l) {
     T.kv_bstride = A.kv_bstride;
     T.st_bstride = A.st_bstride;
     T.meta_bstride = A.meta_bstride;
+    T.pos_bstride = 0;
+    if (A.ptab) {
+        T.ptab = A.ptab;
+        T.pt_ld = A.pt_ld;
+        T.pshift = A.pshift;
+        T.npages = A.npages;
+        T.pos_ptr = A.st->bpos;
+        T.act_ptr = A.st->act;
+        T.pos_bstride = 1;
+        T.kv_bstride = 0;
+    }
     return T;
 }
 
@@ -212,6 +247,8 @@ hipError_t launch_gemv_f16(const void* W, const void* x, float* y, int N, int K,
 // Y[b][n] (=|+=) sum_k W[n][k] x[b][k] for b < B <= 8 on the matrix cores; x fp16 or fp32 (row stride ldx),
 // y fp32 (row stride ldy); K % 64 == 0, K <= 8192.
 hipError_t launch_step_batch(const StepArgs& A, hipStream_t s);
+// Paged cache: page group src copied to dst (copy on write).
+hipError_t launch_page_copy(const StepArgs& A, int src, int dst, hipStream_t s);
 hipError_t launch_attn_any(const AttnArgs& A, int kvfmt, int hd, int G, hipStream_t s);
 hipError_t launch_gemm_b8(const _Float16* W, const void* x, bool x_f32, int ldx, float* y, int ldy, bool acc, int N,
                           int K, int B, int ncu, hipStream_t s);

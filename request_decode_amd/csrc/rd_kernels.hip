@@ -68,12 +68,19 @@ __global__ __launch_bounds__(WG) void k_qkv(StepArgs A, LayerW Lw, int layer) {
 // ---- phase 2a: split-K attention partials, one wave per (kv-head, split) ---------
 // The wave reads each K/V row of its key range once for all G query heads of
 // the group.  Tasks past the splits in use at this position exit at once.
-template <int HD, int G, int KVF>
+// PG: a paged cache (the batch step): the split's page-table entries are
+// staged in LDS first; a sequence that sits the step out is skipped.
+constexpr int PAGE_ENTRIES = 4096;   // page-table entries one split can span
+template <int HD, int G, int KVF, bool PG = false>
 __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
     using Geo = AttnGeo<HD>;
     const AttnArgs T = attn_seq(T0, blockIdx.y);   // sequence blockIdx.y
     constexpr int NW = ATT_WAVES;
     __shared__ float s_att[NW * G * (HD + 2)];
+    __shared__ int s_pt[PG ? PAGE_ENTRIES : 1];
+    if constexpr (PG) {
+        if (!*T.act_ptr) return;
+    }
     const int pos = *T.pos_ptr, L = pos + 1;
     const SplitPlan pl = split_plan(L, T.S, KVF);
     const int t = blockIdx.x;   // one split of one kv-head per workgroup
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
     split_range(pl, L, s, p0, p1);
     AttnAcc<HD, G> acc;
     acc.clear();
-    with_src<HD, KVF, false>(T, g, pos, s == pl.ncut, [&](auto src) {
+    auto run = [&](auto src) {
         using Src = decltype(src);
         typename Src::Buf kb[3];
         attn_wave_first<Src, NW>(src, p0, p1, w, kb);
@@ -95,7 +102,15 @@ __global__ __launch_bounds__(ATT_WAVES * WAVE) void k_attn(AttnArgs T0) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) qv[h][i] = T.q[(g * G + h) * HD + j * 8 + i] * qs;
         attn_wave_run<Src, NW>(src, p0, p1, w, qv, acc, kb, NoFix{});
-    });
+    };
+    if constexpr (PG) {
+        const int pt0 = p0 >> T.pshift, npt = ((p1 - 1) >> T.pshift) - pt0 + 1;   // npt <= PAGE_ENTRIES (host check)
+        for (int i = threadIdx.x; i < npt; i += ATT_WAVES * WAVE) s_pt[i] = T.ptab[pt0 + i];
+        __syncthreads();
+        with_src_paged<HD, KVF>(T, g, pos, s_pt, pt0, npt, run);
+    } else {
+        with_src<HD, KVF, false>(T, g, pos, s == pl.ncut, run);
+    }
     acc.finish();
     attn_part_store<HD, G>(s_att, w, acc);
     __syncthreads();
@@ -122,6 +137,7 @@ template <int HD, int G, int KVF>
 __global__ __launch_bounds__(WG) void k_merge(AttnArgs T0) {
     using Geo = AttnGeo<HD>;
     const AttnArgs T = attn_seq(T0, blockIdx.y);   // sequence blockIdx.y
+    if (T.ptab && !*T.act_ptr) return;             // paged: the sequence sits this step out
     const int pos = *T.pos_ptr;
     const int nact = split_plan(pos + 1, T.S, KVF).nact;
     const int t = blockIdx.x * (WG / WAVE) + wave_id();
@@ -292,11 +308,17 @@ hipError_t launch_attn_t(const AttnArgs& A, int hd, int G, hipStream_t s) {
     const int nseq = A.nseq > 1 ? A.nseq : 1;
     dim3 grid(A.Hk * A.S, nseq), ablock(ATT_WAVES * WAVE), block(WG);   // k_attn: one split per workgroup
     dim3 mgrid((A.H * (hd / 64) + wpb - 1) / wpb, nseq);
-#define RD_ATT(HDv, Gv)                                                        \
-    if (hd == HDv && G == Gv) {                                                \
-        hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, ablock, 0, s, A);     \
-        hipLaunchKernelGGL((k_merge<HDv, Gv, KVF>), mgrid, block, 0, s, A);    \
-        return hipGetLastError();                                              \
+#define RD_ATT(HDv, Gv)                                                                      \
+    if (hd == HDv && G == Gv) {                                                              \
+        if constexpr (KVF != KV_INT8) {                                                      \
+            if (A.ptab) hipLaunchKernelGGL((k_attn<HDv, Gv, KVF, true>), grid, ablock, 0, s, A); \
+            else hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, ablock, 0, s, A);              \
+        } else {                                                                             \
+            if (A.ptab) return hipErrorInvalidValue;                                         \
+            hipLaunchKernelGGL((k_attn<HDv, Gv, KVF>), grid, ablock, 0, s, A);                   \
+        }                                                                                    \
+        hipLaunchKernelGGL((k_merge<HDv, Gv, KVF>), mgrid, block, 0, s, A);                  \
+        return hipGetLastError();                                                            \
     }
     RD_ATT(128, 1) RD_ATT(128, 2) RD_ATT(128, 4) RD_ATT(128, 8)
     RD_ATT(64, 1) RD_ATT(64, 2) RD_ATT(64, 4) RD_ATT(64, 8)

@@ -239,6 +239,22 @@ __device__ __forceinline__ float kv_put(const StepArgs& A, int layer, int which,
     }
 }
 
+// Element d of this step's K (which = 0) or V row of kv head g at position
+// pos of sequence b, into its page of a paged cache (fp16 or E5M2); the
+// host allocates the page before the step.
+template <int KVF>
+__device__ __forceinline__ void kv_put_paged(const StepArgs& A, int b, int layer, int which, int g, int pos, int d,
+                                             float v) {
+    static_assert(KVF != KV_INT8, "paged caches hold fp16 or E5M2 rows");
+    const int page = A.ptab[(size_t)b * A.pt_ld + (pos >> A.pshift)];
+    if (page < 0) return;
+    const size_t R = (size_t)1 << A.pshift;
+    const size_t idx = ((((size_t)layer * A.npages + page) * A.Hk + g) * R + (pos & (R - 1))) * A.hd + d;
+    const uint16_t h = f2h_bits(v);
+    if constexpr (KVF == KV_FP16) reinterpret_cast<uint16_t*>(which ? A.vc : A.kc)[idx] = h;
+    else reinterpret_cast<uint8_t*>(which ? A.vc : A.kc)[idx] = e5m2_encode(h);
+}
+
 // ============================================================================
 // Attention: one wave per (kv-head, key split) task
 // ============================================================================
@@ -322,7 +338,10 @@ struct KvBuf {
     uint32_t w[KVF == KV_INT8 ? 40 : 32];
 };
 
-template <int HD, int SRC, bool P>
+// PG: a paged cache (batch step only): row p's page comes from the split's
+// page-table entries staged in LDS (pt, first entry pt0); a row in a page
+// that is not allocated reads as zeros like a row not fetched.
+template <int HD, int SRC, bool P, bool PG = false>
 struct KvSrc {
     using Geo = AttnGeo<HD>;
     // rows per lane per batch: 16 bytes per lane and row for fp16 rows, 8 for
@@ -342,12 +361,24 @@ struct KvSrc {
     using Buf = KvBuf<KVF>;
     static_assert(2 * U * RW + (SRC == SRC_I8 ? 8 : 0) <= (int)(sizeof(Buf) / 4), "KvBuf");
 
+    static_assert(!PG || SRC == SRC_F16 || SRC == SRC_E5M2, "paged caches hold fp16 or E5M2 rows");
     __amdgpu_buffer_rsrc_t rk, rv, rmk, rmv;
     int g, ld, nseg, pos;
+    int pshift, Hk, pt0, pt_n;
+    const int* pt;
 
-    __device__ __forceinline__ KvSrc(const AttnArgs& A, int g_, int pos_) : g(g_), pos(pos_) {
+    __device__ __forceinline__ KvSrc(const AttnArgs& A, int g_, int pos_, const int* pt_ = nullptr, int pt0_ = 0,
+                                     int pt_n_ = 0)
+        : g(g_), pos(pos_), pt(pt_), pt0(pt0_), pt_n(pt_n_) {
         nseg = A.nseg;
-        if constexpr (SRC == SRC_STAGE) {
+        pshift = A.pshift;
+        Hk = A.Hk;
+        if constexpr (PG) {
+            ld = 0;
+            const size_t bytes = (size_t)A.npages * A.Hk * ((size_t)1 << A.pshift) * HD * ES;
+            rk = attn_rsrc(A.kc, bytes);
+            rv = attn_rsrc(A.vc, bytes);
+        } else if constexpr (SRC == SRC_STAGE) {
             ld = SEG;
             rk = attn_rsrc(A.kst, (size_t)A.Hk * SEG * HD * 2);
             rv = attn_rsrc(A.vst, (size_t)A.Hk * SEG * HD * 2);
@@ -362,6 +393,14 @@ struct KvSrc {
         }
     }
     __device__ __forceinline__ uint32_t row_off(int p, int j) const {
+        if constexpr (PG) {
+            // rows past the split (never fetched) may lie past the staged
+            // entries: their index is clamped to an entry that exists
+            const int e = (p >> pshift) - pt0;
+            const int page = pt[e < pt_n ? e : 0];
+            const int r = p & ((1 << pshift) - 1);
+            return page < 0 ? ROW_NONE : ((((uint32_t)page * Hk + g) << pshift) + r) * (uint32_t)(HD * ES) + j * 8 * ES;
+        }
         const int r = SRC == SRC_STAGE ? p % SEG : p;
         return ((uint32_t)(g * ld + r) * HD + j * 8) * ES;
     }
@@ -630,6 +669,12 @@ __device__ __forceinline__ void attn_wave_run(const Src& src, int p0, int p1, in
 }
 // Calls f with the row source of a split: the cache format's rows, or for
 // INT8 the sealed codes or (open: the open-segment split) the fp16 staging.
+template <int HD, int KVF, class F>
+__device__ __forceinline__ void with_src_paged(const AttnArgs& T, int g, int pos, const int* pt, int pt0, int pt_n,
+                                               F f) {
+    static_assert(KVF != KV_INT8, "paged caches hold fp16 or E5M2 rows");
+    f(KvSrc<HD, KVF == KV_FP16 ? SRC_F16 : SRC_E5M2, false, true>(T, g, pos, pt, pt0, pt_n));
+}
 template <int HD, int KVF, bool P, class F>
 __device__ __forceinline__ void with_src(const AttnArgs& T, int g, int pos, bool open, F f) {
     if constexpr (KVF == KV_INT8) {

@@ -82,6 +82,12 @@ def test_option_validation_on_host(rd):
     assert _create(rd, blob, kv_format=7)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, executor=9)[0] == rd.RD_ERR_INVALID_ARG
     assert _create(rd, blob, attn_splits=1000)[0] == rd.RD_ERR_INVALID_ARG
+    # paged cache: fp16 or E5M2 rows, the batch step, a pool below 2 GiB per layer
+    assert _create(rd, blob, max_batch=2, kv_pages=-1)[0] == rd.RD_ERR_INVALID_ARG
+    assert _create(rd, blob, max_batch=2, kv_pages=8, kv_format=2)[0] == rd.RD_ERR_UNSUPPORTED
+    assert _create(rd, blob, max_batch=1, kv_pages=8)[0] == rd.RD_ERR_UNSUPPORTED
+    assert _create(rd, blob, max_batch=2, kv_pages=1 << 20)[0] == rd.RD_ERR_INVALID_ARG
+    assert _create(rd, blob, max_batch=2, kv_pages=8, max_context=(1 << 22) - 1)[0] == rd.RD_ERR_INVALID_ARG
     # INT8: the open segment is a split of its own, so one split is too few
     assert _create(rd, blob, kv_format=2, attn_splits=1)[0] == rd.RD_ERR_INVALID_ARG
     # 4 kv heads x 64 dims x 2 bytes: at 2^22 positions one layer's K is 2 GiB,
