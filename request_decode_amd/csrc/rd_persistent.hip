@@ -591,15 +591,20 @@ template <int HD, int G>
 constexpr int attn_nq() { return G * 8 + 16; }
 // Row pos: this step's K/V row, from the exchange (it may not be visible in
 // the cache yet; the sources never fetch it under P).
+// (The lane's K and V values are held by value and picked as values: a
+// conditional on two array elements selects their addresses and keeps the
+// arrays in scratch memory.)
 struct FixNewRow {
     int pos;
-    const float (&kn)[8];
-    const float (&vn)[8];
+    float kn[8], vn[8];
     __device__ __forceinline__ bool active(int pb, int n) const { return pb <= pos && pos < pb + n; }
     __device__ __forceinline__ void apply(int p, int which, float (&f)[8]) const {
         if (p == pos)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) f[i] = which ? vn[i] : kn[i];
+            for (int i = 0; i < 8; ++i) {
+                const float k = kn[i], v = vn[i];
+                f[i] = which ? v : k;
+            }
     }
 };
 template <int HD, int G, int KVF>
@@ -624,7 +629,14 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
         acc.clear();
         with_src<HD, KVF, true>(T, sp.g, sp.pos, sp.open, [&](auto src) {
             using Src = decltype(src);
-            attn_wave_run<Src, NWA>(src, sp.p0, sp.p1, w, qv, acc, kb, FixNewRow{sp.pos, kn, vn});
+            FixNewRow fx;
+            fx.pos = sp.pos;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                fx.kn[i] = kn[i];
+                fx.vn[i] = vn[i];
+            }
+            attn_wave_run<Src, NWA>(src, sp.p0, sp.p1, w, qv, acc, kb, fx);
         });
         if (w == 0) tr(141);
         acc.finish();
@@ -725,8 +737,8 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // (cos, sin) of the RoPE pair each lane rotates in the epilogue,
             // loaded while the rows stream (kept for the whole step it would
             // be spilled)
-            float2 cs_lane = make_float2(1.f, 0.f);
-            if (2 * lane < qr1 - qr0) cs_lane = rope[((qr0 + 2 * lane) % HD) >> 1];
+            // (every lane loads one: the column is in the row for any lane)
+            const float2 cs_lane = rope[rope_col(HD, A.H, qr0 + 2 * lane)];
             lds_barrier();
             lds_barrier();
             TR(0 + TR_DONE);
@@ -735,9 +747,12 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // q/k/v words that lead to the merge are published.
             const bool seal_step = KVF == KV_INT8 && (pos + 1) % SEG == 0;
             for (int q = lane; 2 * q < qr1 - qr0; q += WAVE) {
-                const float2 cs = q == lane ? cs_lane : rope[((qr0 + 2 * q) % HD) >> 1];
-                const QkvPair o = qkv_pair(HD, A.H, A.Hk, qr0 + 2 * q, s_part[2 * q], s_part[2 * q + 1], &cs,
-                                           true);
+                // (not `q == lane ? cs_lane : rope[..]`: a conditional on two
+                // float2 lvalues selects their addresses, which puts cs_lane
+                // in scratch memory)
+                float2 cs = cs_lane;
+                if (q != lane) cs = rope[rope_col(HD, A.H, qr0 + 2 * q)];
+                const QkvPair o = qkv_pair_cs(HD, A.H, A.Hk, qr0 + 2 * q, s_part[2 * q], s_part[2 * q + 1], cs);
                 if (o.kind == 0) {
                     publish(&A.qb[o.head * HD + o.d0], o.y0, tag);
                     publish(&A.qb[o.head * HD + o.d1], o.y1, tag);

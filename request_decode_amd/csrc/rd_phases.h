@@ -182,21 +182,23 @@ __device__ __forceinline__ float silu_mul(float gt, float up) {
 // ============================================================================
 // Row pair (row0, row0+1) of the re-ordered QKV matrix: kind 0 = q head,
 // 1 = k head (both rotated: rows 2j, 2j+1 of a head are dims j and j+hd/2),
-// 2 = v (rows are consecutive dims).  rope: the (cos, sin) row of the
-// position, or (own) the pair's own (cos, sin).
+// 2 = v (rows are consecutive dims).  cs: the pair's (cos, sin) (rope_col
+// gives its column in the position's RoPE row; unused for v).
 struct QkvPair {
     int kind, head, d0, d1;
     float y0, y1;
 };
-__device__ __forceinline__ QkvPair qkv_pair(int hd, int H, int Hk, int row0, float a0, float a1, const float2* rope,
-                                            bool own = false) {
+__device__ __forceinline__ int rope_col(int hd, int H, int row0) {
+    const int Nq = H * hd;
+    return ((row0 < Nq ? row0 : row0 - Nq) % hd) >> 1;
+}
+__device__ __forceinline__ QkvPair qkv_pair_cs(int hd, int H, int Hk, int row0, float a0, float a1, float2 cs) {
     QkvPair o;
     const int Nq = H * hd, Nk = Hk * hd;
     if (row0 < Nq + Nk) {
         const bool isq = row0 < Nq;
         const int rho = isq ? row0 : row0 - Nq;
         const int j = (rho % hd) >> 1;
-        const float2 cs = own ? rope[0] : rope[j];
         o.kind = isq ? 0 : 1;
         o.head = rho / hd;
         o.d0 = j;
@@ -214,6 +216,11 @@ __device__ __forceinline__ QkvPair qkv_pair(int hd, int H, int Hk, int row0, flo
         o.y1 = a1;
     }
     return o;
+}
+// The same with the position's RoPE row (cos, sin) pairs.
+__device__ __forceinline__ QkvPair qkv_pair(int hd, int H, int Hk, int row0, float a0, float a1, const float2* rope) {
+    const float2 cs = row0 < (H + Hk) * hd ? rope[rope_col(hd, H, row0)] : make_float2(1.f, 0.f);
+    return qkv_pair_cs(hd, H, Hk, row0, a0, a1, cs);
 }
 
 // Store one element of the new K (which = 0) or V row in the cache format
@@ -450,9 +457,17 @@ struct KvSrc {
     // INT8 codes give code - zp; the row's scale is then applied once
     // (mul), to the row's score for K and to its softmax weight for V.
     static constexpr bool SCALED = SRC == SRC_I8;
+    // Word k of the (scale, zp) pair for K (which = 0) or V of row p's
+    // segment.  A select between two fixed words: an index that depends on
+    // p would keep the buffer's metadata words in scratch memory.
+    __device__ __forceinline__ uint32_t meta(const Buf& b, int pb, int p, int which, int k) const {
+        const bool second = p >= (pb / SEG + 1) * SEG;
+        const uint32_t w0 = which ? b.w[34 + k] : b.w[32 + k];
+        const uint32_t w1 = which ? b.w[38 + k] : b.w[36 + k];
+        return second ? w1 : w0;
+    }
     __device__ __forceinline__ float mul(const Buf& b, int pb, int p, int which) const {
-        const int mo = 32 + 2 * which + (p >= (pb / SEG + 1) * SEG ? 4 : 0);
-        return __uint_as_float(b.w[mo]);
+        return __uint_as_float(meta(b, pb, p, which, 0));
     }
     __device__ __forceinline__ void cvt(const Buf& b, int pb, int u, int p, int which, float (&f)[8]) const {
         const int base = (2 * u + which) * RW;
@@ -477,8 +492,7 @@ struct KvSrc {
         } else {
             // INT8: code - zp with the zero point of the row's segment (the
             // batch's rows fall in the segment of pb or the next one)
-            const int mo = 32 + 2 * which + (p >= (pb / SEG + 1) * SEG ? 4 : 0);
-            const float zp = __uint_as_float(b.w[mo + 1]);
+            const float zp = __uint_as_float(meta(b, pb, p, which, 1));
 #pragma unroll
             for (int i = 0; i < 8; ++i) f[i] = (float)((b.w[base + (i >> 2)] >> ((i & 3) * 8)) & 0xffu) - zp;
         }
