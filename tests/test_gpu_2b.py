@@ -363,6 +363,44 @@ def test_2b_short_graph_eager_teacher_forced(rd, orc, blob2b):
     print(f"2b short: steps={n} graded={graded} max|dlogit|={worst}")
 
 
+@pytest.mark.parametrize("kv", ["fp16", "e5m2"])
+def test_2b_batch8_long_sampled(rd, orc, blob2b, kv):
+    """The batch step's attention at the 2B shape over long contexts: 8
+    sequences fed 2048-token prompts (seed 116) in lockstep, so that every
+    split (8 per sequence and kv head) holds 16 (binary16) or 8 (E5M2)
+    batches and each of its three waves runs the pipelined loop.  Then the oracle's batch
+    step takes rows 0..p-1 of every sequence's GPU cache (E5M2 bytes
+    included: the cache-synchronised protocol) and decodes position p; the
+    GPU re-decodes p (rewound) and every sequence's logits are compared by
+    the per-logit rule."""
+    B, P = 8, 2048
+    ctx = P + 1
+    last = P - 1
+    prompts = synth.prompts(116, P, SHAPE.vocab, B)          # [B][P]
+    gm = rd.Model(blob2b, max_context=ctx, kv_format=kv, executor="graph", batch=B)
+    gm.prefill(prompts[:, :-1].T)                            # positions 0 .. P-2
+    om = orc.OracleModel(blob2b, ctx, batch=B, kv_format=kv)
+    for b in range(B):
+        for l in range(SHAPE.n_layers):
+            for w in (0, 1):
+                rows = gm.export_kv(l, w, seq=b)["rows"]
+                for g in range(SHAPE.n_kv_heads):
+                    om.set_rows(l, w, g, 0, rows[g, :last], b=b)
+    for p in (last, 1500):                                   # descending: each rewinds both sides to p
+        for b in range(B):
+            om.set_pos(p, b)
+        ol, on = om.step(prompts[:, p])
+        gm.set_position(p)
+        gl, gn = gm.decode_step(prompts[:, p])
+        worst = 0.0
+        for b in range(B):
+            e, _ = compare_step(gl[b], ol[b], int(gn[b]), ("b8 long", kv, p, b))
+            worst = max(worst, e)
+        print(f"  batch 8 {kv} p={p}: max|dlogit|={worst:.3e}", flush=True)
+    gm.close()
+    om.close()
+
+
 def test_2b_batch8_short_teacher_forced(rd, orc, blob2b):
     """The 2B model's batch-8 step: 8 prompts of 6 tokens, then 3 greedy
     steps, against the oracle's batch step."""
