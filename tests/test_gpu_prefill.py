@@ -105,16 +105,19 @@ def check_cache(orc, gm, om, shape, kv, n, tag, layers=None):
     return worst
 
 
-@pytest.mark.parametrize("shape_name", ["tiny", "gqa2", "hk8"])
+# (start, n, model): the 2500-token prompt (two chunks of 2048) on the tiny
+# model only, the shorter ones on every small model
+PREFILL_CASES = [(s0, n, m) for s0, n in ((0, 1), (0, 37), (0, 300), (50, 200)) for m in ("tiny", "gqa2", "hk8")]
+PREFILL_CASES += [(0, 2500, "tiny")]
+
+
 @pytest.mark.parametrize("kv", ["fp16", "e5m2", "int8"])
-@pytest.mark.parametrize("start,n", [(0, 1), (0, 37), (0, 300), (50, 200), (0, 2500)])
+@pytest.mark.parametrize("start,n,shape_name", PREFILL_CASES)
 def test_prefill_small_models(rd, orc, shape_name, kv, start, n):
     """Small models: prompts of 1 to 2500 tokens (two chunks of 2048),
     from position 0 or after 50 single decode steps (the chunk starts inside
     a segment and inside a 64-position attention block), every cache row
     against the oracle's, then 3 decode steps teacher-forced."""
-    if shape_name != "tiny" and n == 2500:
-        pytest.skip("the 2500-token case runs on the tiny model")
     shape = {"tiny": synth.SHAPES["tiny"], "gqa2": GQA2, "hk8": HK8}[shape_name]
     print(f"prefill {shape_name} {kv} start={start} n={n}", flush=True)
     blob = synth.make_blob(shape, seed=21)
