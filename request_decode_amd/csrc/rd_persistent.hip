@@ -796,19 +796,18 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             lds_barrier();   // q and the new row staged for the stream waves
             lds_barrier();   // every wave's partial stored
             if (t >= 0) {
-                AttnAcc<HD, G> acc;
-                attn_combine<HD, G, NWA>(s_r + NQ * 64, acc);
-                const int j = lane % LPR;
-                if (lane < LPR) {
+                // the waves' partials combined and published by all 64 lanes
+                // (HD / 64 dims each per head; the arithmetic of attn_combine)
+                const float* sa = s_r + NQ * 64;
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        uint64_t* dst = A.pb + ((size_t)(g * G + h) * A.S + s) * (HD + 2);
+                for (int h = 0; h < G; ++h) {
+                    const AttnWaves<HD, G, NWA> aw(sa, h);
+                    uint64_t* dst = A.pb + ((size_t)(g * G + h) * A.S + s) * (HD + 2);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) publish(&dst[j * 8 + i], acc.o[h][i], tag);
-                        if (lane == 0) {
-                            publish(&dst[HD], acc.m[h], tag);
-                            publish(&dst[HD + 1], acc.l[h], tag);
-                        }
+                    for (int k = 0; k < HD / 64; ++k) publish(&dst[k * 64 + lane], aw.o(sa, h, k * 64 + lane), tag);
+                    if (lane == 0) {
+                        publish(&dst[HD], aw.M, tag);
+                        publish(&dst[HD + 1], aw.L, tag);
                     }
                 }
                 TR(10 + TR_PUB);

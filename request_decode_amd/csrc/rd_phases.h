@@ -721,33 +721,45 @@ __device__ __forceinline__ void attn_part_store(float* s_att, int w, const AttnA
         }
     }
 }
+// Head h's wave weights f_w, its M and its L, and one output dim d: the
+// products are explicit FMAs in wave order from zero, so whichever lane
+// computes a value, and however many it computes, the bits are the same.
 template <int HD, int G, int NW>
-__device__ __forceinline__ void attn_combine(const float* s_att, AttnAcc<HD, G>& out) {
-    const int j = lane_id() % AttnGeo<HD>::LPR;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
+struct AttnWaves {
+    float f[NW], M, L;
+    __device__ __forceinline__ AttnWaves(const float* s_att, int h) {
+#pragma clang fp contract(off)
         float mw[NW];
-        float M = -INFINITY;
+        M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             mw[w] = s_att[(w * G + h) * (HD + 2) + HD];
             M = fmaxf(M, mw[w]);
         }
-        float L = 0.f, o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = 0.f;
+        L = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-            const float* d = s_att + (w * G + h) * (HD + 2);
-            const float f = mw[w] == -INFINITY ? 0.f : exp2_fast(mw[w] - M);
-            L += f * d[HD + 1];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] += f * d[j * 8 + i];
+            f[w] = mw[w] == -INFINITY ? 0.f : exp2_fast(mw[w] - M);
+            L = __builtin_fmaf(f[w], s_att[(w * G + h) * (HD + 2) + HD + 1], L);
         }
-        out.m[h] = M;
-        out.l[h] = L;
+    }
+    __device__ __forceinline__ float o(const float* s_att, int h, int d) const {
+        float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out.o[h][i] = o[i];
+        for (int w = 0; w < NW; ++w) v = __builtin_fmaf(f[w], s_att[(w * G + h) * (HD + 2) + d], v);
+        return v;
+    }
+};
+template <int HD, int G, int NW>
+__device__ __forceinline__ void attn_combine(const float* s_att, AttnAcc<HD, G>& out) {
+    const int j = lane_id() % AttnGeo<HD>::LPR;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const AttnWaves<HD, G, NW> aw(s_att, h);
+        out.m[h] = aw.M;
+        out.l[h] = aw.L;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out.o[h][i] = aw.o(s_att, h, j * 8 + i);
     }
 }
 
