@@ -135,6 +135,18 @@ __device__ __forceinline__ void lds_read_wait(u4v (&d)[N], const unsigned (&a)[N
 __device__ __forceinline__ void lds_write4(unsigned addr, float v) {
     asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
+// The O and down phases' inputs arrive chunk by chunk (stage_stream): the control
+// wave writes a chunk to LDS, waits for the write, then publishes the count
+// of staged chunks in s_flag; stream waves read the count before the chunk.
+__device__ __forceinline__ void post_count(int* s_flag, int n) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(lds_addr(s_flag)), "v"(n) : "memory");
+}
+__device__ __forceinline__ int read_count(const int* s_flag) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_addr(s_flag)) : "memory");
+    return __builtin_amdgcn_readfirstlane(v);
+}
+constexpr int COUNT_SPIN = 1 << 24;   // reads of the count before a stream wave goes on regardless
 
 __device__ __forceinline__ uint64_t tagged(float v, uint32_t tag) {
     return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
@@ -229,6 +241,54 @@ __device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int
             xr[c][2 * i] = h_bits2f((uint16_t)(u & 0xffffu));
             xr[c][2 * i + 1] = h_bits2f((uint16_t)(u >> 16));
         }
+}
+
+// poll_vec_h2 for the O and down phases, staging as it goes: after each round of
+// polls, the chunks complete in every lane are written to LDS in chunk order
+// (the layout of regs_to_lds) and their count posted (fl + chunks staged),
+// so the stream waves start on the first chunks while later ones are still
+// on their way.  A wait that gives up stages the rest as they stand.
+template <int KCH>
+__device__ __forceinline__ void stage_stream(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float* s,
+                                             int* s_flag, int fl) {
+    const int lane = lane_id();
+    const uint64_t done = (uint64_t)tag << 32;
+    auto pair = [&](int k) { return ((k / 4) * 64 + lane) * 4 + k % 4; };
+    uint64_t v[KCH * 4];
+#pragma unroll
+    for (int k = 0; k < KCH * 4; ++k) v[k] = 2 * pair(k) < K ? 0ull : done;
+    int staged = 0;
+    bool live = true;
+    wt.n = 0;
+    while (true) {
+#pragma unroll
+        for (int k = 0; k < KCH * 4; ++k)
+            if ((uint32_t)(v[k] >> 32) != tag) v[k] = ld_agent(word_at(buf, pair(k)));
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            if (c == staged) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ok &= (uint32_t)(v[c * 4 + i] >> 32) == tag;
+                if (__all(ok) || !live) {
+                    float xr[1][8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t u = (uint32_t)v[c * 4 + i];
+                        xr[0][2 * i] = h_bits2f((uint16_t)(u & 0xffffu));
+                        xr[0][2 * i + 1] = h_bits2f((uint16_t)(u >> 16));
+                    }
+                    u4v xh[1];
+                    pack_x<1>(xr, xh);
+                    reinterpret_cast<u4v*>(s)[c * 64 + lane] = xh[0];
+                    ++staged;
+                    post_count(s_flag, fl + staged);
+                }
+            }
+        }
+        if (staged == KCH || !live) break;
+        live = wt.again();
+    }
 }
 
 // The GEMV operand of a phase into LDS for the stream waves: the fp16
@@ -516,29 +576,99 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
     dot_rows<NR, KCH>(w, xh, out);
 }
 
+// consume_rows for the first rows of a phase whose input is staged chunk by
+// chunk (stage_stream): the rows' chunks are taken from the ring as in
+// consume_rows, then each chunk of the input is read once its count is
+// posted (fl: the count before this phase), into xh for the later rows, and
+// reduced at once.  The sums are dot_rows' in the same order.
+template <int NR, int KCH, bool FK, class F>
+__device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const PersistArgs& P,
+                                                  unsigned char* ring, const float* s_r, const int* s_flag, int fl,
+                                                  u4v (&xh)[KCH], int K, float (&out)[NR]) {
+    static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
+    const int lane = lane_id();
+    const unsigned base = lds_addr(ring) + (unsigned)lane * 16u;
+    unsigned ad[NR * KCH];
+    int s = f.slot;
+#pragma unroll
+    for (int i = 0; i < NR * KCH; ++i) {
+        ad[i] = base + (unsigned)s * UNIT;
+        s = s + 1 == RING ? 0 : s + 1;
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
+    u4v wl[NR * KCH];
+    lds_read_wait<NR * KCH>(wl, ad);   // slots read before they are refilled
+    f.template issue_n<NR * KCH>(A, P);
+    if constexpr (!FK) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+            if ((c * 64 + lane) * 8 >= K)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) wl[r * KCH + c] = u4v{0u, 0u, 0u, 0u};
+    }
+    const unsigned xb = lds_addr(s_r) + (unsigned)lane * 16u;
+    float s0[NR], s1[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) s0[r] = s1[r] = 0.f;
+    int have = 0;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        for (int it = 0; have <= c && it < COUNT_SPIN; ++it) have = read_count(s_flag) - fl;
+        {
+            const unsigned a1[1] = {xb + (unsigned)c * 1024u};
+            u4v x1[1];
+            lds_read_wait<1>(x1, a1);
+            xh[c] = x1[0];
+        }
+        u4v wc[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) wc[r] = wl[r * KCH + c];
+        dot_chunk<NR>(wc, xh[c], s0, s1);
+    }
+    dot_finish<NR>(s0, s1, out);
+}
+
 // A stream wave's share of GEMV phase ph, between the workgroup barriers
-// that bracket it: its rows' sums into s_part.
-template <int KCH, int KD, int KA, int KF, bool FK, class F, class Tail>
+// that bracket it: its rows' sums into s_part.  STRM: the input is staged
+// chunk by chunk (no barrier before the phase; s_flag, fl as in
+// consume_rows_strm).
+template <int KCH, int KD, int KA, int KF, bool FK, bool STRM = false, class F, class Tail>
 __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const PersistArgs& P, int sw,
                                              unsigned char* ring, const float* s_r, float* s_part, int ph,
-                                             StreamTracer& tr, Tail tail) {
+                                             StreamTracer& tr, Tail tail, const int* s_flag = nullptr,
+                                             int fl = 0) {
     constexpr int NR = KCH <= 4 ? 2 : 1;
-    lds_barrier();   // input staged
+    if constexpr (!STRM) lds_barrier();   // input staged
     const int kind = ph == 4 * A.n_layers ? 4 : (ph & 3);
     if (sw == 0) tr(100 + 10 * kind);
     const int K = kind == 1 ? A.H * A.hd : kind == 3 ? A.F : A.D;
     const int ra = pick5(f.ra, kind), rb = ra + pick5(f.nr, kind), r0 = pick5(f.r0, kind);
     if (ra < rb) {
         u4v xh[KCH];
-        {   // the fp16 operand from LDS (regs_to_lds), as asm (see lds_read_wait)
+        const unsigned sp = lds_addr(s_part);
+        int r = ra;
+        if constexpr (STRM) {   // the first rows as the input's chunks arrive
+            if (r + NR <= rb) {
+                float v[NR];
+                consume_rows_strm<NR, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v);
+                if (sw == 0) tr(101 + 10 * kind);
+                if (lane_id() == 0)
+#pragma unroll
+                    for (int k = 0; k < NR; ++k) lds_write4(sp + 4u * (unsigned)(r + k - r0), v[k]);
+                r += NR;
+            } else {
+                float v[1];
+                consume_rows_strm<1, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v);
+                if (lane_id() == 0) lds_write4(sp + 4u * (unsigned)(r - r0), v[0]);
+                r += 1;
+            }
+        } else {   // the fp16 operand from LDS (regs_to_lds), as asm (see lds_read_wait)
             const unsigned base = lds_addr(s_r) + (unsigned)lane_id() * 16u;
             unsigned ad[KCH];
 #pragma unroll
             for (int c = 0; c < KCH; ++c) ad[c] = base + (unsigned)c * 1024u;
             lds_read_wait<KCH>(xh, ad);
         }
-        const unsigned sp = lds_addr(s_part);
-        int r = ra;
         for (; r + NR <= rb; r += NR) {
             float v[NR];
             consume_rows<NR, KCH, FK>(f, A, P, sw, ring, xh, K, v);
@@ -647,13 +777,14 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
 
 template <int KD, int KA, int KF, int HD, int G, int KVF, bool FK>
 __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs& P, int sw, unsigned char* ring,
-                                            float* s_r, float* s_part, int* s_nev) {
+                                            float* s_r, float* s_part, const int* s_flag, int* s_nev) {
     const Tracer ct = make_tracer(P, s_nev);
     StreamTracer tr{sw == 0 ? ct.tb : nullptr, ct.cap, 0};
     Feeder<KD, KA, KF, FK> f;
     f.start(A, P, sw, ring);
     const int NL = A.n_layers;
     auto none = [] {};
+    int fl = 0;   // input chunks of the O and down phases posted so far
     for (int step = 0; step < P.n_steps; ++step) {
         const AttnSplit sp = attn_split<KVF>(A, P, step);
         for (int l = 0; l < NL; ++l) {
@@ -667,9 +798,11 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
                     });
             });
             attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, tr);
-            stream_phase<KA, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none);
+            stream_phase<KA, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none, s_flag, fl);
+            fl += KA;
             stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none);
-            stream_phase<KF, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none);
+            stream_phase<KF, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none, s_flag, fl);
+            fl += KF;
         }
         stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr, none);
     }
@@ -681,12 +814,13 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
 // ---- control wave ---------------------------------------------------------------------
 template <int KD, int KA, int KF, int HD, int G, int KVF, int SMAX>
 __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArgs& P, float* s_r,
-                                             const float* s_part, float* s_own, int* s_nev) {
+                                             const float* s_part, float* s_own, int* s_flag, int* s_nev) {
     using Geo = AttnGeo<HD>;
     constexpr int LPR = Geo::LPR;
     const int lane = lane_id(), NL = A.n_layers, b = blockIdx.x, nwg = gridDim.x;
     Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
     const Tracer TR = make_tracer(P, s_nev);
+    int fl = 0;   // input chunks of the O and down phases posted so far
     TR(99);
     auto check_token = [&](int t) {
         if (t < 0 || t >= A.V) {
@@ -850,13 +984,10 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 TR(20 + TR_PUB);
             }
             // ---------------- output projection + residual ----------------
-            {
-                float xr[KA][8];
-                poll_vec_h2<KA>(wt, A.ab, A.H * HD, tag, xr);
-                TR(30 + TR_RECV);
-                regs_to_lds<KA>(s_r, xr);
-            }
-            lds_barrier();
+            // (the input staged chunk by chunk, as for down)
+            stage_stream<KA>(wt, A.ab, A.H * HD, tag, s_r, s_flag, fl);
+            fl += KA;
+            TR(30 + TR_RECV);
             lds_barrier();
             TR(30 + TR_DONE);
             for (int q = lane; 2 * q < dr1 - dr0; q += WAVE) {   // (dr1 - dr0) even
@@ -885,13 +1016,11 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                                      silu_mul(s_part[4 * q + 2], s_part[4 * q + 3])), tag);
             TR(40 + TR_PUB);
             // ---------------- down projection + residual ----------------
-            {
-                float xr[KF][8];
-                poll_vec_h2<KF>(wt, A.mb, A.F, tag, xr);
-                TR(50 + TR_RECV);
-                regs_to_lds<KF>(s_r, xr);
-            }
-            lds_barrier();
+            // (the input staged chunk by chunk: the stream waves start on the
+            // chunks that have arrived, no barrier before the rows)
+            stage_stream<KF>(wt, A.mb, A.F, tag, s_r, s_flag, fl);
+            fl += KF;
+            TR(50 + TR_RECV);
             lds_barrier();
             TR(50 + TR_DONE);
             // This layer's cache rows are stored (acknowledged) before the
@@ -998,13 +1127,16 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
     __shared__ int s_nev[2];                                       // trace events: control, stream
+    __shared__ int s_flag;                                         // O and down input chunks posted
     const int wid = wave_id();
     if (threadIdx.x < 2) s_nev[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s_flag = 0;
     lds_barrier();
     if (wid == 0)
-        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, s_nev);
+        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, &s_flag, s_nev);
     else
-        stream_role<KD, KA, KF, HD, G, KVF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part, s_nev);
+        stream_role<KD, KA, KF, HD, G, KVF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part,
+                                                &s_flag, s_nev);
 }
 
 // ---- host side ------------------------------------------------------------------------

@@ -137,6 +137,32 @@ __device__ __forceinline__ void pack_x(const float (&xr)[KCH][8], u4v (&xh)[KCH]
         for (int i = 0; i < 4; ++i) xh[c][i] = pack_h2(xr[c][2 * i], xr[c][2 * i + 1]);
 }
 
+// One chunk of dot_rows: the chunk's two-term products into the two running
+// sums of each row.
+template <int NR>
+__device__ __forceinline__ void dot_chunk(const u4v (&w)[NR], const u4v xv, float (&s0)[NR], float (&s1)[NR]) {
+    const unsigned x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        // (vector elements go through plain locals before the bit casts)
+        const u4v wv = w[r];
+        const unsigned w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
+        s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), __builtin_bit_cast(h2, x0), s0[r], false);
+        s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), __builtin_bit_cast(h2, x1), s1[r], false);
+        s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), __builtin_bit_cast(h2, x2), s0[r], false);
+        s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), __builtin_bit_cast(h2, x3), s1[r], false);
+    }
+}
+// The row sums of dot_rows from the running sums.
+template <int NR>
+__device__ __forceinline__ void dot_finish(const float (&s0)[NR], const float (&s1)[NR], float (&out)[NR]) {
+    float v[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) v[r] = row16_sum(s0[r] + s1[r]);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+        out[r] = ((readlane_f(v[r], 0) + readlane_f(v[r], 16)) + readlane_f(v[r], 32)) + readlane_f(v[r], 48);
+}
 // out[r] = row r . x for NR loaded rows (columns past K already zero) and
 // the fp16 operand x, the same value in every lane.  Per lane: two running
 // fp32 sums over the chunks in order, each step a two-term fp16 dot product
@@ -150,24 +176,12 @@ __device__ __forceinline__ void dot_rows(const u4v (&w)[NR][KCH], const u4v (&xh
     for (int r = 0; r < NR; ++r) s0[r] = s1[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
+        u4v wc[NR];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            // (vector elements go through plain locals before the bit casts)
-            const u4v wv = w[r][c], xv = xh[c];
-            const unsigned w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
-            const unsigned x0 = xv.x, x1 = xv.y, x2 = xv.z, x3 = xv.w;
-            s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w0), __builtin_bit_cast(h2, x0), s0[r], false);
-            s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w1), __builtin_bit_cast(h2, x1), s1[r], false);
-            s0[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w2), __builtin_bit_cast(h2, x2), s0[r], false);
-            s1[r] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w3), __builtin_bit_cast(h2, x3), s1[r], false);
-        }
+        for (int r = 0; r < NR; ++r) wc[r] = w[r][c];
+        dot_chunk<NR>(wc, xh[c], s0, s1);
     }
-    float v[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) v[r] = row16_sum(s0[r] + s1[r]);
-#pragma unroll
-    for (int r = 0; r < NR; ++r)
-        out[r] = ((readlane_f(v[r], 0) + readlane_f(v[r], 16)) + readlane_f(v[r], 32)) + readlane_f(v[r], 48);
+    dot_finish<NR>(s0, s1, out);
 }
 
 // SwiGLU output m = silu(gate) * up, rounded to fp16 (nearest even): the
