@@ -291,6 +291,25 @@ __device__ __forceinline__ void stage_stream(Waiter& wt, const uint64_t* buf, in
     }
 }
 
+// A normalised operand (xr) into LDS chunk by chunk, each chunk's count
+// posted as soon as it is written (the RMSNorm phases: the norm needs the
+// whole vector, then the stream waves start on chunk 0 while the control
+// wave writes the rest).  The layout and values of regs_to_lds.
+template <int KCH>
+__device__ __forceinline__ void stage_chunks(float* s, const float (&xr)[KCH][8], int* s_flag, int fl) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        float x1[1][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x1[0][i] = xr[c][i];
+        u4v xh[1];
+        pack_x<1>(x1, xh);
+        reinterpret_cast<u4v*>(s)[c * 64 + lane] = xh[0];
+        post_count(s_flag, fl + c + 1);
+    }
+}
+
 // The GEMV operand of a phase into LDS for the stream waves: the fp16
 // rounding of the vector (pack_x), 16 bytes per lane and chunk at byte
 // (c*64 + lane)*16, zero past K.
@@ -784,23 +803,25 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
     f.start(A, P, sw, ring);
     const int NL = A.n_layers;
     auto none = [] {};
-    int fl = 0;   // input chunks of the O and down phases posted so far
+    int fl = 0;   // input chunks of the layers' GEMV phases posted so far
     for (int step = 0; step < P.n_steps; ++step) {
         const AttnSplit sp = attn_split<KVF>(A, P, step);
         for (int l = 0; l < NL; ++l) {
             const AttnArgs T = attn_args(A, l);
             KvBuf<KVF> kb[3];
             // after its QKV rows: the raw K/V rows of its first attention batch
-            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr, [&] {
+            stream_phase<KD, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l, tr, [&] {
                 if (sp.t >= 0)
                     with_src<HD, KVF, true>(T, sp.g, sp.pos, sp.open, [&](auto src) {
                         attn_wave_first<decltype(src), NWA>(src, sp.p0, sp.p1, sw, kb);
                     });
-            });
+            }, s_flag, fl);
+            fl += KD;
             attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, tr);
             stream_phase<KA, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none, s_flag, fl);
             fl += KA;
-            stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none);
+            stream_phase<KD, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none, s_flag, fl);
+            fl += KD;
             stream_phase<KF, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none, s_flag, fl);
             fl += KF;
         }
@@ -820,7 +841,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     const int lane = lane_id(), NL = A.n_layers, b = blockIdx.x, nwg = gridDim.x;
     Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
     const Tracer TR = make_tracer(P, s_nev);
-    int fl = 0;   // input chunks of the O and down phases posted so far
+    int fl = 0;   // input chunks of the layers' GEMV phases posted so far
     TR(99);
     auto check_token = [&](int t) {
         if (t < 0 || t >= A.V) {
@@ -865,7 +886,8 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 }
                 TR(0 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
-                regs_to_lds<KD>(s_r, xr);
+                stage_chunks<KD>(s_r, xr, s_flag, fl);
+                fl += KD;
             }
             TR(0 + TR_STAGED);
             // (cos, sin) of the RoPE pair each lane rotates in the epilogue,
@@ -873,8 +895,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // be spilled)
             // (every lane loads one: the column is in the row for any lane)
             const float2 cs_lane = rope[rope_col(HD, A.H, qr0 + 2 * lane)];
-            lds_barrier();
-            lds_barrier();
+            lds_barrier();   // row sums complete
             TR(0 + TR_DONE);
             // On the step that seals an INT8 segment the merge reads the open
             // segment, this step's row included: that row is stored before the
@@ -1004,10 +1025,10 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 poll_vec_h2<KD>(wt, A.xb2, A.D, tag, xr);
                 TR(40 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
-                regs_to_lds<KD>(s_r, xr);
+                stage_chunks<KD>(s_r, xr, s_flag, fl);
+                fl += KD;
             }
-            lds_barrier();
-            lds_barrier();
+            lds_barrier();   // row sums complete
             TR(40 + TR_DONE);
             // m[i], m[i+1] as one fp16 pair per word (gr0 % 4 == 0)
             for (int q = lane; 4 * q < gr1 - gr0; q += WAVE)
@@ -1127,7 +1148,7 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
     __shared__ int s_nev[2];                                       // trace events: control, stream
-    __shared__ int s_flag;                                         // O and down input chunks posted
+    __shared__ int s_flag;                                         // GEMV input chunks posted
     const int wid = wave_id();
     if (threadIdx.x < 2) s_nev[threadIdx.x] = 0;
     if (threadIdx.x == 0) s_flag = 0;
