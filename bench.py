@@ -147,13 +147,16 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
     seg = {k: [] for k in ("layer", "qkv", "att", "merge", "o", "gu", "down", "x_qkv", "x_att", "x_merge", "x_o",
                            "x_gu", "x_down", "att.start", "att.loop", "att.tail")}
     # inside each GEMV phase (stream wave 0's events 100 + 10 * kind + point:
-    # released, first rows reduced, all rows reduced; kinds 0 QKV, 1 O,
-    # 2 gate/up, 3 down): staging of the input, release of the stream waves,
-    # first rows, the rest of the rows, the control wave's epilogue
+    # phase entered, first rows reduced, all rows reduced; kinds 0 QKV, 1 O,
+    # 2 gate/up, 3 down).  The stream waves enter a phase before its input is
+    # there and reduce their first rows as its chunks are posted, so: the
+    # control wave's staging (QKV only), first rows reduced counted from the
+    # control wave's input received (negative: before the whole input was
+    # in), the rest of the rows, the control wave's epilogue
     ctrl = {"qkv": 0, "o": 30, "gu": 40, "down": 50}
     kind = {"qkv": 0, "o": 1, "gu": 2, "down": 3}
     for ph in ctrl:
-        for part in ("stage", "release", "first", "rows", "epilogue"):
+        for part in ("stage", "first", "rows", "epilogue", "barrier", "publish"):
             seg[f"{ph}.{part}"] = []
     for d in per:
         for l in range(2, 22):
@@ -171,13 +174,17 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
             for ph, c in ctrl.items():
                 k = 100 + 10 * kind[ph]
                 staged = g(c + 1) if g(c + 1) is not None else g(c)   # only QKV records its staging
-                ev = (g(c), staged, g(k), g(k + 1), g(k + 2), g(c + 2), g(c + 3))
+                ev = (g(c), staged, g(k + 1), g(k + 2), g(c + 3), g(c + 2))
                 if None not in ev:
                     seg[f"{ph}.stage"].append(ev[1] - ev[0])
-                    seg[f"{ph}.release"].append(ev[2] - ev[1])
-                    seg[f"{ph}.first"].append(ev[3] - ev[2])
-                    seg[f"{ph}.rows"].append(ev[4] - ev[3])
-                    seg[f"{ph}.epilogue"].append(ev[6] - ev[4])
+                    seg[f"{ph}.first"].append(ev[2] - ev[0])
+                    seg[f"{ph}.rows"].append(ev[3] - ev[2])
+                    seg[f"{ph}.epilogue"].append(ev[4] - ev[3])
+                    # the epilogue in two: until the row sums' barrier has
+                    # passed (the other stream waves' rows), then the
+                    # control wave's own work
+                    seg[f"{ph}.barrier"].append(ev[5] - ev[3])
+                    seg[f"{ph}.publish"].append(ev[4] - ev[5])
             if g(10) is not None and g(13) is not None:
                 seg["x_att"].append(g(10) - g(3))
                 seg["att"].append(g(13) - g(10))
