@@ -197,7 +197,30 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
                 seg["x_merge"].append(g(20) - (g(13) if g(13) is not None else g(3)))
                 seg["merge"].append(g(23) - g(20))
                 seg["x_o"].append(g(30) - g(23))
+    # Each exchange seen across workgroups (the clock is shared): how far the
+    # last producer's publish trails the median producer's ("skew"), and how
+    # long after the last publish the median consumer has its input ("after
+    # last"); per layer, then the median over layers.  (producer event,
+    # consumer event, consumer in the next layer)
+    xch = {"qkv>att": (3, 10, 0), "att>merge": (13, 20, 0), "merge>o": (23, 30, 0), "o>gu": (33, 40, 0),
+           "gu>down": (43, 50, 0), "down>qkv": (53, 0, 1)}
+    for name, (pe, ce, nxt) in xch.items():
+        sk, al = [], []
+        for l in range(2, 21):
+            prod = [d[(pe, l)] for d in per if (pe, l) in d]
+            cons = [d[(ce, l + nxt)] for d in per if (ce, l + nxt) in d]
+            if prod and cons:
+                last = max(prod)
+                sk.append(last - float(np.median(prod)))
+                al.append(float(np.median(cons)) - last)
+        if sk:
+            seg[f"skew.{name}"] = sk
+            seg[f"after_last.{name}"] = al
     med = {k: round(float(np.median(v)), 3) for k, v in seg.items() if v}
+    for k in ("qkv", "att", "merge", "o", "gu", "down"):   # spread of the phases' own time
+        if seg[k]:
+            med[f"p90.{k}"] = round(float(np.percentile(seg[k], 90)), 3)
+            med[f"max.{k}"] = round(float(np.max(seg[k])), 3)
     med["exchanges"] = round(sum(med.get(k, 0.0) for k in ("x_qkv", "x_att", "x_merge", "x_o", "x_gu", "x_down")), 3)
     med["workgroups"] = len(per)
     return med

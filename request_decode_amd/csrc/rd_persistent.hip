@@ -243,17 +243,23 @@ __device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int
         }
 }
 
-// poll_vec_h2 for the O and down phases, staging as it goes: after each round of
-// polls, the chunks complete in every lane are written to LDS in chunk order
-// (the layout of regs_to_lds) and their count posted (fl + chunks staged),
-// so the stream waves start on the first chunks while later ones are still
-// on their way.  A wait that gives up stages the rest as they stand.
+// The O and down phases' input (fp16 pairs, word w: elements 2w, 2w+1),
+// polled and staged as it goes: after each round of polls, the chunks
+// complete in every lane are written to LDS in chunk order (the layout of
+// regs_to_lds: LDS word j of a chunk holds its pair j) and their count posted
+// (fl + chunks staged), so the stream waves start on the first chunks while
+// later ones are still on their way.  No norm needs the elements in a lane's
+// registers here, so load i of chunk c reads the chunk's pairs i*64 + lane:
+// 512 contiguous bytes per load instruction, each line requested once per
+// round (four loads of one lane's four consecutive pairs would span 2 KB
+// each and request every line four times).  A wait that gives up stages the
+// rest as they stand.
 template <int KCH>
 __device__ __forceinline__ void stage_stream(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float* s,
                                              int* s_flag, int fl) {
     const int lane = lane_id();
     const uint64_t done = (uint64_t)tag << 32;
-    auto pair = [&](int k) { return ((k / 4) * 64 + lane) * 4 + k % 4; };
+    auto pair = [&](int k) { return (k / 4) * 256 + (k % 4) * 64 + lane; };
     uint64_t v[KCH * 4];
 #pragma unroll
     for (int k = 0; k < KCH * 4; ++k) v[k] = 2 * pair(k) < K ? 0ull : done;
@@ -271,16 +277,8 @@ __device__ __forceinline__ void stage_stream(Waiter& wt, const uint64_t* buf, in
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ok &= (uint32_t)(v[c * 4 + i] >> 32) == tag;
                 if (__all(ok) || !live) {
-                    float xr[1][8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const uint32_t u = (uint32_t)v[c * 4 + i];
-                        xr[0][2 * i] = h_bits2f((uint16_t)(u & 0xffffu));
-                        xr[0][2 * i + 1] = h_bits2f((uint16_t)(u >> 16));
-                    }
-                    u4v xh[1];
-                    pack_x<1>(xr, xh);
-                    reinterpret_cast<u4v*>(s)[c * 64 + lane] = xh[0];
+                    for (int i = 0; i < 4; ++i) reinterpret_cast<uint32_t*>(s)[pair(c * 4 + i)] = (uint32_t)v[c * 4 + i];
                     ++staged;
                     post_count(s_flag, fl + staged);
                 }
