@@ -210,37 +210,32 @@ __device__ __forceinline__ void poll_words(Waiter& wt, const uint64_t* buf, IDX&
     for (int k = 0; k < NW; ++k) val[k] = __uint_as_float((uint32_t)v[k]);
 }
 
-// Poll a K-element vector published in the GEMV input layout (lane l, chunk
-// c: elements (c*64+l)*8..+7) into registers, in one round trip.
+// Poll a K-element vector published as fp16 pairs (word w: elements 2w,
+// 2w+1) into the GEMV input layout in registers (lane l, chunk c: elements
+// (c*64+l)*8..+7), which the RMSNorm sums in.  The poll loads read whole
+// lines (as stage_stream: load i of chunk c reads the chunk's words
+// i*64 + lane), and the words reach the lane layout through LDS (s, whose
+// chunks the caller has not posted yet).
 template <int KCH>
-__device__ __forceinline__ void poll_vec(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float (&xr)[KCH][8]) {
-    const int lane = lane_id();
-    float val[KCH * 8];
-    auto col = [&](int k) { return ((k / 8) * 64 + lane) * 8 + k % 8; };
-    poll_words<KCH * 8>(wt, buf, col, [&](int k) { return col(k) < K; }, tag, val);
-#pragma unroll
-    for (int c = 0; c < KCH; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xr[c][i] = val[c * 8 + i];
-}
-
-// The same for a vector published as fp16 pairs (word w: elements 2w, 2w+1):
-// the lane's 8 elements of chunk c are 4 consecutive words.
-template <int KCH>
-__device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int K, uint32_t tag,
-                                            float (&xr)[KCH][8]) {
+__device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float* s,
+                                                float (&xr)[KCH][8]) {
     const int lane = lane_id();
     float val[KCH * 4];
-    auto word = [&](int k) { return ((k / 4) * 64 + lane) * 4 + k % 4; };
+    auto word = [&](int k) { return (k / 4) * 256 + (k % 4) * 64 + lane; };
     poll_words<KCH * 4>(wt, buf, word, [&](int k) { return 2 * word(k) < K; }, tag, val);
+    uint32_t* sw = reinterpret_cast<uint32_t*>(s);
 #pragma unroll
-    for (int c = 0; c < KCH; ++c)
+    for (int k = 0; k < KCH * 4; ++k) sw[word(k)] = __float_as_uint(val[k]);
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+        const u4v w = reinterpret_cast<const u4v*>(s)[c * 64 + lane];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t u = __float_as_uint(val[c * 4 + i]);
-            xr[c][2 * i] = h_bits2f((uint16_t)(u & 0xffffu));
-            xr[c][2 * i + 1] = h_bits2f((uint16_t)(u >> 16));
+            xr[c][2 * i] = h_bits2f((uint16_t)(u[i] & 0xffffu));
+            xr[c][2 * i + 1] = h_bits2f((uint16_t)(u[i] >> 16));
         }
+    }
 }
 
 // The O and down phases' input (fp16 pairs, word w: elements 2w, 2w+1),
@@ -880,7 +875,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                     load_x_f16<KD>(e, A.D, xr);
                     for (int i = lane; i < dr1 - dr0; i += WAVE) s_own[i] = (float)e[dr0 + i];
                 } else {
-                    poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, l - 1), xr);
+                    poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, l - 1), s_r, xr);
                 }
                 TR(0 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
@@ -1020,7 +1015,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // ---------------- RMSNorm + gate/up + SwiGLU ----------------
             {
                 float xr[KD][8];
-                poll_vec_h2<KD>(wt, A.xb2, A.D, tag, xr);
+                poll_vec_h2<KD>(wt, A.xb2, A.D, tag, s_r, xr);
                 TR(40 + TR_RECV);
                 rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
                 stage_chunks<KD>(s_r, xr, s_flag, fl);
@@ -1057,7 +1052,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
         // ---------------- final RMSNorm + LM head + argmax ----------------
         {
             float xr[KD][8];
-            poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), xr);
+            poll_vec_h2<KD>(wt, A.xb1, A.D, tag_of(A, P, step, NL - 1), s_r, xr);
             TR(60 + TR_RECV);
             rmsnorm_gain<KD>(xr, gain, A.D, A.eps);
             regs_to_lds<KD>(s_r, xr);
