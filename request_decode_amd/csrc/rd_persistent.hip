@@ -592,11 +592,12 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
 // chunk (stage_stream): the rows' chunks are taken from the ring as in
 // consume_rows, then each chunk of the input is read once its count is
 // posted (fl: the count before this phase), into xh for the later rows, and
-// reduced at once.  The sums are dot_rows' in the same order.
+// reduced at once.  The slots are refilled at once, or (late) once chunk 0
+// is posted.  The sums are dot_rows' in the same order.
 template <int NR, int KCH, bool FK, class F>
 __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const PersistArgs& P,
                                                   unsigned char* ring, const float* s_r, const int* s_flag, int fl,
-                                                  u4v (&xh)[KCH], int K, float (&out)[NR]) {
+                                                  u4v (&xh)[KCH], int K, float (&out)[NR], bool late) {
     static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
     const int lane = lane_id();
     const unsigned base = lds_addr(ring) + (unsigned)lane * 16u;
@@ -610,7 +611,7 @@ __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
     u4v wl[NR * KCH];
     lds_read_wait<NR * KCH>(wl, ad);   // slots read before they are refilled
-    f.template issue_n<NR * KCH>(A, P);
+    if (!late) f.template issue_n<NR * KCH>(A, P);
     if constexpr (!FK) {
 #pragma unroll
         for (int c = 0; c < KCH; ++c)
@@ -626,6 +627,7 @@ __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
         for (int it = 0; have <= c && it < COUNT_SPIN; ++it) have = read_count(s_flag) - fl;
+        if (c == 0 && late) f.template issue_n<NR * KCH>(A, P);
         {
             const unsigned a1[1] = {xb + (unsigned)c * 1024u};
             u4v x1[1];
@@ -655,6 +657,13 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
     if (sw == 0) tr(100 + 10 * kind);
     const int K = kind == 1 ? A.H * A.hd : kind == 3 ? A.F : A.D;
     const int ra = pick5(f.ra, kind), rb = ra + pick5(f.nr, kind), r0 = pick5(f.r0, kind);
+    // QKV and gate/up (inputs normalised by the control wave): the first
+    // rows' slots are refilled once chunk 0 is posted.  At phase entry the
+    // control wave is publishing the previous phase's output, and those
+    // stores would queue behind the refills in the CU's memory path; by
+    // chunk 0 its poll is over.  O and down refill at entry: their chunk 0
+    // arrives while the control wave still polls the rest.
+    const bool late = kind == 0 || kind == 2;
     if (ra < rb) {
         u4v xh[KCH];
         const unsigned sp = lds_addr(s_part);
@@ -662,7 +671,7 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
         if constexpr (STRM) {   // the first rows as the input's chunks arrive
             if (r + NR <= rb) {
                 float v[NR];
-                consume_rows_strm<NR, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v);
+                consume_rows_strm<NR, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late);
                 if (sw == 0) tr(101 + 10 * kind);
                 if (lane_id() == 0)
 #pragma unroll
@@ -670,7 +679,7 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
                 r += NR;
             } else {
                 float v[1];
-                consume_rows_strm<1, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v);
+                consume_rows_strm<1, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late);
                 if (lane_id() == 0) lds_write4(sp + 4u * (unsigned)(r - r0), v[0]);
                 r += 1;
             }
