@@ -927,28 +927,30 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // ---------------- attention split (all waves) ----------------
             constexpr int NQ = attn_nq<HD, G>();
             if (t >= 0) {
-                const int lane = lane_id(), j = lane % LPR, slot = lane / LPR;
+                const int lane = lane_id();
                 const bool has_new = p1 == L;
-                float val[NQ];
-#pragma unroll
-                for (int k = 0; k < NQ; ++k) val[k] = 0.f;
-                // q of the group's heads, then the new K and V rows of kv-head g
-                auto qidx = [&](int k) {
-                    return k < G * 8 ? (g * G + k / 8) * HD + j * 8 + k % 8
-                                     : Nq + (k - G * 8) / 8 * Nk + g * HD + j * 8 + k % 8;
+                // q of the group's heads, then the new K and V rows of kv-head
+                // g: (G + 2) * HD words, polled by all 64 lanes with 512
+                // contiguous bytes per load (word w: q head w / HD, or K, V)
+                constexpr int NWL = (G + 2) * HD / 64;
+                static_assert((G + 2) * HD % 64 == 0, "q, K and V words in whole loads");
+                auto widx = [&](int i) {
+                    const int w = i * 64 + lane;
+                    return w < G * HD ? g * G * HD + w : Nq + (w / HD - G) * Nk + g * HD + w % HD;
                 };
-                // the lanes of slot 0 poll; the other slots take their copy (same dims)
-                poll_words<NQ>(wt, A.qb, qidx, [&](int k) { return slot == 0 && (k < G * 8 || has_new); }, tag, val);
-                if constexpr (LPR == 16) {   // slot 0 is row 0
-#pragma unroll
-                    for (int k = 0; k < NQ; ++k) val[k] = row0_bcast(val[k]);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < NQ; ++k) val[k] = __shfl(val[k], j, WAVE);
-                }
+                float wv[NWL];
+                poll_words<NWL>(wt, A.qb, widx, [&](int i) { return i * 64 + lane < G * HD || has_new; }, tag, wv);
                 TR(10 + TR_RECV);
+                // to the stream waves' layout: value k of lane (slot, j) at
+                // s_r[k * 64 + slot * LPR + j] is dim j * 8 + k % 8 of vector
+                // k / 8 (the G q heads, then K, V), the same for every slot
 #pragma unroll
-                for (int k = 0; k < NQ; ++k) s_r[k * 64 + lane] = val[k];
+                for (int i = 0; i < NWL; ++i) {
+                    const int w = i * 64 + lane, d = w % HD;
+                    const int k = (w / HD) * 8 + d % 8, jj = d / 8;
+#pragma unroll
+                    for (int sl = 0; sl < 64 / LPR; ++sl) s_r[k * 64 + sl * LPR + jj] = wv[i];
+                }
             }
             lds_barrier();   // q and the new row staged for the stream waves
             lds_barrier();   // every wave's partial stored
