@@ -197,6 +197,17 @@ def layer_trace(m, token: int, reps: int, rewind: bool = True):
                 seg["x_merge"].append(g(20) - (g(13) if g(13) is not None else g(3)))
                 seg["merge"].append(g(23) - g(20))
                 seg["x_o"].append(g(30) - g(23))
+    # The step's tail: the final RMSNorm's input wait (after layer NL-1's down
+    # publish), the LM head phase (input received -> row sums complete), the
+    # argmax exchange (-> next token in hand)
+    nl = max((k[1] for d in per for k in d if k[0] == 53), default=-1)
+    lm = {"lm.wait": [], "lm.rows": [], "lm.argmax": []}
+    for d in per:
+        if None not in (d.get((53, nl)), d.get((60, 0)), d.get((62, 0)), d.get((63, 0))):
+            lm["lm.wait"].append(d[(60, 0)] - d[(53, nl)])
+            lm["lm.rows"].append(d[(62, 0)] - d[(60, 0)])
+            lm["lm.argmax"].append(d[(63, 0)] - d[(62, 0)])
+    seg.update({k: v for k, v in lm.items() if v})
     # Each exchange seen across workgroups (the clock is shared): how far the
     # last producer's publish trails the median producer's ("skew"), and how
     # long after the last publish the median consumer has its input ("after
