@@ -765,16 +765,19 @@ __device__ __forceinline__ void attn_stream(const AttnArgs& T, const StepArgs& A
     lds_barrier();   // q and the new row staged
     if (w == 0) tr(140);
     if (sp.t >= 0) {
-        const int lane = lane_id();
+        // (value k of the lane's 8 dims at s_r[k * LPR + j]: the lanes of
+        // every slot read the same words, an LDS broadcast)
+        constexpr int LPR = AttnGeo<HD>::LPR;
+        const int j = lane_id() % LPR;
         float qv[G][8], kn[8], vn[8];
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qv[h][i] = s_r[(h * 8 + i) * 64 + lane] * (A.scale * LOG2E);
+            for (int i = 0; i < 8; ++i) qv[h][i] = s_r[(h * 8 + i) * LPR + j] * (A.scale * LOG2E);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            kn[i] = s_r[(G * 8 + i) * 64 + lane];
-            vn[i] = s_r[(G * 8 + 8 + i) * 64 + lane];
+            kn[i] = s_r[(G * 8 + i) * LPR + j];
+            vn[i] = s_r[(G * 8 + 8 + i) * LPR + j];
         }
         AttnAcc<HD, G> acc;
         acc.clear();
@@ -941,15 +944,13 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 float wv[NWL];
                 poll_words<NWL>(wt, A.qb, widx, [&](int i) { return i * 64 + lane < G * HD || has_new; }, tag, wv);
                 TR(10 + TR_RECV);
-                // to the stream waves' layout: value k of lane (slot, j) at
-                // s_r[k * 64 + slot * LPR + j] is dim j * 8 + k % 8 of vector
-                // k / 8 (the G q heads, then K, V), the same for every slot
+                // to the stream waves' layout: value k of lane j of a slot at
+                // s_r[k * LPR + j] is dim j * 8 + k % 8 of vector k / 8 (the G
+                // q heads, then K, V); every slot reads the same words
 #pragma unroll
                 for (int i = 0; i < NWL; ++i) {
                     const int w = i * 64 + lane, d = w % HD;
-                    const int k = (w / HD) * 8 + d % 8, jj = d / 8;
-#pragma unroll
-                    for (int sl = 0; sl < 64 / LPR; ++sl) s_r[k * 64 + sl * LPR + jj] = wv[i];
+                    s_r[((w / HD) * 8 + d % 8) * LPR + d / 8] = wv[i];
                 }
             }
             lds_barrier();   // q and the new row staged for the stream waves
