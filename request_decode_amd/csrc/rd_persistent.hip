@@ -212,20 +212,34 @@ __device__ __forceinline__ void poll_words(Waiter& wt, const uint64_t* buf, IDX&
 
 // Poll a K-element vector published as fp16 pairs (word w: elements 2w,
 // 2w+1) into the GEMV input layout in registers (lane l, chunk c: elements
-// (c*64+l)*8..+7), which the RMSNorm sums in.  The poll loads read whole
-// lines (as stage_stream: load i of chunk c reads the chunk's words
-// i*64 + lane), and the words reach the lane layout through LDS (s, whose
-// chunks the caller has not posted yet).
+// (c*64+l)*8..+7), which the RMSNorm sums in.  The poll loads read 16
+// bytes per lane and whole lines (as stage_stream16: load i of chunk c reads
+// the chunk's words i*128 + 2*lane, +1, each word checked for its own tag),
+// and the words reach the lane layout through LDS (s, whose chunks the
+// caller has not posted yet).
 template <int KCH>
 __device__ __forceinline__ void poll_vec_h2(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float* s,
-                                                float (&xr)[KCH][8]) {
+                                               float (&xr)[KCH][8]) {
     const int lane = lane_id();
-    float val[KCH * 4];
-    auto word = [&](int k) { return (k / 4) * 256 + (k % 4) * 64 + lane; };
-    poll_words<KCH * 4>(wt, buf, word, [&](int k) { return 2 * word(k) < K; }, tag, val);
-    uint32_t* sw = reinterpret_cast<uint32_t*>(s);
+    const __amdgpu_buffer_rsrc_t rs = attn_rsrc(buf, (size_t)K * 4);
+    auto pair = [&](int k) { return (k / 2) * 256 + (k % 2) * 128 + 2 * lane; };
+    u4v v[KCH * 2];
 #pragma unroll
-    for (int k = 0; k < KCH * 4; ++k) sw[word(k)] = __float_as_uint(val[k]);
+    for (int k = 0; k < KCH * 2; ++k) v[k] = 2 * pair(k) < K ? u4v{0u, 0u, 0u, 0u} : u4v{0u, tag, 0u, tag};
+    wt.n = 0;
+    while (true) {
+#pragma unroll
+        for (int k = 0; k < KCH * 2; ++k)
+            if (v[k].y != tag || v[k].w != tag)
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)pair(k) * 8u, 0, AUX_AGENT);
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < KCH * 2; ++k) all &= v[k].y == tag && v[k].w == tag;
+        if (__all(all)) break;
+        if (!wt.again()) break;
+    }
+#pragma unroll
+    for (int k = 0; k < KCH * 2; ++k) reinterpret_cast<u2v*>(s)[pair(k) / 2] = u2v{v[k].x, v[k].z};
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
         const u4v w = reinterpret_cast<const u4v*>(s)[c * 64 + lane];
@@ -274,6 +288,51 @@ __device__ __forceinline__ void stage_stream(Waiter& wt, const uint64_t* buf, in
                 if (__all(ok) || !live) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) reinterpret_cast<uint32_t*>(s)[pair(c * 4 + i)] = (uint32_t)v[c * 4 + i];
+                    ++staged;
+                    post_count(s_flag, fl + staged);
+                }
+            }
+        }
+        if (staged == KCH || !live) break;
+        live = wt.again();
+    }
+}
+
+// stage_stream with 16-byte poll loads: lane l's load i of chunk c reads the
+// chunk's words i*128 + 2l, +1 (1 KiB contiguous per load instruction, half
+// the instructions per round).  Each 8-byte word was written by one 64-bit
+// store and carries its own tag, so each is checked on its own.  A poll
+// round waits for all of its loads, and each load instruction queues in the
+// CU's memory path behind the weight refills: for the down input (d_ff
+// elements, 44 eight-byte loads per lane) fewer instructions shorten the
+// round.  (agent-coherent buffer loads, as the attention's.)
+template <int KCH>
+__device__ __forceinline__ void stage_stream16(Waiter& wt, const uint64_t* buf, int K, uint32_t tag, float* s,
+                                               int* s_flag, int fl) {
+    const int lane = lane_id();
+    const __amdgpu_buffer_rsrc_t rs = attn_rsrc(buf, (size_t)K * 4);
+    auto pair = [&](int k) { return (k / 2) * 256 + (k % 2) * 128 + 2 * lane; };
+    u4v v[KCH * 2];
+#pragma unroll
+    for (int k = 0; k < KCH * 2; ++k) v[k] = 2 * pair(k) < K ? u4v{0u, 0u, 0u, 0u} : u4v{0u, tag, 0u, tag};
+    int staged = 0;
+    bool live = true;
+    wt.n = 0;
+    while (true) {
+#pragma unroll
+        for (int k = 0; k < KCH * 2; ++k)
+            if (v[k].y != tag || v[k].w != tag)
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)pair(k) * 8u, 0, AUX_AGENT);
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) {
+            if (c == staged) {
+                bool ok = true;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) ok &= v[c * 2 + i].y == tag && v[c * 2 + i].w == tag;
+                if (__all(ok) || !live) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        reinterpret_cast<u2v*>(s)[pair(c * 2 + i) / 2] = u2v{v[c * 2 + i].x, v[c * 2 + i].z};
                     ++staged;
                     post_count(s_flag, fl + staged);
                 }
@@ -1044,7 +1103,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
             // ---------------- down projection + residual ----------------
             // (the input staged chunk by chunk: the stream waves start on the
             // chunks that have arrived, no barrier before the rows)
-            stage_stream<KF>(wt, A.mb, A.F, tag, s_r, s_flag, fl);
+            stage_stream16<KF>(wt, A.mb, A.F, tag, s_r, s_flag, fl);
             fl += KF;
             TR(50 + TR_RECV);
             lds_barrier();
