@@ -992,24 +992,57 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 const int lane = lane_id();
                 const bool has_new = p1 == L;
                 // q of the group's heads, then the new K and V rows of kv-head
-                // g: (G + 2) * HD words, polled by all 64 lanes with 512
-                // contiguous bytes per load (word w: q head w / HD, or K, V)
+                // g: (G + 2) * HD words (word w: q head w / HD, or K, V), polled
+                // by all 64 lanes with contiguous loads: 16 bytes per lane (load
+                // i: words i*128 + 2*lane, +1, each with its own tag) where the
+                // words fill whole loads, else 8 (load i: word i*64 + lane)
                 constexpr int NWL = (G + 2) * HD / 64;
                 static_assert((G + 2) * HD % 64 == 0, "q, K and V words in whole loads");
-                auto widx = [&](int i) {
-                    const int w = i * 64 + lane;
+                auto waddr = [&](int w) {
                     return w < G * HD ? g * G * HD + w : Nq + (w / HD - G) * Nk + g * HD + w % HD;
                 };
-                float wv[NWL];
-                poll_words<NWL>(wt, A.qb, widx, [&](int i) { return i * 64 + lane < G * HD || has_new; }, tag, wv);
-                TR(10 + TR_RECV);
+                auto widx = [&](int i) { return waddr(i * 64 + lane); };
+                auto widx2 = [&](int i) { return waddr(i * 128 + 2 * lane); };
                 // to the stream waves' layout: value k of lane j of a slot at
                 // s_r[k * LPR + j] is dim j * 8 + k % 8 of vector k / 8 (the G
                 // q heads, then K, V); every slot reads the same words
+                if constexpr ((G + 2) * HD % 128 == 0) {
+                    constexpr int NL2 = NWL / 2;
+                    const __amdgpu_buffer_rsrc_t rs = attn_rsrc(A.qb, (size_t)(Nq + 2 * Nk) * 8);
+                    u4v v2[NL2];
 #pragma unroll
-                for (int i = 0; i < NWL; ++i) {
-                    const int w = i * 64 + lane, d = w % HD;
-                    s_r[((w / HD) * 8 + d % 8) * LPR + d / 8] = wv[i];
+                    for (int i = 0; i < NL2; ++i)
+                        v2[i] = i * 128 + 2 * lane < G * HD || has_new ? u4v{0u, 0u, 0u, 0u} : u4v{0u, tag, 0u, tag};
+                    wt.n = 0;
+                    while (true) {
+#pragma unroll
+                        for (int i = 0; i < NL2; ++i)
+                            if (v2[i].y != tag || v2[i].w != tag)
+                                v2[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (unsigned)widx2(i) * 8u, 0, AUX_AGENT);
+                        bool all = true;
+#pragma unroll
+                        for (int i = 0; i < NL2; ++i) all &= v2[i].y == tag && v2[i].w == tag;
+                        if (__all(all)) break;
+                        if (!wt.again()) break;
+                    }
+                    TR(10 + TR_RECV);
+#pragma unroll
+                    for (int i = 0; i < NL2; ++i)
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int w = i * 128 + 2 * lane + e, d = w % HD;
+                            s_r[((w / HD) * 8 + d % 8) * LPR + d / 8] = __uint_as_float(e ? v2[i].z : v2[i].x);
+                        }
+                } else {
+                    float wv[NWL];
+                    poll_words<NWL>(wt, A.qb, widx, [&](int i) { return i * 64 + lane < G * HD || has_new; }, tag,
+                                    wv);
+                    TR(10 + TR_RECV);
+#pragma unroll
+                    for (int i = 0; i < NWL; ++i) {
+                        const int w = i * 64 + lane, d = w % HD;
+                        s_r[((w / HD) * 8 + d % 8) * LPR + d / 8] = wv[i];
+                    }
                 }
             }
             lds_barrier();   // q and the new row staged for the stream waves
