@@ -55,6 +55,8 @@ def lib():
         L.orc_seg_dequant.restype = C.c_float
         L.orc_seg_dequant.argtypes = [C.c_uint8, C.c_float, C.c_float]
         L.orc_seg_dequant_n.argtypes = [u8p, C.c_size_t, C.c_float, C.c_float, fp]
+        L.orc_delta_seal.argtypes = [u16p, C.c_int, C.c_int, u16p, u8p, fp, fp]
+        L.orc_delta_restore.argtypes = [u16p, u8p, C.c_int, C.c_int, C.c_float, C.c_float, fp]
         L.orc_q4_quant.argtypes = [u16p, C.c_int, C.c_int, u8p, fp]
         L.orc_q4_dequant.argtypes = [u8p, fp, C.c_int, C.c_int, u16p]
         L.orc_q4_code.restype = C.c_int
@@ -139,6 +141,32 @@ def seg_quant(h: np.ndarray):
     s, z = C.c_float(), C.c_float()
     lib().orc_seg_quant(_p(h, C.c_uint16), h.size, _p(codes, C.c_uint8), C.byref(s), C.byref(z))
     return codes, np.float32(s.value), np.float32(z.value)
+
+
+def delta_seal(x: np.ndarray):
+    """Delta quantization of one segment (orc_delta_seal): binary16 bits
+    [n, hd] -> (anchor uint16 [hd], codes uint8 [n-1, hd], float32 scale,
+    float32 zp)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n, hd = x.shape
+    anchor = np.empty(hd, np.uint16)
+    codes = np.empty((max(n - 1, 0), hd), np.uint8)
+    s, z = C.c_float(), C.c_float()
+    lib().orc_delta_seal(_p(x, C.c_uint16), n, hd, _p(anchor, C.c_uint16), _p(codes, C.c_uint8), C.byref(s),
+                         C.byref(z))
+    return anchor, codes, np.float32(s.value), np.float32(z.value)
+
+
+def delta_restore(anchor: np.ndarray, codes: np.ndarray, scale, zp) -> np.ndarray:
+    """The segment's rows restored from a delta seal (orc_delta_restore):
+    float32 [n, hd]."""
+    a = np.ascontiguousarray(anchor, dtype=np.uint16)
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    hd = a.size
+    n = c.shape[0] + 1
+    y = np.empty((n, hd), np.float32)
+    lib().orc_delta_restore(_p(a, C.c_uint16), _p(c, C.c_uint8), n, hd, float(scale), float(zp), _p(y, C.c_float))
+    return y
 
 
 def seg_dequant(codes: np.ndarray, scale, zp) -> np.ndarray:

@@ -153,6 +153,60 @@ void orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale_out, f
 
 float orc_seg_dequant(uint8_t code, float scale, float zp) { return ((float)code - zp) * scale; }
 
+/* ------------------------------------------------------------------------ */
+/* Delta quantization ("Grok-3 v3.2.4 hot update deep dive", §3.2: the       */
+/* scheme before the adaptive-range one stores the difference between       */
+/* adjacent tokens' K/V values instead of the values, then quantizes the     */
+/* differences to INT8).  Reading taken where the page is silent: a segment  */
+/* of n rows of hd fp16 values keeps its first row as it is (the anchor);    */
+/* the differences d[p][j] = x[p][j] - x[p-1][j] (p = 1..n-1) of the exact   */
+/* values are taken in binary32 and quantized together as one segment with   */
+/* the adaptive-range quantizer of the same section (orc_seg_quant's         */
+/* formula, on binary32 inputs); a row is restored by adding the             */
+/* dequantized differences in row order, so quantization errors add up      */
+/* along the segment.  Binary32 throughout.                                 */
+
+void orc_delta_seal(const uint16_t* x, int n, int hd, uint16_t* anchor, uint8_t* codes, float* scale_out,
+                    float* zp_out) {
+    for (int j = 0; j < hd; ++j) anchor[j] = x[j];
+    const int m = (n - 1) * hd;
+    if (m <= 0) {   /* one row: no differences */
+        *scale_out = 1.0f;
+        *zp_out = 0.0f;
+        return;
+    }
+    float mn = INFINITY, mx = -INFINITY;
+    for (int p = 1; p < n; ++p)
+        for (int j = 0; j < hd; ++j) {
+            float d = (float)orc_h2d(x[p * hd + j]) - (float)orc_h2d(x[(p - 1) * hd + j]);
+            if (d < mn) mn = d;
+            if (d > mx) mx = d;
+        }
+    float scale = (mx - mn) / 255.0f;
+    if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;   /* as orc_seg_quant */
+    float zp = rintf(-mn / scale);
+    for (int p = 1; p < n; ++p)
+        for (int j = 0; j < hd; ++j) {
+            float d = (float)orc_h2d(x[p * hd + j]) - (float)orc_h2d(x[(p - 1) * hd + j]);
+            float q = rintf(d / scale) + zp;
+            if (q < 0.0f) q = 0.0f;
+            if (q > 255.0f) q = 255.0f;
+            codes[(p - 1) * hd + j] = (uint8_t)q;
+        }
+    *scale_out = scale;
+    *zp_out = zp;
+}
+
+void orc_delta_restore(const uint16_t* anchor, const uint8_t* codes, int n, int hd, float scale, float zp,
+                       float* y) {
+    for (int j = 0; j < hd; ++j) y[j] = (float)orc_h2d(anchor[j]);
+    for (int p = 1; p < n; ++p)
+        for (int j = 0; j < hd; ++j) {
+            float t = ((float)codes[(p - 1) * hd + j] - zp) * scale;
+            y[p * hd + j] = y[(p - 1) * hd + j] + t;
+        }
+}
+
 void orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, float* out) {
     for (size_t i = 0; i < n; ++i) out[i] = orc_seg_dequant(codes[i], scale, zp);
 }

@@ -46,6 +46,8 @@ void orc_h_from_e5m2_n(const uint8_t* e, size_t n, uint16_t* out);
  * All in binary32.  Degenerate max==min uses scale |min| (1 when the
  * segment is all zeros), which reproduces the constant exactly. */
 void  orc_seg_quant(const uint16_t* x, int n, uint8_t* codes, float* scale, float* zp);
+void  orc_delta_seal(const uint16_t* x, int n, int hd, uint16_t* anchor, uint8_t* codes, float* scale, float* zp);
+void  orc_delta_restore(const uint16_t* anchor, const uint8_t* codes, int n, int hd, float scale, float zp, float* y);
 float orc_seg_dequant(uint8_t code, float scale, float zp);
 void  orc_seg_dequant_n(const uint8_t* codes, size_t n, float scale, float zp, float* out);
 
