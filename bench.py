@@ -321,6 +321,68 @@ def gemv_microbench(rd, torch, stream, iters: int = 3):
     return out
 
 
+DELTA_SEGS = 24 * 2 * 8 * 64   # K and V segments of the 2B cache at 8192 keys: layers x 2 x kv heads x 64
+
+
+def delta_kv_bench(rd, torch, stream, iters: int = 5):
+    """Delta quantization of K/V segments (rd_delta_seal, rd_delta_restore)
+    over the K and V segments of the whole 2B cache at 8192 keys: 24576
+    segments of 128 rows x 128 fp16 values, seeded random walks along the
+    rows drawn on the device.  Each kernel timed over `iters` launches
+    between HIP events on the bench stream; algorithmic bytes: seal reads
+    the rows and writes anchor, codes and (scale, zp); restore reads those
+    and writes the rows in fp32."""
+    n_seg, n, hd = DELTA_SEGS, 128, 128
+    g = torch.Generator(device="cuda").manual_seed(17)
+    with torch.cuda.stream(stream):
+        x = torch.randn((n_seg, 1, hd), generator=g, device="cuda")
+        x = (x + torch.cumsum(0.05 * torch.randn((n_seg, n, hd), generator=g, device="cuda"), dim=1)).half()
+        anchor = torch.empty((n_seg, hd), dtype=torch.int16, device="cuda")
+        codes = torch.empty((n_seg, n - 1, hd), dtype=torch.uint8, device="cuda")
+        meta = torch.empty((n_seg, 2), dtype=torch.float32, device="cuda")
+        out = torch.empty((n_seg, n, hd), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    s = stream.cuda_stream
+    seal = lambda: rd.rd_delta_seal(x.data_ptr(), n_seg, n, hd, anchor.data_ptr(), codes.data_ptr(), meta.data_ptr(), s)
+    restore = lambda: rd.rd_delta_restore(anchor.data_ptr(), codes.data_ptr(), meta.data_ptr(), n_seg, n, hd,
+                                          out.data_ptr(), s)
+    sealed = hd * 2 + (n - 1) * hd + 8
+    res = {"segments": n_seg, "rows": n, "head_dim": hd}
+    for name, f, nbytes in (("seal", seal, n_seg * (n * hd * 2 + sealed)), ("restore", restore, n_seg * (sealed + n * hd * 4))):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        gbps = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 1), "bytes": nbytes, "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        print(f"[bench] delta {name}: {n_seg} segments, {us:.1f} us, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+    del x, anchor, codes, meta, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def delta_oracle_time(seconds: float = 2.0):
+    """The oracle's delta seal of one 128 x 128 segment, timed on one host
+    core over about `seconds` (random walks as in delta_kv_bench)."""
+    import time
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(17)
+    segs = (np.cumsum(rng.normal(0, 0.05, (16, 128, 128)), axis=1) + rng.normal(0, 1, (16, 1, 128)))
+    segs = segs.astype(np.float16).view(np.uint16)
+    oracle.delta_seal(segs[0])
+    t0, k = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        oracle.delta_seal(segs[k % 16])
+        k += 1
+    return {"us_per_segment": round((time.perf_counter() - t0) / k * 1e6, 1), "segments": k, "cores": 1}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,7 +399,7 @@ def main():
     ap.add_argument("--phase-iters", type=int, default=96)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV microbench")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV and delta-quantization microbenchmarks")
     ap.add_argument("--prefill", default="batched", choices=["batched", "steps"],
                     help="how the prompt is fed: the batched prefill (matrix products per layer), or one "
                          "teacher-forced decode step per token")
@@ -458,6 +520,7 @@ def main():
     m.close()
     del out
     gemv = None if args.no_gemv else gemv_microbench(rd, torch, stream)
+    delta = None if args.no_gemv else delta_kv_bench(rd, torch, stream)
 
     if persistent:
         roof = {"bound": "hbm", "kernel": "k_persist (whole decode steps, one launch for all timed steps)",
@@ -511,6 +574,8 @@ def main():
         big = [r for r in gemv if (r["N"], r["K"]) == (16384, 4096)]
         if big:
             res["gemv_16384x4096_b1_frac"] = big[0]["b1"]["frac"]
+    if delta is not None:
+        res["delta_kv"] = delta
     # device resources released before the interpreter's own teardown
     torch.cuda.synchronize()
     rd.release_scratch()
@@ -518,6 +583,8 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(blob, shape, args.cpu_seconds, base,
                                            first if B == 1 else int(first[0]))
+        if delta is not None:   # the oracle's delta seal beside the kernel's
+            res["delta_kv"]["oracle_seal"] = delta_oracle_time()
     print(json.dumps(res), flush=True)
 
 

@@ -419,6 +419,28 @@ rd_status rd_e5m2_encode(const uint16_t* in, uint8_t* out, size_t n, void* strea
 rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uint8_t* codes, float* meta,
                        void* stream);
 
+/* Delta quantization of n_seg K/V segments ("Grok-3 v3.2.4 hot update deep
+ * dive", §3.2: the scheme that stores the differences between adjacent
+ * tokens' values and quantizes them to INT8).  A segment is n rows of hd
+ * fp16 values.  Its first row is kept as it is (anchor); the differences
+ * x[p][j] - x[p-1][j] of rows 1..n-1, in binary32, are quantized together
+ * with the formula of rd_seg_quant (their min/max in fp32, scale, zp, codes).
+ * in: device u16 [n_seg][n][hd]; anchor: device u16 [n_seg][hd]; codes:
+ * device u8 [n_seg][n-1][hd] (may be NULL when n == 1); meta: device f32
+ * [n_seg][2] (scale, zp; 1 and 0 when n == 1).  1 <= n <= 4096,
+ * 1 <= hd <= 1024.  Buffers are the caller's; INVALID_ARG on bad sizes or
+ * NULL pointers, nothing launched. */
+rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n, int32_t hd, uint16_t* anchor, uint8_t* codes,
+                        float* meta, void* stream);
+
+/* The rows of delta-sealed segments restored (same section): out[s][0] =
+ * anchor, out[s][p][j] = out[s][p-1][j] + (code - zp) * scale, in binary32
+ * rounded after each operation, in row order, so the quantization errors of
+ * the differences add up along the segment.  out: device f32 [n_seg][n][hd];
+ * the other arguments as rd_delta_seal's outputs. */
+rd_status rd_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int32_t n_seg, int32_t n,
+                           int32_t hd, float* out, void* stream);
+
 /* *out = index of the largest of v[0..n) (lowest index on ties): the greedy
  * sampling the step keeps on the GPU ("Real-time LLM inference on standard
  * GPUs", loss table).  v: device f32 [n]; out: device i32 [1].  Uses the

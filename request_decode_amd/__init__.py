@@ -91,6 +91,8 @@ SIGNATURES = [
     ("rd_gemv_q4", _I32, [_VP, _VP, _VP, _VP, _I32, _I32, _VP]),
     ("rd_e5m2_encode", _I32, [_VP, _VP, _SZ, _VP]),
     ("rd_seg_quant", _I32, [_VP, _I32, _I32, _VP, _VP, _VP]),
+    ("rd_delta_seal", _I32, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
+    ("rd_delta_restore", _I32, [_VP, _VP, _VP, _I32, _I32, _I32, _VP, _VP]),
     ("rd_argmax_f32", _I32, [_VP, _I32, _VP, _VP]),
     ("rd_release_scratch", _I32, []),
 ]
@@ -354,6 +356,14 @@ def rd_gemv_q4(codes: int, scales: int, x: int, y: int, N: int, K: int, stream: 
 
 def rd_e5m2_encode(inp: int, out: int, n: int, stream: int = 0):
     check(lib().rd_e5m2_encode(inp, out, n, stream or None))
+
+
+def rd_delta_seal(inp: int, n_seg: int, n: int, hd: int, anchor: int, codes: int, meta: int, stream: int = 0):
+    check(lib().rd_delta_seal(inp, n_seg, n, hd, anchor, codes or None, meta, stream or None))
+
+
+def rd_delta_restore(anchor: int, codes: int, meta: int, n_seg: int, n: int, hd: int, out: int, stream: int = 0):
+    check(lib().rd_delta_restore(anchor, codes or None, meta, n_seg, n, hd, out, stream or None))
 
 
 def rd_seg_quant(inp: int, n_seg: int, seg_elems: int, codes: int, meta: int, stream: int = 0):

@@ -1354,6 +1354,25 @@ extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg
     return RD_OK;
 }
 
+extern "C" rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n, int32_t hd, uint16_t* anchor,
+                                   uint8_t* codes, float* meta, void* stream) {
+    if (!in || !anchor || !meta || (!codes && n > 1)) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (n_seg < 0 || n < 1 || n > 4096 || hd < 1 || hd > 1024)
+        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, 1 <= hd <= 1024");
+    K_TRY(launch_delta_seal(in, n_seg, n, hd, anchor, codes, meta, (hipStream_t)stream));
+    return RD_OK;
+}
+
+extern "C" rd_status rd_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int32_t n_seg,
+                                      int32_t n, int32_t hd, float* out, void* stream) {
+    if (!anchor || !meta || !out || (!codes && n > 1)) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
+    if (n_seg < 0 || n < 1 || n > 4096 || hd < 1 || hd > 1024)
+        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, 1 <= hd <= 1024");
+    if ((size_t)n_seg * hd > 0xffffffffull * 256) return fail(RD_ERR_INVALID_ARG, "too many segments");
+    K_TRY(launch_delta_restore(anchor, codes, meta, n_seg, n, hd, out, (hipStream_t)stream));
+    return RD_OK;
+}
+
 extern "C" rd_status rd_argmax_f32(const float* v, int32_t n, int32_t* out, void* stream) {
     if (!v || !out) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
     if (n < 1) return fail(RD_ERR_INVALID_ARG, "n must be >= 1");

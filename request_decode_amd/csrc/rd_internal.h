@@ -263,6 +263,10 @@ hipError_t launch_attention(const AttnArgs& A, int kvfmt, int hd, int G, hipStre
 hipError_t launch_e5m2(const uint16_t* in, uint8_t* out, size_t n, hipStream_t s);
 hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_t* codes, float* meta,
                             hipStream_t s);
+hipError_t launch_delta_seal(const uint16_t* in, int n_seg, int n, int hd, uint16_t* anchor, uint8_t* codes,
+                             float* meta, hipStream_t s);
+hipError_t launch_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int n_seg, int n,
+                                int hd, float* out, hipStream_t s);
 hipError_t launch_argmax(const float* v, int n, int* out, float* part_val, int* part_idx, int* part_cnt,
                          hipStream_t s);
 int lm_head_workgroups(int V);

@@ -269,6 +269,86 @@ __global__ __launch_bounds__(WAVE) void k_seg_quant(const uint16_t* __restrict__
     seal_segment<false>(in + off, seg_elems, codes + off, meta + (size_t)blockIdx.x * 2);
 }
 
+// ---- delta quantization of K/V segments ("Grok-3 v3.2.4 hot update deep
+// dive", §3.2: the adjacent-token differences of the values, quantized to
+// INT8).  A segment is n rows of hd fp16 values: its first row is kept as
+// the anchor, and the differences x[p] - x[p-1] (binary32) of rows 1..n-1
+// are quantized together with the adaptive-range formula of seal_segment.
+// One workgroup per segment.
+__global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ in, int n, int hd,
+                                                   uint16_t* __restrict__ anchor, uint8_t* __restrict__ codes,
+                                                   float* __restrict__ meta) {
+    __shared__ float s_mn[WG / WAVE], s_mx[WG / WAVE];
+    const size_t seg = blockIdx.x;
+    const uint16_t* x = in + seg * (size_t)n * hd;
+    const int m = (n - 1) * hd;   // differences: element i is x[hd + i] - x[i]
+    for (int j = threadIdx.x; j < hd; j += WG) anchor[seg * hd + j] = x[j];
+    if (m == 0) {   // one row: no differences
+        if (threadIdx.x == 0) {
+            meta[seg * 2] = 1.0f;
+            meta[seg * 2 + 1] = 0.0f;
+        }
+        return;
+    }
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = threadIdx.x; i < m; i += WG) {
+        const float d = h_bits2f(x[hd + i]) - h_bits2f(x[i]);
+        mn = fminf(mn, d);
+        mx = fmaxf(mx, d);
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane_id() == 0) {
+        s_mn[wave_id()] = mn;
+        s_mx[wave_id()] = mx;
+    }
+    __syncthreads();
+    mn = s_mn[0];
+    mx = s_mx[0];
+#pragma unroll
+    for (int w = 1; w < WG / WAVE; ++w) {
+        mn = fminf(mn, s_mn[w]);
+        mx = fmaxf(mx, s_mx[w]);
+    }
+    float scale = (mx - mn) / 255.0f;
+    if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;   // one repeated difference (seal_segment)
+    const float zp = rintf(-mn / scale);
+    uint8_t* c = codes + seg * (size_t)m;
+    for (int i = threadIdx.x; i < m; i += WG) {
+        const float d = h_bits2f(x[hd + i]) - h_bits2f(x[i]);
+        c[i] = (uint8_t)fminf(fmaxf(rintf(d / scale) + zp, 0.0f), 255.0f);
+    }
+    if (threadIdx.x == 0) {
+        meta[seg * 2] = scale;
+        meta[seg * 2 + 1] = zp;
+    }
+}
+
+// The rows of delta-sealed segments restored: one thread per (segment,
+// element of a row), adding the dequantized differences in row order:
+// y[0] = anchor, y[p] = y[p-1] + (code - zp) * scale (binary32, rounded
+// after each operation).
+__global__ __launch_bounds__(WG) void k_delta_restore(const uint16_t* __restrict__ anchor,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const float* __restrict__ meta, int n_seg, int n, int hd,
+                                                      float* __restrict__ out) {
+#pragma clang fp contract(off)   // a product and a sum, each rounded (no fused multiply-add)
+    const size_t t = (size_t)blockIdx.x * WG + threadIdx.x;
+    if (t >= (size_t)n_seg * hd) return;
+    const size_t seg = t / hd;
+    const int j = (int)(t % hd);
+    const float scale = meta[seg * 2], zp = meta[seg * 2 + 1];
+    float y = h_bits2f(anchor[seg * hd + j]);
+    float* o = out + seg * (size_t)n * hd + j;
+    const uint8_t* c = codes + seg * (size_t)(n - 1) * hd + j;
+    o[0] = y;
+    for (int p = 1; p < n; ++p) {
+        const float d = ((float)c[(size_t)(p - 1) * hd] - zp) * scale;
+        y = y + d;
+        o[(size_t)p * hd] = y;
+    }
+}
+
 __global__ __launch_bounds__(WG) void k_argmax(const float* __restrict__ v, int n, int* out, float* pv, int* pi,
                                                int* cnt) {
     Best b{-INFINITY, INT_MAX};
@@ -429,6 +509,22 @@ hipError_t launch_seg_quant(const uint16_t* in, int n_seg, int seg_elems, uint8_
                             hipStream_t s) {
     if (n_seg == 0) return hipSuccess;
     hipLaunchKernelGGL(k_seg_quant, dim3(n_seg), dim3(WAVE), 0, s, in, seg_elems, codes, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_seal(const uint16_t* in, int n_seg, int n, int hd, uint16_t* anchor, uint8_t* codes,
+                             float* meta, hipStream_t s) {
+    if (n_seg == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_delta_seal, dim3(n_seg), dim3(WG), 0, s, in, n, hd, anchor, codes, meta);
+    return hipGetLastError();
+}
+
+hipError_t launch_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int n_seg, int n,
+                                int hd, float* out, hipStream_t s) {
+    const size_t threads = (size_t)n_seg * hd;
+    if (threads == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_delta_restore, dim3((unsigned)((threads + WG - 1) / WG)), dim3(WG), 0, s, anchor, codes,
+                       meta, n_seg, n, hd, out);
     return hipGetLastError();
 }
 
