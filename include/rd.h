@@ -427,8 +427,9 @@ rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg_elems, uin
  * with the formula of rd_seg_quant (their min/max in fp32, scale, zp, codes).
  * in: device u16 [n_seg][n][hd]; anchor: device u16 [n_seg][hd]; codes:
  * device u8 [n_seg][n-1][hd] (may be NULL when n == 1); meta: device f32
- * [n_seg][2] (scale, zp; 1 and 0 when n == 1).  1 <= n <= 4096,
- * 1 <= hd <= 1024.  Buffers are the caller's; INVALID_ARG on bad sizes or
+ * [n_seg][2] (scale, zp; 1 and 0 when n == 1).  1 <= n <= 4096, hd a
+ * multiple of 8 in [8, 1024]; in and anchor 16-byte aligned, codes 8-byte
+ * aligned.  Buffers are the caller's; INVALID_ARG on bad sizes, alignment or
  * NULL pointers, nothing launched. */
 rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n, int32_t hd, uint16_t* anchor, uint8_t* codes,
                         float* meta, void* stream);
@@ -437,7 +438,7 @@ rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n, int32_t hd
  * anchor, out[s][p][j] = out[s][p-1][j] + (code - zp) * scale, in binary32
  * rounded after each operation, in row order, so the quantization errors of
  * the differences add up along the segment.  out: device f32 [n_seg][n][hd];
- * the other arguments as rd_delta_seal's outputs. */
+ * the other arguments as rd_delta_seal's outputs (out 16-byte aligned). */
 rd_status rd_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int32_t n_seg, int32_t n,
                            int32_t hd, float* out, void* stream);
 

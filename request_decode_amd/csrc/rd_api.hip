@@ -1357,8 +1357,10 @@ extern "C" rd_status rd_seg_quant(const uint16_t* in, int32_t n_seg, int32_t seg
 extern "C" rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n, int32_t hd, uint16_t* anchor,
                                    uint8_t* codes, float* meta, void* stream) {
     if (!in || !anchor || !meta || (!codes && n > 1)) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
-    if (n_seg < 0 || n < 1 || n > 4096 || hd < 1 || hd > 1024)
-        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, 1 <= hd <= 1024");
+    if (n_seg < 0 || n < 1 || n > 4096 || hd < 8 || hd > 1024 || hd % 8)
+        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, hd a multiple of 8 in [8, 1024]");
+    if ((((uintptr_t)in | (uintptr_t)anchor) & 15) || ((uintptr_t)codes & 7))
+        return fail(RD_ERR_INVALID_ARG, "in and anchor must be 16-byte aligned, codes 8-byte aligned");
     K_TRY(launch_delta_seal(in, n_seg, n, hd, anchor, codes, meta, (hipStream_t)stream));
     return RD_OK;
 }
@@ -1366,9 +1368,11 @@ extern "C" rd_status rd_delta_seal(const uint16_t* in, int32_t n_seg, int32_t n,
 extern "C" rd_status rd_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int32_t n_seg,
                                       int32_t n, int32_t hd, float* out, void* stream) {
     if (!anchor || !meta || !out || (!codes && n > 1)) return fail(RD_ERR_INVALID_ARG, "NULL pointer");
-    if (n_seg < 0 || n < 1 || n > 4096 || hd < 1 || hd > 1024)
-        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, 1 <= hd <= 1024");
-    if ((size_t)n_seg * hd > 0xffffffffull * 256) return fail(RD_ERR_INVALID_ARG, "too many segments");
+    if (n_seg < 0 || n < 1 || n > 4096 || hd < 8 || hd > 1024 || hd % 8)
+        return fail(RD_ERR_INVALID_ARG, "need n_seg >= 0, 1 <= n <= 4096, hd a multiple of 8 in [8, 1024]");
+    if ((((uintptr_t)anchor | (uintptr_t)out) & 15) || ((uintptr_t)codes & 7))
+        return fail(RD_ERR_INVALID_ARG, "anchor and out must be 16-byte aligned, codes 8-byte aligned");
+    if ((size_t)n_seg * (hd / 8) > 0xffffffffull * 256) return fail(RD_ERR_INVALID_ARG, "too many segments");
     K_TRY(launch_delta_restore(anchor, codes, meta, n_seg, n, hd, out, (hipStream_t)stream));
     return RD_OK;
 }

@@ -271,10 +271,16 @@ __global__ __launch_bounds__(WAVE) void k_seg_quant(const uint16_t* __restrict__
 
 // ---- delta quantization of K/V segments ("Grok-3 v3.2.4 hot update deep
 // dive", §3.2: the adjacent-token differences of the values, quantized to
-// INT8).  A segment is n rows of hd fp16 values: its first row is kept as
-// the anchor, and the differences x[p] - x[p-1] (binary32) of rows 1..n-1
-// are quantized together with the adaptive-range formula of seal_segment.
-// One workgroup per segment.
+// INT8).  A segment is n rows of hd fp16 values (hd % 8 == 0): its first row
+// is kept as the anchor, and the differences x[p] - x[p-1] (binary32) of rows
+// 1..n-1 are quantized together with the adaptive-range formula of
+// seal_segment.  One workgroup per segment; a thread takes 8 consecutive
+// differences at a time (16-byte loads of both rows, 8-byte code stores).
+__device__ __forceinline__ void delta8(const uint16_t* x, int hd, int i, float (&d)[8]) {
+    const h8 a = as_h8(ld16(x + hd + i)), b = as_h8(ld16(x + i));
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d[k] = (float)a[k] - (float)b[k];
+}
 __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ in, int n, int hd,
                                                    uint16_t* __restrict__ anchor, uint8_t* __restrict__ codes,
                                                    float* __restrict__ meta) {
@@ -282,7 +288,8 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
     const size_t seg = blockIdx.x;
     const uint16_t* x = in + seg * (size_t)n * hd;
     const int m = (n - 1) * hd;   // differences: element i is x[hd + i] - x[i]
-    for (int j = threadIdx.x; j < hd; j += WG) anchor[seg * hd + j] = x[j];
+    for (int j = threadIdx.x * 8; j < hd; j += WG * 8)
+        *reinterpret_cast<u4v*>(anchor + seg * hd + j) = ld16(x + j);
     if (m == 0) {   // one row: no differences
         if (threadIdx.x == 0) {
             meta[seg * 2] = 1.0f;
@@ -291,10 +298,14 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
         return;
     }
     float mn = INFINITY, mx = -INFINITY;
-    for (int i = threadIdx.x; i < m; i += WG) {
-        const float d = h_bits2f(x[hd + i]) - h_bits2f(x[i]);
-        mn = fminf(mn, d);
-        mx = fmaxf(mx, d);
+    for (int i = threadIdx.x * 8; i < m; i += WG * 8) {
+        float d[8];
+        delta8(x, hd, i, d);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            mn = fminf(mn, d[k]);
+            mx = fmaxf(mx, d[k]);
+        }
     }
     mn = wave_min(mn);
     mx = wave_max(mx);
@@ -314,9 +325,14 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
     if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;   // one repeated difference (seal_segment)
     const float zp = rintf(-mn / scale);
     uint8_t* c = codes + seg * (size_t)m;
-    for (int i = threadIdx.x; i < m; i += WG) {
-        const float d = h_bits2f(x[hd + i]) - h_bits2f(x[i]);
-        c[i] = (uint8_t)fminf(fmaxf(rintf(d / scale) + zp, 0.0f), 255.0f);
+    for (int i = threadIdx.x * 8; i < m; i += WG * 8) {   // the segment again (it is in the cache by now)
+        float d[8];
+        delta8(x, hd, i, d);
+        uint64_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            packed |= (uint64_t)(unsigned)fminf(fmaxf(rintf(d[k] / scale) + zp, 0.0f), 255.0f) << (8 * k);
+        *reinterpret_cast<uint64_t*>(c + i) = packed;
     }
     if (threadIdx.x == 0) {
         meta[seg * 2] = scale;
@@ -324,28 +340,39 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
     }
 }
 
-// The rows of delta-sealed segments restored: one thread per (segment,
-// element of a row), adding the dequantized differences in row order:
-// y[0] = anchor, y[p] = y[p-1] + (code - zp) * scale (binary32, rounded
-// after each operation).
+// The rows of delta-sealed segments restored: one thread per (segment, 8
+// consecutive elements of a row), adding the dequantized differences in row
+// order: y[0] = anchor, y[p] = y[p-1] + (code - zp) * scale (binary32,
+// rounded after each operation; 8 independent sums per thread).
 __global__ __launch_bounds__(WG) void k_delta_restore(const uint16_t* __restrict__ anchor,
                                                       const uint8_t* __restrict__ codes,
                                                       const float* __restrict__ meta, int n_seg, int n, int hd,
                                                       float* __restrict__ out) {
 #pragma clang fp contract(off)   // a product and a sum, each rounded (no fused multiply-add)
+    const int g8 = hd / 8;
     const size_t t = (size_t)blockIdx.x * WG + threadIdx.x;
-    if (t >= (size_t)n_seg * hd) return;
-    const size_t seg = t / hd;
-    const int j = (int)(t % hd);
+    if (t >= (size_t)n_seg * g8) return;
+    const size_t seg = t / g8;
+    const int j = (int)(t % g8) * 8;
     const float scale = meta[seg * 2], zp = meta[seg * 2 + 1];
-    float y = h_bits2f(anchor[seg * hd + j]);
+    const h8 a = as_h8(ld16(anchor + seg * hd + j));
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = (float)a[k];
     float* o = out + seg * (size_t)n * hd + j;
     const uint8_t* c = codes + seg * (size_t)(n - 1) * hd + j;
-    o[0] = y;
+    reinterpret_cast<float4*>(o)[0] = float4{y[0], y[1], y[2], y[3]};
+    reinterpret_cast<float4*>(o)[1] = float4{y[4], y[5], y[6], y[7]};
     for (int p = 1; p < n; ++p) {
-        const float d = ((float)c[(size_t)(p - 1) * hd] - zp) * scale;
-        y = y + d;
-        o[(size_t)p * hd] = y;
+        const uint64_t cw = *reinterpret_cast<const uint64_t*>(c + (size_t)(p - 1) * hd);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float d = ((float)(unsigned)((cw >> (8 * k)) & 0xffu) - zp) * scale;
+            y[k] = y[k] + d;
+        }
+        float* op = o + (size_t)p * hd;
+        reinterpret_cast<float4*>(op)[0] = float4{y[0], y[1], y[2], y[3]};
+        reinterpret_cast<float4*>(op)[1] = float4{y[4], y[5], y[6], y[7]};
     }
 }
 
@@ -521,7 +548,7 @@ hipError_t launch_delta_seal(const uint16_t* in, int n_seg, int n, int hd, uint1
 
 hipError_t launch_delta_restore(const uint16_t* anchor, const uint8_t* codes, const float* meta, int n_seg, int n,
                                 int hd, float* out, hipStream_t s) {
-    const size_t threads = (size_t)n_seg * hd;
+    const size_t threads = (size_t)n_seg * (hd / 8);
     if (threads == 0) return hipSuccess;
     hipLaunchKernelGGL(k_delta_restore, dim3((unsigned)((threads + WG - 1) / WG)), dim3(WG), 0, s, anchor, codes,
                        meta, n_seg, n, hd, out);

@@ -88,7 +88,7 @@ def test_delta_full_size_sampled(rd, orc):
 
 def test_delta_errors(rd):
     import request_decode_amd as r
-    for args in [(1, 0, 128), (1, 4097, 128), (1, 128, 0), (1, 128, 1025), (-1, 128, 128)]:
+    for args in [(1, 0, 128), (1, 4097, 128), (1, 128, 0), (1, 128, 1025), (-1, 128, 128), (1, 128, 12)]:
         with pytest.raises(r.RdError):
             rd.rd_delta_seal(16, args[0], args[1], args[2], 16, 16, 16)
         with pytest.raises(r.RdError):
