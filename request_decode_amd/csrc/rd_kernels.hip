@@ -297,14 +297,35 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
         }
         return;
     }
+    // segments of up to DELTA_REG groups of 8 per thread (128 x 128: 8) keep
+    // their differences in registers for the second pass; larger ones read
+    // the segment again
+    constexpr int DELTA_REG = 8;
+    const bool in_regs = m <= DELTA_REG * WG * 8;
+    float dr[DELTA_REG][8];
     float mn = INFINITY, mx = -INFINITY;
-    for (int i = threadIdx.x * 8; i < m; i += WG * 8) {
-        float d[8];
-        delta8(x, hd, i, d);
+    if (in_regs) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            mn = fminf(mn, d[k]);
-            mx = fmaxf(mx, d[k]);
+        for (int r = 0; r < DELTA_REG; ++r) {
+            const int i = (threadIdx.x + r * WG) * 8;
+            if (i < m) {
+                delta8(x, hd, i, dr[r]);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    mn = fminf(mn, dr[r][k]);
+                    mx = fmaxf(mx, dr[r][k]);
+                }
+            }
+        }
+    } else {
+        for (int i = threadIdx.x * 8; i < m; i += WG * 8) {
+            float d[8];
+            delta8(x, hd, i, d);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                mn = fminf(mn, d[k]);
+                mx = fmaxf(mx, d[k]);
+            }
         }
     }
     mn = wave_min(mn);
@@ -325,14 +346,25 @@ __global__ __launch_bounds__(WG) void k_delta_seal(const uint16_t* __restrict__ 
     if (!(scale > 0.0f)) scale = mn != 0.0f ? fabsf(mn) : 1.0f;   // one repeated difference (seal_segment)
     const float zp = rintf(-mn / scale);
     uint8_t* c = codes + seg * (size_t)m;
-    for (int i = threadIdx.x * 8; i < m; i += WG * 8) {   // the segment again (it is in the cache by now)
-        float d[8];
-        delta8(x, hd, i, d);
+    auto code8 = [&](const float (&d)[8]) {
         uint64_t packed = 0;
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             packed |= (uint64_t)(unsigned)fminf(fmaxf(rintf(d[k] / scale) + zp, 0.0f), 255.0f) << (8 * k);
-        *reinterpret_cast<uint64_t*>(c + i) = packed;
+        return packed;
+    };
+    if (in_regs) {
+#pragma unroll
+        for (int r = 0; r < DELTA_REG; ++r) {
+            const int i = (threadIdx.x + r * WG) * 8;
+            if (i < m) *reinterpret_cast<uint64_t*>(c + i) = code8(dr[r]);
+        }
+    } else {
+        for (int i = threadIdx.x * 8; i < m; i += WG * 8) {   // the segment again (it is in the cache by now)
+            float d[8];
+            delta8(x, hd, i, d);
+            *reinterpret_cast<uint64_t*>(c + i) = code8(d);
+        }
     }
     if (threadIdx.x == 0) {
         meta[seg * 2] = scale;

@@ -48,7 +48,7 @@ def _walks(rng, n_seg, n, hd, step=0.05):
     return x.astype(np.float16).view(np.uint16)
 
 
-@pytest.mark.parametrize("n,hd", [(128, 128), (128, 64), (37, 96), (2, 8), (1, 128)])
+@pytest.mark.parametrize("n,hd", [(128, 128), (128, 64), (37, 96), (2, 8), (1, 128), (300, 64)])
 def test_delta_bit_exact(rd, orc, n, hd):
     rng = np.random.default_rng(100 + n + hd)
     x = _walks(rng, 6, n, hd)
