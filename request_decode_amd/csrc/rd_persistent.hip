@@ -651,12 +651,14 @@ __device__ __forceinline__ void consume_rows(F& f, const StepArgs& A, const Pers
 // chunk (stage_stream): the rows' chunks are taken from the ring as in
 // consume_rows, then each chunk of the input is read once its count is
 // posted (fl: the count before this phase), into xh for the later rows, and
-// reduced at once.  The slots are refilled at once, or (late) once chunk 0
-// is posted.  The sums are dot_rows' in the same order.
+// reduced at once.  The slots are refilled at once, (late) once chunk 0 is
+// posted, or (gate > 0) once the control wave's count of attention publishes
+// reaches gate.  The sums are dot_rows' in the same order.
 template <int NR, int KCH, bool FK, class F>
 __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const PersistArgs& P,
                                                   unsigned char* ring, const float* s_r, const int* s_flag, int fl,
-                                                  u4v (&xh)[KCH], int K, float (&out)[NR], bool late) {
+                                                  u4v (&xh)[KCH], int K, float (&out)[NR], bool late,
+                                                  int gate = 0) {
     static_assert(NR * KCH <= RING, "ring shorter than the rows reduced together");
     const int lane = lane_id();
     const unsigned base = lds_addr(ring) + (unsigned)lane * 16u;
@@ -670,7 +672,15 @@ __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(RING - NR * KCH) : "memory");
     u4v wl[NR * KCH];
     lds_read_wait<NR * KCH>(wl, ad);   // slots read before they are refilled
-    if (!late) f.template issue_n<NR * KCH>(A, P);
+    if (!late) {
+        // gate > 0 (O): once the control wave has issued the attention split's
+        // stores (it posts its count in s_flag[1]), so that they do not queue
+        // behind these refills in the CU's memory path
+        if (gate > 0)
+            for (int it = 0; it < COUNT_SPIN && read_count(s_flag + 1) < gate; ++it) {
+            }
+        f.template issue_n<NR * KCH>(A, P);
+    }
     if constexpr (!FK) {
 #pragma unroll
         for (int c = 0; c < KCH; ++c)
@@ -709,7 +719,7 @@ template <int KCH, int KD, int KA, int KF, bool FK, bool STRM = false, class F, 
 __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const PersistArgs& P, int sw,
                                              unsigned char* ring, const float* s_r, float* s_part, int ph,
                                              StreamTracer& tr, Tail tail, const int* s_flag = nullptr,
-                                             int fl = 0) {
+                                             int fl = 0, int gate = 0) {
     constexpr int NR = KCH <= 4 ? 2 : 1;
     if constexpr (!STRM) lds_barrier();   // input staged
     const int kind = ph == 4 * A.n_layers ? 4 : (ph & 3);
@@ -730,7 +740,7 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
         if constexpr (STRM) {   // the first rows as the input's chunks arrive
             if (r + NR <= rb) {
                 float v[NR];
-                consume_rows_strm<NR, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late);
+                consume_rows_strm<NR, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late, gate);
                 if (sw == 0) tr(101 + 10 * kind);
                 if (lane_id() == 0)
 #pragma unroll
@@ -738,7 +748,7 @@ __device__ __forceinline__ void stream_phase(F& f, const StepArgs& A, const Pers
                 r += NR;
             } else {
                 float v[1];
-                consume_rows_strm<1, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late);
+                consume_rows_strm<1, KCH, FK>(f, A, P, ring, s_r, s_flag, fl, xh, K, v, late, gate);
                 if (lane_id() == 0) lds_write4(sp + 4u * (unsigned)(r - r0), v[0]);
                 r += 1;
             }
@@ -867,7 +877,8 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
     f.start(A, P, sw, ring);
     const int NL = A.n_layers;
     auto none = [] {};
-    int fl = 0;   // input chunks of the layers' GEMV phases posted so far
+    int fl = 0;     // input chunks of the layers' GEMV phases posted so far
+    int pubs = 0;   // attention splits published by the control wave so far
     for (int step = 0; step < P.n_steps; ++step) {
         const AttnSplit sp = attn_split<KVF>(A, P, step);
         for (int l = 0; l < NL; ++l) {
@@ -882,7 +893,9 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
             }, s_flag, fl);
             fl += KD;
             attn_stream<HD, G, KVF>(T, A, sp, sw, s_r, kb, tr);
-            stream_phase<KA, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none, s_flag, fl);
+            ++pubs;
+            stream_phase<KA, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 1, tr, none, s_flag, fl,
+                                                   pubs);
             fl += KA;
             stream_phase<KD, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none, s_flag, fl);
             fl += KD;
@@ -906,6 +919,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
     const Tracer TR = make_tracer(P, s_nev);
     int fl = 0;   // input chunks of the layers' GEMV phases posted so far
+    int pubs = 0;   // attention splits published (posted for the stream waves)
     TR(99);
     auto check_token = [&](int t) {
         if (t < 0 || t >= A.V) {
@@ -1064,6 +1078,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                 }
                 TR(10 + TR_PUB);
             }
+            post_count(s_flag + 1, ++pubs);   // the split's stores are issued: the O refills may follow
             // ---------------- merge of one query head ----------------
             if (mt >= 0) {
                 const int lane = lane_id();
@@ -1245,16 +1260,16 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
     __shared__ int s_nev[2];                                       // trace events: control, stream
-    __shared__ int s_flag;                                         // GEMV input chunks posted
+    __shared__ int s_flag[2];   // GEMV input chunks posted; attention splits published (control wave)
     const int wid = wave_id();
     if (threadIdx.x < 2) s_nev[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s_flag = 0;
+    if (threadIdx.x < 2) s_flag[threadIdx.x] = 0;
     lds_barrier();
     if (wid == 0)
-        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, &s_flag, s_nev);
+        control_role<KD, KA, KF, HD, G, KVF, SMAX>(A, P, s_r, s_part, s_own, s_flag, s_nev);
     else
         stream_role<KD, KA, KF, HD, G, KVF, FK>(A, P, wid - 1, s_ring + (wid - 1) * RING * UNIT, s_r, s_part,
-                                                &s_flag, s_nev);
+                                                s_flag, s_nev);
 }
 
 // ---- host side ------------------------------------------------------------------------
