@@ -673,9 +673,10 @@ __device__ __forceinline__ void consume_rows_strm(F& f, const StepArgs& A, const
     u4v wl[NR * KCH];
     lds_read_wait<NR * KCH>(wl, ad);   // slots read before they are refilled
     if (!late) {
-        // gate > 0 (O): once the control wave has issued the attention split's
-        // stores (it posts its count in s_flag[1]), so that they do not queue
-        // behind these refills in the CU's memory path
+        // gate > 0 (O, down): once the control wave has issued the stores of
+        // the attention split or the SwiGLU output (it posts their count in
+        // s_flag[1]), so that they do not queue behind these refills in the
+        // CU's memory path
         if (gate > 0)
             for (int it = 0; it < COUNT_SPIN && read_count(s_flag + 1) < gate; ++it) {
             }
@@ -878,7 +879,7 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
     const int NL = A.n_layers;
     auto none = [] {};
     int fl = 0;     // input chunks of the layers' GEMV phases posted so far
-    int pubs = 0;   // attention splits published by the control wave so far
+    int pubs = 0;   // the control wave's posted publishes (attention split, SwiGLU) so far
     for (int step = 0; step < P.n_steps; ++step) {
         const AttnSplit sp = attn_split<KVF>(A, P, step);
         for (int l = 0; l < NL; ++l) {
@@ -899,7 +900,9 @@ __device__ __forceinline__ void stream_role(const StepArgs& A, const PersistArgs
             fl += KA;
             stream_phase<KD, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 2, tr, none, s_flag, fl);
             fl += KD;
-            stream_phase<KF, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none, s_flag, fl);
+            ++pubs;
+            stream_phase<KF, KD, KA, KF, FK, true>(f, A, P, sw, ring, s_r, s_part, 4 * l + 3, tr, none, s_flag, fl,
+                                                   pubs);
             fl += KF;
         }
         stream_phase<KD, KD, KA, KF, FK>(f, A, P, sw, ring, s_r, s_part, 4 * NL, tr, none);
@@ -919,7 +922,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
     Waiter wt{A.abort_word, &A.st->err, P.spin_limit, 0};
     const Tracer TR = make_tracer(P, s_nev);
     int fl = 0;   // input chunks of the layers' GEMV phases posted so far
-    int pubs = 0;   // attention splits published (posted for the stream waves)
+    int pubs = 0;   // publishes posted for the stream waves (attention split, SwiGLU)
     TR(99);
     auto check_token = [&](int t) {
         if (t < 0 || t >= A.V) {
@@ -1148,6 +1151,7 @@ __device__ __forceinline__ void control_role(const StepArgs& A, const PersistArg
                              pack_h2(silu_mul(s_part[4 * q], s_part[4 * q + 1]),
                                      silu_mul(s_part[4 * q + 2], s_part[4 * q + 3])), tag);
             TR(40 + TR_PUB);
+            post_count(s_flag + 1, ++pubs);   // the SwiGLU stores are issued: the down refills may follow
             // ---------------- down projection + residual ----------------
             // (the input staged chunk by chunk: the stream waves start on the
             // chunks that have arrived, no barrier before the rows)
@@ -1260,7 +1264,7 @@ __global__ __launch_bounds__(PWG) void k_persist(StepArgs A, PersistArgs P) {
     __shared__ float s_part[PART_MAX];                             // row sums of the phase
     __shared__ float s_own[OWN_MAX];                               // owned rows of the residual stream
     __shared__ int s_nev[2];                                       // trace events: control, stream
-    __shared__ int s_flag[2];   // GEMV input chunks posted; attention splits published (control wave)
+    __shared__ int s_flag[2];   // GEMV input chunks posted; the control wave's publishes (attention, SwiGLU)
     const int wid = wave_id();
     if (threadIdx.x < 2) s_nev[threadIdx.x] = 0;
     if (threadIdx.x < 2) s_flag[threadIdx.x] = 0;
